@@ -1,0 +1,508 @@
+"""Pins for the fp64 oracle: closed forms, brute force, finite differences,
+invariants and the pages' own worked example.  None of these re-types the
+oracle's formulas; each checks it against something the pages or the
+mathematics fix independently.  Mutation tests at the end plant plausible
+mistakes in the oracle (on the CPU) and check that a pin catches each one.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle.lp_oracle as O
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------------------
+# independent brute-force formulations (pure Python, math.fsum, no max shift)
+# ---------------------------------------------------------------------------
+
+def bf_row(z, y, tau):
+    """softmax by direct exp / fsum on a safe range; returns (lp_y, entropy)."""
+    scale = (1.0 / tau) if (tau > 0 and tau != 1.0) else 1.0
+    e = [math.exp(float(v) * scale) for v in z]
+    S = math.fsum(e)
+    p = [x / S for x in e]
+    H = -math.fsum(pi * math.log(pi) for pi in p if pi > 0)
+    return math.log(p[y]), H
+
+
+def bf_kl(u, v):
+    eu = [math.exp(float(x)) for x in u]
+    ev = [math.exp(float(x)) for x in v]
+    Su, Sv = math.fsum(eu), math.fsum(ev)
+    return math.fsum((b / Sv) * math.log((b / Sv) / (a / Su)) for a, b in zip(eu, ev))
+
+
+def bf_matmul_T(Hm, Wm):
+    T, h = len(Hm), len(Hm[0])
+    V = len(Wm)
+    return [[math.fsum(Hm[t][k] * Wm[j][k] for k in range(h)) for j in range(V)] for t in range(T)]
+
+
+# ---------------------------------------------------------------------------
+# pins: logits-input path
+# ---------------------------------------------------------------------------
+
+def pin_uniform():
+    for V in (1, 2, 7, 1000, 151936):
+        for c in (0.0, -3.5, 12.25):
+            for tau in (1.0, 0.7, 2.0):
+                lp, H, _ = O.logprobs_entropy(np.full((1, V), c), [V - 1], None, tau)
+                assert abs(lp[0] + math.log(V)) < 1e-12 * max(1, math.log(V))
+                assert abs(H[0] - math.log(V)) < 1e-12 * max(1, math.log(V))
+
+
+def test_uniform_rows_closed_form():
+    pin_uniform()
+
+
+def test_single_class():
+    lp, H, _ = O.logprobs_entropy(np.array([[3.25], [-7.0]]), [0, 0], None, 0.7)
+    assert np.all(lp == 0.0) and np.all(H == 0.0)
+
+
+def pin_two_class():
+    rng = np.random.default_rng(1)
+    for _ in range(50):
+        z = rng.normal(0, 3, size=2)
+        y = int(rng.integers(0, 2))
+        tau = float(rng.choice([0.7, 1.0, 1.9]))
+        d = (z[1 - y] - z[y]) / tau
+        lp_ref = -math.log1p(math.exp(d))          # -softplus(d)
+        q = 1.0 / (1.0 + math.exp(-d))             # prob of the other class
+        H_ref = -(q * math.log(q) + (1 - q) * math.log(1 - q))
+        lp, H, _ = O.logprobs_entropy(z[None, :], [y], None, tau)
+        assert abs(lp[0] - lp_ref) < 1e-12
+        assert abs(H[0] - H_ref) < 1e-12
+
+
+def test_two_class_closed_form():
+    pin_two_class()
+
+
+def pin_brute_force():
+    rng = np.random.default_rng(2)
+    for V in (1, 2, 3, 5, 8, 16):
+        T = 6
+        z = rng.normal(0, 2.5, size=(T, V))
+        if V > 2:
+            z[1, :] = 1.5               # ties everywhere
+            z[2, 0] = z[2, 1] = z.max() + 1  # two equal maxima
+        for tau in (1.0, 0.7, 1.9, -1.0, 0.0):
+            for y in range(V):
+                targets = np.full(T, y)
+                lp, H, _ = O.logprobs_entropy(z, targets, None, tau)
+                for t in range(T):
+                    lp_ref, H_ref = bf_row(z[t], y, tau)
+                    assert abs(lp[t] - lp_ref) < 1e-12, (V, tau, y, t)
+                    assert abs(H[t] - H_ref) < 1e-12, (V, tau, y, t)
+
+
+def test_brute_force_small_vocab():
+    pin_brute_force()
+
+
+def test_temperature_literal_reading():
+    """tau <= 0 or tau == 1: no scaling (the helper's own condition)."""
+    rng = np.random.default_rng(3)
+    z = rng.normal(0, 3, size=(4, 33))
+    y = rng.integers(0, 33, size=4)
+    base = O.logprobs_entropy(z, y, None, 1.0)
+    for tau in (-1.0, 0.0, -0.5):
+        other = O.logprobs_entropy(z, y, None, tau)
+        for a, b in zip(base, other):
+            assert np.array_equal(a, b)
+    # scaling identity: tau=0.5 on z equals tau=1 on 2z
+    a = O.logprobs_entropy(z, y, None, 0.5)
+    b = O.logprobs_entropy(2.0 * z, y, None, 1.0)
+    for x1, x2 in zip(a, b):
+        assert np.allclose(x1, x2, atol=1e-12, rtol=0)
+
+
+def test_invariants_random_rows():
+    rng = np.random.default_rng(4)
+    for V in (3, 100, 4099):
+        z = rng.normal(0, 4, size=(16, V))
+        y = rng.integers(0, V, size=16)
+        lp, H, lse = O.logprobs_entropy(z, y, None, 0.7)
+        assert np.all(lp <= 1e-15)
+        assert np.all(H >= -1e-15) and np.all(H <= math.log(V) + 1e-12)
+        # lse bounds: max <= lse <= max + log V
+        zt = z / 0.7
+        assert np.all(lse >= zt.max(1) - 1e-12) and np.all(lse <= zt.max(1) + math.log(V) + 1e-12)
+
+
+def test_one_hot_limit():
+    V = 1000
+    z = np.zeros((1, V))
+    z[0, 17] = 100.0
+    lp, H, _ = O.logprobs_entropy(z, [17], None, 1.0)
+    eps = (V - 1) * math.exp(-100.0)
+    assert abs(lp[0] + eps) < 1e-30
+    assert 0.0 <= H[0] < 1e-38
+
+
+def test_neg_inf_logits_add_nothing():
+    z = np.array([[0.0, -np.inf, -np.inf, 0.0], [5.0, -np.inf, -np.inf, -np.inf]])
+    lp, H, _ = O.logprobs_entropy(z, [0, 0], None, 0.7)
+    assert abs(lp[0] + math.log(2)) < 1e-15 and abs(H[0] - math.log(2)) < 1e-15
+    assert lp[1] == 0.0 and H[1] == 0.0
+
+
+def test_unscored_rows_are_zero_and_targets_unread():
+    rng = np.random.default_rng(5)
+    z = rng.normal(size=(5, 9))
+    targets = np.array([3, -100, 8, 10**9, 0])
+    mask = np.array([1, 0, 1, 0, 1], dtype=np.uint8)
+    lp, H, lse = O.logprobs_entropy(z, targets, mask, 0.7)
+    assert lp[1] == 0 and H[1] == 0 and lp[3] == 0 and H[3] == 0 and lse[1] == 0
+    assert np.all(np.isfinite(lp))
+
+
+def test_out_of_range_target_poisons_logprob_only():
+    z = np.zeros((2, 4))
+    lp, H, _ = O.logprobs_entropy(z, [4, -1], None, 1.0)
+    assert np.all(np.isnan(lp))
+    assert np.allclose(H, math.log(4))
+
+
+def test_empty_input():
+    lp, H, lse = O.logprobs_entropy(np.zeros((0, 8)), np.zeros(0, dtype=np.int64), None, 0.7)
+    assert lp.shape == (0,) and H.shape == (0,)
+    assert O.chunk_plan(0, 4) == []
+
+
+def _read_golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line)
+    return rows
+
+
+def test_chunk_plan_page_example():
+    """The page's worked example: 5 rows, chunk size 2 -> chunks of 2, 2, 1 rows."""
+    lines = _read_golden("chunk_plan_5x8_c2.txt")
+    T, V, c = (int(x) for x in lines[0].split())
+    want = [int(x) for x in lines[1].split()]
+    assert [n for _, n in O.chunk_plan(T, c)] == want
+    # every row in exactly one chunk, in order
+    plan = O.chunk_plan(T, c)
+    assert [s for s, _ in plan] == [0, 2, 4]
+
+
+def test_chunk_plan_reading():
+    assert [n for _, n in O.chunk_plan(9, 4)] == [4, 4, 1]
+    assert O.chunk_plan(7, 0) == [(0, 7)] and O.chunk_plan(7, -1) == [(0, 7)]
+    assert O.chunk_plan(7, 100) == [(0, 7)]
+    assert [n for _, n in O.chunk_plan(8192, 4096)] == [4096, 4096]
+
+
+def test_chunking_does_not_change_rows():
+    rng = np.random.default_rng(6)
+    z = rng.normal(0, 3, size=(11, 257))
+    y = rng.integers(0, 257, size=11)
+    full = O.logprobs_entropy(z, y, None, 0.7)
+    for c in (1, 3, 4, 11, 20):
+        parts = [O.logprobs_entropy(z[s:s + n], y[s:s + n], None, 0.7) for s, n in O.chunk_plan(11, c)]
+        for k in range(3):
+            assert np.array_equal(np.concatenate([p[k] for p in parts]), full[k])
+
+
+# ---------------------------------------------------------------------------
+# pins: widening and rounding of inputs
+# ---------------------------------------------------------------------------
+
+def test_widen_known_bits():
+    bf = np.array([0x3F80, 0xC000, 0x7F80, 0xFF80, 0x0001, 0x4049], dtype=np.uint16)
+    w = O.widen_bf16(bf)
+    assert w[0] == 1.0 and w[1] == -2.0 and w[2] == np.inf and w[3] == -np.inf
+    assert w[4] == 2.0 ** -133  # smallest bf16 subnormal
+    assert w[5] == 3.140625
+    hf = np.array([0x3C00, 0x7BFF, 0xFC00, 0x0001], dtype=np.uint16)
+    w = O.widen_fp16(hf)
+    assert w[0] == 1.0 and w[1] == 65504.0 and w[2] == -np.inf and w[3] == 2.0 ** -24
+
+
+def test_bf16_rounding_is_nearest_even():
+    x = np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -8 + 2 ** -20, -2.5], dtype=np.float32)
+    b = synth.f32_to_bf16_bits(x)
+    assert list(O.widen_bf16(b)) == [1.0, 1.0 + 2 ** -6, 1.0 + 2 ** -7, -2.5]
+
+
+def test_generators_deterministic():
+    a = synth.LogitsInput(T=64, V=300, run_lo=8, run_hi=20, chunk_rows=16).build().arrays
+    b = synth.LogitsInput(T=64, V=300, run_lo=8, run_hi=20, chunk_rows=16).build().arrays
+    for k in a:
+        assert np.array_equal(a[k], b[k])
+    frac = a["mask"].mean()
+    assert 0.5 < frac < 0.95
+    assert a["spike_rows"].sum() == round(0.3 * 64)
+
+
+# ---------------------------------------------------------------------------
+# pins: fused LM head forward and backward
+# ---------------------------------------------------------------------------
+
+def pin_lm_head_brute_force():
+    rng = np.random.default_rng(7)
+    T, h, V = 5, 3, 7
+    Hm = rng.normal(size=(T, h))
+    Wm = rng.normal(size=(V, h))
+    y = rng.integers(0, V, size=T)
+    mask = np.array([1, 1, 0, 1, 1])
+    Z = bf_matmul_T(Hm.tolist(), Wm.tolist())
+    for tau in (1.0, 0.7):
+        lp, H, _ = O.lm_head_logprobs_entropy(Hm, Wm, y, mask, tau)
+        for t in range(T):
+            if not mask[t]:
+                assert lp[t] == 0 and H[t] == 0
+                continue
+            lp_ref, H_ref = bf_row(Z[t], int(y[t]), tau)
+            assert abs(lp[t] - lp_ref) < 1e-12 and abs(H[t] - H_ref) < 1e-12
+
+
+def test_lm_head_brute_force():
+    pin_lm_head_brute_force()
+
+
+def test_lm_head_matches_logits_path_on_tiny_config():
+    cfg = synth.tiny_lm_head()
+    A = cfg.arrays
+    Hd = O.widen_bf16(A["hidden"])
+    Wd = O.widen_bf16(A["weight"])
+    lp, H, lse = O.lm_head_logprobs_entropy(Hd, Wd, A["targets"], A["mask"], cfg.temperature)
+    Z = bf_matmul_T(Hd[:2].tolist(), Wd.tolist())
+    for t in range(2):
+        lp_ref, H_ref = bf_row(Z[t], int(A["targets"][t]), cfg.temperature)
+        assert abs(lp[t] - lp_ref) < 1e-11 and abs(H[t] - H_ref) < 1e-11
+
+
+def pin_backward_finite_differences(tau=0.7, seed=8):
+    rng = np.random.default_rng(seed)
+    T, h, V = 4, 5, 6
+    Hm = rng.normal(size=(T, h))
+    Wm = rng.normal(0, 0.7, size=(V, h))
+    y = rng.integers(0, V, size=T)
+    mask = np.array([1, 0, 1, 1])
+    g_lp = rng.normal(size=T)
+    g_H = rng.normal(0, 0.5, size=T)
+    dH, dW = O.lm_head_backward(Hm, Wm, y, mask, tau, g_lp, g_H)
+    eps = 1e-5
+
+    def L(Hx, Wx):
+        return O.lm_head_loss(Hx, Wx, y, mask, tau, g_lp, g_H)
+
+    for t in range(T):
+        for k in range(h):
+            Hp, Hn = Hm.copy(), Hm.copy()
+            Hp[t, k] += eps
+            Hn[t, k] -= eps
+            fd = (L(Hp, Wm) - L(Hn, Wm)) / (2 * eps)
+            assert abs(fd - dH[t, k]) <= 1e-6 * max(1.0, abs(fd)), ("dH", t, k, fd, dH[t, k])
+    for j in range(V):
+        for k in range(h):
+            Wp, Wn = Wm.copy(), Wm.copy()
+            Wp[j, k] += eps
+            Wn[j, k] -= eps
+            fd = (L(Hm, Wp) - L(Hm, Wn)) / (2 * eps)
+            assert abs(fd - dW[j, k]) <= 1e-6 * max(1.0, abs(fd)), ("dW", j, k, fd, dW[j, k])
+
+
+@pytest.mark.parametrize("tau", [1.0, 0.7, 1.6])
+def test_backward_finite_differences(tau):
+    pin_backward_finite_differences(tau)
+
+
+def test_backward_invariants():
+    rng = np.random.default_rng(9)
+    T, h, V = 6, 8, 13
+    Hm = rng.normal(size=(T, h))
+    Wm = rng.normal(size=(V, h))
+    y = rng.integers(0, V, size=T)
+    mask = np.array([1, 1, 0, 1, 0, 1])
+    g_lp, g_H = rng.normal(size=T), rng.normal(size=T)
+    rows, dZ = O.lm_head_logit_grad(Hm, Wm, y, mask, 0.7, g_lp, g_H)
+    assert list(rows) == [0, 1, 3, 5]
+    assert np.allclose(dZ.sum(axis=1), 0.0, atol=1e-13)
+    dH, dW = O.lm_head_backward(Hm, Wm, y, mask, 0.7, g_lp, g_H)
+    assert np.all(dH[[2, 4]] == 0)
+    # no scored rows: both gradients vanish
+    dH0, dW0 = O.lm_head_backward(Hm, Wm, y, np.zeros(T), 0.7, g_lp, g_H)
+    assert not dH0.any() and not dW0.any()
+    # g_H = 0, tau = 1: dZ_t = g_lp,t (onehot - softmax(z_t)), written out by hand
+    rows, dZ = O.lm_head_logit_grad(Hm, Wm, y, None, 1.0, g_lp, None)
+    Z = bf_matmul_T(Hm.tolist(), Wm.tolist())
+    for t in range(T):
+        e = [math.exp(v) for v in Z[t]]
+        S = math.fsum(e)
+        for j in range(V):
+            want = g_lp[t] * ((1.0 if j == y[t] else 0.0) - e[j] / S)
+            assert abs(dZ[t, j] - want) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# pins: KL and prob diff
+# ---------------------------------------------------------------------------
+
+def test_kl_self_is_exactly_zero():
+    rng = np.random.default_rng(10)
+    u = rng.normal(0, 4, size=(8, 129))
+    assert np.all(O.kl_full_vocab(u, u) == 0.0)
+
+
+def pin_kl_two_class():
+    rng = np.random.default_rng(11)
+    for _ in range(40):
+        u = rng.normal(0, 2, size=2)
+        v = rng.normal(0, 2, size=2)
+        q = 1 / (1 + math.exp(u[0] - u[1]))   # student prob of class 1
+        p = 1 / (1 + math.exp(v[0] - v[1]))   # teacher prob of class 1
+        want = p * math.log(p / q) + (1 - p) * math.log((1 - p) / (1 - q))
+        got = O.kl_full_vocab(u[None], v[None])[0]
+        assert abs(got - want) < 1e-12
+
+
+def test_kl_two_class_bernoulli():
+    pin_kl_two_class()
+
+
+def pin_kl_brute_force():
+    rng = np.random.default_rng(12)
+    for V in (1, 2, 5, 16):
+        u = rng.normal(0, 3, size=(5, V))
+        v = u + rng.normal(0, 0.5, size=(5, V))
+        got = O.kl_full_vocab(u, v)
+        for t in range(5):
+            assert abs(got[t] - bf_kl(u[t], v[t])) < 1e-12
+
+
+def test_kl_brute_force():
+    pin_kl_brute_force()
+
+
+def test_kl_invariants():
+    rng = np.random.default_rng(13)
+    u = rng.normal(0, 4, size=(8, 1000))
+    v = u + rng.normal(0, 0.5, size=u.shape)
+    kl = O.kl_full_vocab(u, v)
+    assert np.all(kl >= 0)
+    # shifting a row by a constant leaves its distribution unchanged
+    assert np.allclose(O.kl_full_vocab(u + 3.0, u), 0.0, atol=1e-12)
+
+
+def test_prob_diff_page_cases():
+    a = np.log(np.array([0.5, 0.25, 1.0, 0.125]))
+    b = np.log(np.array([0.25, 0.25, 0.5, 0.5]))
+    d = O.prob_diff(a, b, None)
+    assert np.allclose(d, [0.25, 0.0, 0.5, 0.375], atol=1e-15, rtol=0)
+    # all-False mask -> all-zero diff (msprobe edge-case table)
+    assert np.all(O.prob_diff(a, b, np.zeros(4)) == 0)
+    m = np.array([1, 0, 1, 0])
+    assert np.allclose(O.prob_diff(a, b, m), [0.25, 0, 0.5, 0], atol=1e-15, rtol=0)
+    assert np.all(O.prob_diff(a, a, None) == 0)
+
+
+def test_kl_and_prob_diff_bundle():
+    rng = np.random.default_rng(14)
+    u = rng.normal(0, 4, size=(6, 50))
+    v = u + rng.normal(0, 0.5, size=u.shape)
+    y = rng.integers(0, 50, size=6)
+    m = np.array([1, 0, 1, 1, 0, 1])
+    kl, lpu, lpv, d = O.kl_and_prob_diff(u, v, y, m)
+    for t in range(6):
+        lpu_ref, _ = bf_row(u[t], int(y[t]), 1.0)
+        lpv_ref, _ = bf_row(v[t], int(y[t]), 1.0)
+        assert abs(lpu[t] - lpu_ref) < 1e-12 and abs(lpv[t] - lpv_ref) < 1e-12
+        want = abs(math.exp(lpu_ref) - math.exp(lpv_ref)) if m[t] else 0.0
+        assert abs(d[t] - want) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# negative controls: the pins are sensitive to the failure modes the pages name
+# ---------------------------------------------------------------------------
+
+def test_negative_control_temperature_in_model_precision():
+    """Dividing by the temperature in bf16 (before the upcast) is measurably
+    wrong on logits-input-like rows, so a kernel that matches the oracle to
+    1e-5 cannot be doing it."""
+    cfg = synth.LogitsInput(T=32, V=151936).build()
+    A = cfg.arrays
+    z = O.widen_bf16(A["logits"])
+    lp, H, _ = O.logprobs_entropy(z, A["targets"], None, 0.7)
+    z_bf16_div = O.widen_bf16(synth.f32_to_bf16_bits((z / 0.7).astype(np.float32)))
+    lp2, H2, _ = O.logprobs_entropy(z_bf16_div, A["targets"], None, 1.0)
+    assert max(np.abs(lp - lp2).max(), np.abs(H - H2).max()) > 1e-3
+
+
+def test_negative_control_fp16_accumulation_overflows():
+    cfg = synth.KLPair(T=4, V=129280).build()
+    u = cfg.arrays["student"].view(np.float16)
+    with np.errstate(over="ignore"):
+        s16 = np.exp(u[0]).sum(dtype=np.float16)
+        q16 = (u[0] * u[0]).sum(dtype=np.float16)
+    assert np.isinf(s16) and np.isinf(q16)
+    kl = O.kl_full_vocab(O.widen_fp16(cfg.arrays["student"]), O.widen_fp16(cfg.arrays["teacher"]))
+    assert np.all(np.isfinite(kl))
+
+
+# ---------------------------------------------------------------------------
+# mutation tests: plant a mistake in the oracle, on the CPU; a pin must fail
+# ---------------------------------------------------------------------------
+
+def _must_fail(pin):
+    with pytest.raises(AssertionError):
+        pin()
+
+
+def test_mutation_entropy_sign(monkeypatch):
+    orig = O.shannon_entropy
+    monkeypatch.setattr(O, "shannon_entropy", lambda lp: -orig(lp))
+    _must_fail(pin_uniform)
+
+
+def test_mutation_temperature_multiplied(monkeypatch):
+    monkeypatch.setattr(O, "tempered", lambda z, t: np.asarray(z, float) * t if O.temperature_applies(t)
+                        else np.asarray(z, float).copy())
+    _must_fail(pin_two_class)
+
+
+def test_mutation_dropped_max_shift_term(monkeypatch):
+    def bad(zt):
+        zt = np.atleast_2d(zt)
+        return np.log(np.exp(zt - zt.max(1, keepdims=True)).sum(1))   # forgot + max
+    monkeypatch.setattr(O, "log_normaliser", bad)
+    _must_fail(pin_brute_force)
+
+
+def test_mutation_wrong_vocab_index(monkeypatch):
+    monkeypatch.setattr(O, "lm_head_logits", lambda Hd, W, vocab_block=0: (np.asarray(W, float) @ np.asarray(Hd, float).T).T[:, ::-1])
+    _must_fail(pin_lm_head_brute_force)
+
+
+def test_mutation_backward_drops_entropy_term(monkeypatch):
+    orig = O.lm_head_logit_grad
+    monkeypatch.setattr(O, "lm_head_logit_grad",
+                        lambda Hm, Wm, y, m, tau, g_lp, g_H: orig(Hm, Wm, y, m, tau, g_lp, None))
+    _must_fail(pin_backward_finite_differences)
+
+
+def test_mutation_backward_missing_temperature(monkeypatch):
+    orig = O.lm_head_logit_grad
+    def bad(Hm, Wm, y, m, tau, g_lp, g_H):
+        rows, dZ = orig(Hm, Wm, y, m, tau, g_lp, g_H)
+        return rows, dZ * tau
+    monkeypatch.setattr(O, "lm_head_logit_grad", bad)
+    _must_fail(pin_backward_finite_differences)
+
+
+def test_mutation_kl_direction(monkeypatch):
+    orig = O.kl_full_vocab
+    monkeypatch.setattr(O, "kl_full_vocab", lambda u, v: orig(v, u))
+    _must_fail(pin_kl_two_class)
