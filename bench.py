@@ -1,0 +1,336 @@
+#!/usr/bin/env python3
+"""Benchmark of the per-token log-prob / entropy hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--paths all|lm_head_fwd,...]
+
+Headline (`value`): scored tokens/s of the fused LM-head forward (log-prob +
+entropy of softmax(hidden @ W^T / 0.7)) on T = 32768 packed rows (about 70 %
+scored), h = 5120, V = 151936, bf16, tile 4096 rows.  One step is one call of
+lp_lm_head_logprobs_entropy with inputs already resident in HBM.  The same
+JSON line carries the other paths of the hot path measured the same way
+(logits-input rows, exact KL + prob diff, fused forward + backward), the
+roofline of the dominant kernel from live per-launch HIP-event timing, and
+the fp64 oracle timed on the host cores over a bounded sample.
+
+Inputs are seeded and synthetic (see synth/); the oracle is used only for the
+CPU-baseline leg and a sampled parity check of every path.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "scored tokens/s, fused LM-head logprob+entropy; % of MFMA / HBM peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+ALL_PATHS = ("lm_head_fwd", "logits_input", "kl_prob_diff", "lm_head_fwd_bwd")
+
+
+def to_dev_bits(bits, dtype):
+    """uint16 bit array -> device bf16/fp16 tensor with the same bits."""
+    import numpy as np
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda")
+    return t.view(torch.bfloat16 if dtype == "bf16" else torch.float16)
+
+
+def to_dev(a):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def _events_ms(torch, fn, steps):
+    s = torch.cuda.current_stream()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(s)
+    for _ in range(steps):
+        fn()
+    b.record(s)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b)
+
+
+def _timed(lp, torch, fn, steps, warmup, kernels):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    lp.lp_timing_enable(True)
+    ms = _events_ms(torch, fn, steps)
+    per_kernel = {k: lp.lp_timing_read(k) for k in kernels}
+    lp.lp_timing_enable(False)
+    return ms, per_kernel
+
+
+def bench_lm_head_fwd(lp, torch, np, synth, O, steps, warmup, cpu_seconds):
+    cfg = synth.LMHead().build()
+    A = cfg.arrays
+    hid, W = to_dev_bits(A["hidden"], "bf16"), to_dev_bits(A["weight"], "bf16")
+    y, m = to_dev(A["targets"]), to_dev(A["mask"])
+    Ts = int(A["mask"].sum())
+    ws = torch.empty(lp.lp_lm_head_workspace_bytes(cfg.T, cfg.h, cfg.V, cfg.tile_rows, False), dtype=torch.uint8,
+                     device="cuda")
+    out = {}
+
+    def step():
+        out["r"] = lp.lp_lm_head_logprobs_entropy(hid, W, y, m, cfg.temperature, cfg.tile_rows, workspace=ws)
+
+    ms, kt = _timed(lp, torch, step, steps, warmup, ["k_fwd_tile", "k_fwd_merge", "k_compact"])
+    flop_step = 2.0 * Ts * cfg.V * cfg.h
+    n_launch, gemm_ms = kt["k_fwd_tile"]
+    achieved = flop_step * steps / (gemm_ms * 1e-3) / 1e12
+    # parity on sampled rows
+    lpv, Hv, _ = (t.cpu().numpy() for t in out["r"])
+    scored = np.nonzero(A["mask"])[0]
+    rows = np.unique(np.random.default_rng(0).choice(scored, 8, replace=False))
+    lp_o, H_o, _ = O.lm_head_logprobs_entropy(O.widen_bf16(A["hidden"][rows]), _LazyWeight(O, A["weight"]),
+                                              A["targets"][rows], None, cfg.temperature)
+    err = float(max(np.abs(lpv[rows] - lp_o).max(), np.abs(Hv[rows] - H_o).max()))
+    res = dict(
+        workload=f"fused LM-head forward: T={cfg.T} packed rows ({Ts} scored), h={cfg.h}, V={cfg.V}, bf16, "
+                 f"tau {cfg.temperature}, tile {cfg.tile_rows}",
+        T=cfg.T, scored_rows=Ts, h=cfg.h, V=cfg.V, temperature=cfg.temperature, tile_rows=cfg.tile_rows,
+        ms_per_step=ms / steps, tokens_per_s=Ts * steps / (ms * 1e-3),
+        roofline=dict(bound="mfma", kernel="k_fwd_tile", achieved=achieved, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                      frac=achieved / BF16_PEAK_TFLOPS, traffic=None,
+                      launches_per_step=n_launch / steps, kernel_ms_per_step=gemm_ms / steps,
+                      algorithmic_flop_per_step=flop_step),
+        parity_max_abs_err_sampled=err, parity_tol=2e-3,
+        kernel_ms_per_step={k: v[1] / steps for k, v in kt.items()},
+    )
+    if cpu_seconds > 0:
+        res["cpu_baseline"] = _cpu_baseline_lm_head(O, np, A, cfg, scored, cpu_seconds)
+    del hid, W, y, m, ws, out
+    torch.cuda.empty_cache()
+    return res
+
+
+class _LazyWeight:
+    """Widens bf16 weight rows to fp64 only for the vocab block asked for."""
+
+    def __init__(self, O, bits):
+        self.O, self.bits, self.shape = O, bits, bits.shape
+
+    def __getitem__(self, sl):
+        return self.O.widen_bf16(self.bits[sl])
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [d.get("num_threads", 0) for d in threadpool_info() if d.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:  # pragma: no cover
+        return 1
+
+
+def _cpu_baseline_lm_head(O, np, A, cfg, scored, seconds):
+    """Oracle on a bounded sample of scored rows, scaled to tokens/s."""
+    W = _LazyWeight(O, A["weight"])
+    n = 8
+    t = 0.0
+    while True:
+        rows = scored[:n]
+        t0 = time.perf_counter()
+        O.lm_head_logprobs_entropy(O.widen_bf16(A["hidden"][rows]), W, A["targets"][rows], None, cfg.temperature)
+        t = time.perf_counter() - t0
+        if t >= seconds / 3 or n >= len(scored):
+            break
+        n = min(len(scored), int(n * max(2.0, seconds / 3 / max(t, 1e-3))))
+    return dict(value=n / t, unit="scored tokens/s", cores=_blas_threads(), kind="oracle",
+                sample=f"{n} scored rows of the same workload through the fp64 oracle (full V={cfg.V}, h={cfg.h})",
+                seconds=t)
+
+
+def bench_logits_input(lp, torch, np, synth, O, steps, warmup):
+    cfg = synth.LogitsInput().build()
+    A = cfg.arrays
+    x, y, m = to_dev_bits(A["logits"], "bf16"), to_dev(A["targets"]), to_dev(A["mask"])
+    Ts = int(A["mask"].sum())
+    lpo = torch.empty(cfg.T, device="cuda")
+    Ho = torch.empty(cfg.T, device="cuda")
+
+    def step():
+        lp.lp_logprobs_entropy(x, y, m, cfg.temperature, cfg.chunk_rows, logprob=lpo, entropy=Ho)
+
+    ms, kt = _timed(lp, torch, step, steps, warmup, ["k_logprobs_entropy"])
+    n_launch, kms = kt["k_logprobs_entropy"]
+    bytes_step = Ts * (2 * cfg.V + 8 + 8) + cfg.T * 1 + (cfg.T - Ts) * 8
+    achieved = bytes_step * steps / (kms * 1e-3) / 1e9
+    scored = np.nonzero(A["mask"])[0]
+    rows = np.unique(np.random.default_rng(1).choice(scored, 16, replace=False))
+    lp_o, H_o, _ = O.logprobs_entropy(O.widen_bf16(A["logits"][rows]), A["targets"][rows], None, cfg.temperature)
+    err = float(max(np.abs(lpo.cpu().numpy()[rows] - lp_o).max(), np.abs(Ho.cpu().numpy()[rows] - H_o).max()))
+    res = dict(
+        workload=f"logits input: bf16 [{cfg.T}, {cfg.V}] ({Ts} scored rows), tau {cfg.temperature}, "
+                 f"chunk {cfg.chunk_rows}",
+        ms_per_step=ms / steps, tokens_per_s=Ts * steps / (ms * 1e-3),
+        roofline=dict(bound="hbm", kernel="k_logprobs_entropy", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
+                      frac=achieved / HBM_PEAK_GBS, traffic=None, launches_per_step=n_launch / steps,
+                      algorithmic_bytes_per_step=bytes_step),
+        parity_max_abs_err_sampled=err, parity_tol=1e-5)
+    del x, y, m, lpo, Ho
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_kl(lp, torch, np, synth, O, steps, warmup):
+    cfg = synth.KLPair().build()
+    A = cfg.arrays
+    u, v = to_dev_bits(A["student"], "fp16"), to_dev_bits(A["teacher"], "fp16")
+    y, dm = to_dev(A["targets"]), to_dev(A["diff_mask"])
+    out = {}
+
+    def step():
+        out["r"] = lp.lp_kl_full_vocab(u, v, y, dm)
+
+    ms, kt = _timed(lp, torch, step, steps, warmup, ["k_kl_full_vocab"])
+    n_launch, kms = kt["k_kl_full_vocab"]
+    bytes_step = cfg.T * (2 * 2 * cfg.V + 8 + 1 + 4 * 4)
+    achieved = bytes_step * steps / (kms * 1e-3) / 1e9
+    kl = out["r"][0].cpu().numpy()
+    rows = np.unique(np.random.default_rng(2).choice(cfg.T, 8, replace=False))
+    kl_o = O.kl_full_vocab(O.widen_fp16(A["student"][rows]), O.widen_fp16(A["teacher"][rows]))
+    res = dict(
+        workload=f"exact KL(teacher||student) + target log-probs + masked prob diff: fp16 [{cfg.T}, {cfg.V}] x 2",
+        ms_per_step=ms / steps, tokens_per_s=cfg.T * steps / (ms * 1e-3),
+        roofline=dict(bound="hbm", kernel="k_kl_full_vocab", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
+                      frac=achieved / HBM_PEAK_GBS, traffic=None, launches_per_step=n_launch / steps,
+                      algorithmic_bytes_per_step=bytes_step),
+        parity_max_abs_err_sampled=float(np.abs(kl[rows] - kl_o).max()), parity_tol=1e-5)
+    del u, v, y, dm, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_lm_head_fwd_bwd(lp, torch, np, synth, O, steps, warmup):
+    cfg = synth.LMHead(T=114688, prompt_frac=0.2, temperature=1.0, grads=True, workload=synth.W_LM_HEAD_BWD).build()
+    A = cfg.arrays
+    hid, W = to_dev_bits(A["hidden"], "bf16"), to_dev_bits(A["weight"], "bf16")
+    y, m = to_dev(A["targets"]), to_dev(A["mask"])
+    glp, gH = to_dev(A["grad_logprob"]), to_dev(A["grad_entropy"])
+    Ts = int(A["mask"].sum())
+    wsf = torch.empty(lp.lp_lm_head_workspace_bytes(cfg.T, cfg.h, cfg.V, cfg.tile_rows, False), dtype=torch.uint8,
+                      device="cuda")
+    wsb = torch.empty(lp.lp_lm_head_workspace_bytes(cfg.T, cfg.h, cfg.V, cfg.tile_rows, True), dtype=torch.uint8,
+                      device="cuda")
+    out = {}
+
+    def step():
+        lpv, Hv, lse = lp.lp_lm_head_logprobs_entropy(hid, W, y, m, cfg.temperature, cfg.tile_rows, workspace=wsf)
+        out["g"] = lp.lp_lm_head_logprobs_entropy_backward(hid, W, y, m, cfg.temperature, cfg.tile_rows, lse, Hv,
+                                                           glp, gH, workspace=wsb)
+        out["f"] = (lpv, Hv, lse)
+
+    kernels = ["k_fwd_tile", "k_bwd_dz", "k_out_gemm_dhidden", "k_out_gemm_dweight", "k_transpose_bf16"]
+    ms, kt = _timed(lp, torch, step, steps, warmup, kernels)
+    flop_step = 8.0 * Ts * cfg.V * cfg.h
+    mfma_ms = sum(kt[k][1] for k in ("k_fwd_tile", "k_bwd_dz", "k_out_gemm_dhidden", "k_out_gemm_dweight"))
+    achieved = flop_step * steps / (mfma_ms * 1e-3) / 1e12
+    # sampled parity: two scored rows of dHidden (needs only those rows' logits)
+    dH = out["g"][0]
+    scored = np.nonzero(A["mask"])[0]
+    rows = np.array([scored[0], scored[len(scored) // 2]])
+    Wl = _LazyWeight(O, A["weight"])
+    rr, dZ = O.lm_head_logit_grad(O.widen_bf16(A["hidden"][rows]), Wl, A["targets"][rows], None, cfg.temperature,
+                                  A["grad_logprob"][rows], A["grad_entropy"][rows])
+    want = np.zeros((len(rows), cfg.h))
+    for j0 in range(0, cfg.V, 16384):
+        want += dZ[:, j0:j0 + 16384] @ Wl[j0:j0 + 16384]
+    got = dH[torch.as_tensor(rows)].cpu().numpy()
+    rel = float(np.linalg.norm(got - want) / np.linalg.norm(want))
+    res = dict(
+        workload=f"fused LM-head forward + recompute backward: T={cfg.T} packed rows ({Ts} scored), h={cfg.h}, "
+                 f"V={cfg.V}, bf16, tau {cfg.temperature}, tile {cfg.tile_rows}, dHidden and dW in fp32",
+        ms_per_step=ms / steps, tokens_per_s=Ts * steps / (ms * 1e-3),
+        roofline=dict(bound="mfma", kernel="all MFMA GEMMs (fwd + dZ recompute + dHidden + dW)", achieved=achieved,
+                      peak=BF16_PEAK_TFLOPS, unit="TFLOP/s", frac=achieved / BF16_PEAK_TFLOPS, traffic=None,
+                      algorithmic_flop_per_step=flop_step),
+        kernel_ms_per_step={k: v[1] / steps for k, v in kt.items()},
+        parity_dhidden_rel_err_sampled=rel, parity_tol=1e-2)
+    del hid, W, y, m, glp, gH, wsf, wsb, out, dH
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--paths", default="all", help="comma list of " + ",".join(ALL_PATHS))
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
+              "(rows shard with no exchange; see DESIGN.md for how the path would shard)", file=sys.stderr)
+        sys.exit(2)
+    paths = ALL_PATHS if args.paths == "all" else tuple(p.strip() for p in args.paths.split(","))
+
+    import numpy as np
+    import torch
+
+    import entropy_chunked_row_amd as lp
+    import synth
+    from oracle import lp_oracle as O
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    lp.load()
+    results = {}
+    for p in paths:
+        log(f"path {p}: building inputs and timing")
+        t0 = time.time()
+        if p == "lm_head_fwd":
+            results[p] = bench_lm_head_fwd(lp, torch, np, synth, O, args.steps, args.warmup, args.cpu_seconds)
+        elif p == "logits_input":
+            results[p] = bench_logits_input(lp, torch, np, synth, O, args.steps, args.warmup)
+        elif p == "kl_prob_diff":
+            results[p] = bench_kl(lp, torch, np, synth, O, args.steps, args.warmup)
+        elif p == "lm_head_fwd_bwd":
+            results[p] = bench_lm_head_fwd_bwd(lp, torch, np, synth, O, max(1, args.steps // 5),
+                                               min(1, args.warmup))
+        else:
+            raise SystemExit(f"unknown path {p}")
+        log(f"path {p}: done in {time.time() - t0:.1f}s: {results[p]['tokens_per_s']:.4g} tok/s, "
+            f"{results[p]['ms_per_step']:.3f} ms/step")
+
+    head_key = "lm_head_fwd" if "lm_head_fwd" in results else paths[0]
+    head = results[head_key]
+    line = {
+        "metric": METRIC,
+        "value": head["tokens_per_s"],
+        "unit": "scored tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": head["workload"], "path": head_key},
+        "roofline": head["roofline"],
+        "cpu_baseline": head.get("cpu_baseline"),
+        "paths": {k: v for k, v in results.items() if k != head_key},
+        "parity": {k: {kk: vv for kk, vv in v.items() if kk.startswith("parity")} for k, v in results.items()},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

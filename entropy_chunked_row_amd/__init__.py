@@ -1,0 +1,227 @@
+"""Python binding of liblp.so: per-token log-probs, entropy and exact KL over a
+large vocabulary on MI355X.
+
+Functions carry the C names (include/lp.h).  This layer only marshals
+arguments: it checks tensor placement and layout, allocates outputs and
+workspace with torch (device memory is all torch is used for) and passes raw
+pointers plus the current HIP stream.  Every number is computed by the HIP
+kernels; if liblp.so is missing, every call raises.
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+from . import _lib
+from ._lib import LP_BF16, LP_FP16, LP_FP32, LPError, check, load
+
+__all__ = [
+    "lp_logprobs_entropy", "lp_lm_head_logprobs_entropy", "lp_lm_head_logprobs_entropy_backward",
+    "lp_lm_head_workspace_bytes", "lp_kl_full_vocab", "lp_prob_diff", "lp_version", "lp_timing_enable",
+    "lp_timing_read", "LPError", "load",
+]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return LP_BF16
+    if t.dtype == torch.float16:
+        return LP_FP16
+    if t.dtype == torch.float32:
+        return LP_FP32
+    raise TypeError(f"unsupported logits dtype {t.dtype}")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t, name):
+    if t is not None and not t.is_cuda:
+        raise ValueError(f"{name} must be a device (GPU) tensor")
+
+
+def _rows(t, name):
+    """2-D tensor with unit stride along columns; returns its leading dimension."""
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be 2-D with contiguous rows")
+    return t.stride(0) if t.size(0) > 1 else max(t.stride(0), t.size(1))
+
+
+def _vec(t, name, dtype=None):
+    if t is None:
+        return None
+    torch = _torch()
+    if dtype is not None and t.dtype != dtype:
+        if dtype == torch.uint8 and t.dtype == torch.bool:
+            t = t.view(torch.uint8)
+        else:
+            raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    _dev(t, name)
+    return t
+
+
+def _stream(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def lp_version() -> int:
+    return load().lp_version()
+
+
+def lp_timing_enable(on: bool) -> None:
+    """Start (clearing old records) or stop per-kernel HIP-event timing."""
+    load().lp_timing_enable(1 if on else 0)
+
+
+def lp_timing_read(kernel: str):
+    """(launches, total_ms) recorded for `kernel` since timing was enabled."""
+    import ctypes
+    n = ctypes.c_int64(0)
+    ms = ctypes.c_double(0.0)
+    check("lp_timing_read", load().lp_timing_read(kernel.encode(), ctypes.byref(n), ctypes.byref(ms)))
+    return int(n.value), float(ms.value)
+
+
+def lp_logprobs_entropy(logits, targets, mask=None, temperature: float = 1.0, chunk_rows: int = -1, *,
+                        want_entropy: bool = True, logprob=None, entropy=None, stream=None):
+    """(logprob[T], entropy[T] or None) of model-precision logits [T, V]."""
+    torch = _torch()
+    lib = load()
+    _dev(logits, "logits")
+    T, V = logits.shape
+    ld = _rows(logits, "logits")
+    targets = _vec(targets, "targets", torch.int64)
+    mask = _vec(mask, "mask", torch.uint8)
+    if logprob is None:
+        logprob = torch.empty(T, dtype=torch.float32, device=logits.device)
+    if want_entropy and entropy is None:
+        entropy = torch.empty(T, dtype=torch.float32, device=logits.device)
+    st = lib.lp_logprobs_entropy(_ptr(logits), _dtype_code(logits), T, V, ld, _ptr(targets), _ptr(mask),
+                                 float(temperature), int(chunk_rows), _ptr(logprob), _ptr(entropy), _stream(stream))
+    check("lp_logprobs_entropy", st)
+    return logprob, entropy
+
+
+def lp_lm_head_workspace_bytes(T: int, h: int, V: int, tile_rows: int, backward: bool) -> int:
+    return int(load().lp_lm_head_workspace_bytes(T, h, V, tile_rows, 1 if backward else 0))
+
+
+def _workspace(nbytes: int, device, workspace):
+    torch = _torch()
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError("workspace too small")
+        return workspace
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def lp_lm_head_logprobs_entropy(hidden, weight, targets, mask=None, temperature: float = 1.0,
+                                tile_rows: int = 4096, *, want_entropy: bool = True, want_lse: bool = True,
+                                workspace=None, stream=None):
+    """(logprob, entropy, lse) of softmax(hidden @ weight^T / temperature); bf16 hidden [T, h], weight [V, h]."""
+    torch = _torch()
+    lib = load()
+    _dev(hidden, "hidden")
+    _dev(weight, "weight")
+    if hidden.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16:
+        raise TypeError("hidden and weight must be bfloat16")
+    T, h = hidden.shape
+    V, h2 = weight.shape
+    if h2 != h:
+        raise ValueError("hidden and weight disagree on h")
+    targets = _vec(targets, "targets", torch.int64)
+    mask = _vec(mask, "mask", torch.uint8)
+    dev = hidden.device
+    lp = torch.empty(T, dtype=torch.float32, device=dev)
+    H = torch.empty(T, dtype=torch.float32, device=dev) if want_entropy else None
+    lse = torch.empty(T, dtype=torch.float32, device=dev) if want_lse else None
+    nbytes = lp_lm_head_workspace_bytes(T, h, V, tile_rows, False)
+    ws = _workspace(nbytes, dev, workspace)
+    st = lib.lp_lm_head_logprobs_entropy(_ptr(hidden), _rows(hidden, "hidden"), _ptr(weight), _rows(weight, "weight"),
+                                         T, h, V, _ptr(targets), _ptr(mask), float(temperature), int(tile_rows),
+                                         _ptr(lp), _ptr(H), _ptr(lse), _ptr(ws), ws.numel(), _stream(stream))
+    check("lp_lm_head_logprobs_entropy", st)
+    return lp, H, lse
+
+
+def lp_lm_head_logprobs_entropy_backward(hidden, weight, targets, mask, temperature: float, tile_rows: int,
+                                         lse, entropy, grad_logprob, grad_entropy=None, *,
+                                         need_grad_hidden: bool = True, need_grad_weight: bool = True,
+                                         workspace=None, stream=None) -> Tuple:
+    """(grad_hidden fp32 [T, h] or None, grad_weight fp32 [V, h] or None)."""
+    torch = _torch()
+    lib = load()
+    _dev(hidden, "hidden")
+    _dev(weight, "weight")
+    T, h = hidden.shape
+    V = weight.shape[0]
+    targets = _vec(targets, "targets", torch.int64)
+    mask = _vec(mask, "mask", torch.uint8)
+    lse = _vec(lse, "lse", torch.float32)
+    entropy = _vec(entropy, "entropy", torch.float32)
+    grad_logprob = _vec(grad_logprob, "grad_logprob", torch.float32)
+    grad_entropy = _vec(grad_entropy, "grad_entropy", torch.float32)
+    dev = hidden.device
+    dH = torch.empty((T, h), dtype=torch.float32, device=dev) if need_grad_hidden else None
+    dW = torch.empty((V, h), dtype=torch.float32, device=dev) if need_grad_weight else None
+    nbytes = lp_lm_head_workspace_bytes(T, h, V, tile_rows, True)
+    ws = _workspace(nbytes, dev, workspace)
+    st = lib.lp_lm_head_logprobs_entropy_backward(
+        _ptr(hidden), _rows(hidden, "hidden"), _ptr(weight), _rows(weight, "weight"), T, h, V, _ptr(targets),
+        _ptr(mask), float(temperature), int(tile_rows), _ptr(lse), _ptr(entropy), _ptr(grad_logprob),
+        _ptr(grad_entropy), _ptr(dH), _ptr(dW), _ptr(ws), ws.numel(), _stream(stream))
+    check("lp_lm_head_logprobs_entropy_backward", st)
+    return dH, dW
+
+
+def lp_kl_full_vocab(student, teacher, targets=None, diff_mask=None, *, want_target_logprobs: bool = True,
+                     stream=None):
+    """(kl, lp_student, lp_teacher, prob_diff); the last three are None without targets."""
+    torch = _torch()
+    lib = load()
+    _dev(student, "student")
+    _dev(teacher, "teacher")
+    if student.dtype != teacher.dtype or student.shape != teacher.shape:
+        raise ValueError("student and teacher must have the same dtype and shape")
+    T, V = student.shape
+    targets = _vec(targets, "targets", torch.int64)
+    diff_mask = _vec(diff_mask, "diff_mask", torch.uint8)
+    dev = student.device
+    kl = torch.empty(T, dtype=torch.float32, device=dev)
+    lps = lpt = diff = None
+    if targets is not None and want_target_logprobs:
+        lps = torch.empty(T, dtype=torch.float32, device=dev)
+        lpt = torch.empty(T, dtype=torch.float32, device=dev)
+        diff = torch.empty(T, dtype=torch.float32, device=dev)
+    st = lib.lp_kl_full_vocab(_ptr(student), _ptr(teacher), _dtype_code(student), T, V, _rows(student, "student"),
+                              _rows(teacher, "teacher"), _ptr(kl), _ptr(targets), _ptr(diff_mask), _ptr(lps),
+                              _ptr(lpt), _ptr(diff), _stream(stream))
+    check("lp_kl_full_vocab", st)
+    return kl, lps, lpt, diff
+
+
+def lp_prob_diff(lp_a, lp_b, mask=None, *, out=None, stream=None):
+    """mask * |exp(lp_a) - exp(lp_b)| elementwise (fp32 vectors)."""
+    torch = _torch()
+    lib = load()
+    lp_a = _vec(lp_a, "lp_a", torch.float32)
+    lp_b = _vec(lp_b, "lp_b", torch.float32)
+    mask = _vec(mask, "mask", torch.uint8)
+    n = lp_a.numel()
+    if lp_b.numel() != n or (mask is not None and mask.numel() != n):
+        raise ValueError("lp_a, lp_b and mask must have the same length")
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device=lp_a.device)
+    st = lib.lp_prob_diff(_ptr(lp_a), _ptr(lp_b), _ptr(mask), n, _ptr(out), _stream(stream))
+    check("lp_prob_diff", st)
+    return out

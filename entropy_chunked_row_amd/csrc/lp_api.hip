@@ -1,0 +1,250 @@
+// C ABI of liblp.so (declared in include/lp.h): argument validation, chunk /
+// tile scheduling and stream-ordered launches.  Every check runs on the host
+// before anything is launched; a rejected call touches no output.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/lp.h"
+#include "lp_internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = {0};
+
+lp_status fail(lp_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+lp_status ok() {
+  g_err[0] = 0;
+  return LP_OK;
+}
+
+lp_status hip_fail(hipError_t e, const char* where) {
+  return fail(LP_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+constexpr double kLog2eD = 1.44269504088896340736;
+constexpr int64_t kMaxV = (int64_t(1) << 30);
+
+bool temperature_applies(float t) { return t > 0.f && t != 1.f; }
+
+// c = log2(e) / tau_effective, rounded once.
+float exp2_scale(float temperature) {
+  const double tau = temperature_applies(temperature) ? static_cast<double>(temperature) : 1.0;
+  return static_cast<float>(kLog2eD / tau);
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t dtype_bytes(int d) { return d == LP_FP32 ? 4 : 2; }
+
+}  // namespace
+
+extern "C" {
+
+int lp_version(void) { return 100; }
+
+const char* lp_status_string(int status) {
+  switch (status) {
+    case LP_OK: return "LP_OK";
+    case LP_ERR_INVALID_ARGUMENT: return "LP_ERR_INVALID_ARGUMENT";
+    case LP_ERR_UNSUPPORTED: return "LP_ERR_UNSUPPORTED";
+    case LP_ERR_WORKSPACE_TOO_SMALL: return "LP_ERR_WORKSPACE_TOO_SMALL";
+    case LP_ERR_HIP: return "LP_ERR_HIP";
+    default: return "unknown status";
+  }
+}
+
+const char* lp_last_error(void) { return g_err; }
+
+lp_status lp_logprobs_entropy(const void* logits, lp_dtype dtype, int64_t T, int64_t V, int64_t ld,
+                              const int64_t* targets, const uint8_t* mask, float temperature,
+                              int64_t chunk_rows, float* logprob, float* entropy, void* stream) {
+  if (dtype != LP_BF16 && dtype != LP_FP16 && dtype != LP_FP32)
+    return fail(LP_ERR_INVALID_ARGUMENT, "lp_logprobs_entropy: unknown dtype %d", static_cast<int>(dtype));
+  if (T < 0) return fail(LP_ERR_INVALID_ARGUMENT, "lp_logprobs_entropy: T < 0");
+  if (V <= 0 || V > kMaxV) return fail(LP_ERR_INVALID_ARGUMENT, "lp_logprobs_entropy: V out of range (1..2^30)");
+  if (ld < V) return fail(LP_ERR_INVALID_ARGUMENT, "lp_logprobs_entropy: ld < V");
+  if (!isfinite(temperature)) return fail(LP_ERR_INVALID_ARGUMENT, "lp_logprobs_entropy: temperature not finite");
+  if (T == 0) return ok();
+  if (!logits || !targets || !logprob)
+    return fail(LP_ERR_INVALID_ARGUMENT, "lp_logprobs_entropy: logits, targets and logprob are required");
+  if (!aligned(logits, dtype_bytes(dtype)) || !aligned(logprob, 4) || (entropy && !aligned(entropy, 4)) ||
+      !aligned(targets, 8))
+    return fail(LP_ERR_INVALID_ARGUMENT, "lp_logprobs_entropy: misaligned pointer");
+  const int64_t chunk = (chunk_rows <= 0 || chunk_rows > T) ? T : chunk_rows;
+  if (chunk > 0x7fffffff) return fail(LP_ERR_UNSUPPORTED, "lp_logprobs_entropy: more than 2^31-1 rows per chunk");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  lp::RowArgs a;
+  a.x = logits;
+  a.ld = ld;
+  a.V = static_cast<int>(V);
+  a.targets = targets;
+  a.mask = mask;
+  a.c = exp2_scale(temperature);
+  a.logprob = logprob;
+  a.entropy = entropy;
+  for (int64_t r0 = 0; r0 < T; r0 += chunk) {
+    a.row0 = r0;
+    a.rows = (T - r0 < chunk) ? (T - r0) : chunk;
+    hipError_t e = lp::launch_logprobs_entropy(static_cast<int>(dtype), a, s);
+    if (e != hipSuccess) return hip_fail(e, "lp_logprobs_entropy launch");
+  }
+  return ok();
+}
+
+size_t lp_lm_head_workspace_bytes(int64_t T, int64_t h, int64_t V, int64_t tile_rows, int backward) {
+  lp::LMHeadWorkspace w;
+  if (!lp::lmhead_workspace_layout(T, h, V, tile_rows, backward, &w)) return 0;
+  return w.total;
+}
+
+static lp_status check_lmhead(const char* fn, const void* hidden, int64_t ld_h, const void* weight, int64_t ld_w,
+                              int64_t T, int64_t h, int64_t V, const int64_t* targets, float temperature,
+                              int64_t tile_rows, void* workspace, size_t workspace_bytes, int backward,
+                              lp::LMHeadWorkspace* w) {
+  if (T < 0) return fail(LP_ERR_INVALID_ARGUMENT, "%s: T < 0", fn);
+  if (h <= 0 || V <= 0 || V > kMaxV || h > kMaxV)
+    return fail(LP_ERR_INVALID_ARGUMENT, "%s: h and V must be in 1..2^30", fn);
+  if (ld_h < h || ld_w < h) return fail(LP_ERR_INVALID_ARGUMENT, "%s: ld_h and ld_w must be >= h", fn);
+  if (tile_rows <= 0) return fail(LP_ERR_INVALID_ARGUMENT, "%s: tile_rows must be > 0", fn);
+  if (!isfinite(temperature)) return fail(LP_ERR_INVALID_ARGUMENT, "%s: temperature not finite", fn);
+  if (h % 8 || ld_h % 8 || ld_w % 8)
+    return fail(LP_ERR_UNSUPPORTED, "%s: h, ld_h and ld_w must be multiples of 8", fn);
+  if (T == 0) return LP_OK;
+  if (!hidden || !weight || !targets) return fail(LP_ERR_INVALID_ARGUMENT, "%s: hidden, weight, targets required", fn);
+  if (!aligned(hidden, 16) || !aligned(weight, 16))
+    return fail(LP_ERR_UNSUPPORTED, "%s: hidden and weight must be 16-byte aligned", fn);
+  if (!aligned(targets, 8)) return fail(LP_ERR_INVALID_ARGUMENT, "%s: misaligned targets", fn);
+  if (!lp::lmhead_workspace_layout(T, h, V, tile_rows, backward, w))
+    return fail(LP_ERR_INVALID_ARGUMENT, "%s: sizes overflow the workspace layout", fn);
+  if (!workspace || workspace_bytes < w->total)
+    return fail(LP_ERR_WORKSPACE_TOO_SMALL, "%s: workspace needs %zu bytes, got %zu", fn, w->total,
+                workspace ? workspace_bytes : size_t(0));
+  if (!aligned(workspace, 256)) return fail(LP_ERR_INVALID_ARGUMENT, "%s: workspace must be 256-byte aligned", fn);
+  return LP_OK;
+}
+
+static lp::LMHeadShape make_shape(const void* hidden, int64_t ld_h, const void* weight, int64_t ld_w, int64_t T,
+                                  int64_t h, int64_t V, const int64_t* targets, const uint8_t* mask,
+                                  float temperature, int64_t tile_rows) {
+  lp::LMHeadShape sh;
+  sh.hidden = static_cast<const uint16_t*>(hidden);
+  sh.ld_h = ld_h;
+  sh.weight = static_cast<const uint16_t*>(weight);
+  sh.ld_w = ld_w;
+  sh.T = T;
+  sh.h = static_cast<int>(h);
+  sh.V = static_cast<int>(V);
+  sh.targets = targets;
+  sh.mask = mask;
+  sh.c = exp2_scale(temperature);
+  sh.inv_tau = temperature_applies(temperature) ? 1.0f / temperature : 1.0f;
+  sh.tile_rows = tile_rows;
+  return sh;
+}
+
+lp_status lp_lm_head_logprobs_entropy(const void* hidden, int64_t ld_h, const void* weight, int64_t ld_w,
+                                      int64_t T, int64_t h, int64_t V, const int64_t* targets,
+                                      const uint8_t* mask, float temperature, int64_t tile_rows,
+                                      float* logprob, float* entropy, float* lse, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  const char* fn = "lp_lm_head_logprobs_entropy";
+  lp::LMHeadWorkspace w;
+  lp_status st = check_lmhead(fn, hidden, ld_h, weight, ld_w, T, h, V, targets, temperature, tile_rows,
+                              workspace, workspace_bytes, 0, &w);
+  if (st != LP_OK) return st;
+  if (T == 0) return ok();
+  if (!logprob) return fail(LP_ERR_INVALID_ARGUMENT, "%s: logprob is required", fn);
+  lp::LMHeadShape sh = make_shape(hidden, ld_h, weight, ld_w, T, h, V, targets, mask, temperature, tile_rows);
+  hipError_t e = lp::launch_lmhead_forward(sh, logprob, entropy, lse, static_cast<char*>(workspace), w,
+                                           static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return ok();
+}
+
+lp_status lp_lm_head_logprobs_entropy_backward(const void* hidden, int64_t ld_h, const void* weight,
+                                               int64_t ld_w, int64_t T, int64_t h, int64_t V,
+                                               const int64_t* targets, const uint8_t* mask,
+                                               float temperature, int64_t tile_rows, const float* lse,
+                                               const float* entropy, const float* grad_logprob,
+                                               const float* grad_entropy, float* grad_hidden,
+                                               float* grad_weight, void* workspace, size_t workspace_bytes,
+                                               void* stream) {
+  const char* fn = "lp_lm_head_logprobs_entropy_backward";
+  lp::LMHeadWorkspace w;
+  lp_status st = check_lmhead(fn, hidden, ld_h, weight, ld_w, T, h, V, targets, temperature, tile_rows,
+                              workspace, workspace_bytes, 1, &w);
+  if (st != LP_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T == 0) {
+    // no rows: the weight gradient is still defined (all zero)
+    if (grad_weight) {
+      hipError_t e = lp::launch_zero_f32(grad_weight, V * h, s);
+      if (e != hipSuccess) return hip_fail(e, fn);
+    }
+    return ok();
+  }
+  if (!lse || !entropy || !grad_logprob)
+    return fail(LP_ERR_INVALID_ARGUMENT, "%s: lse, entropy and grad_logprob are required", fn);
+  lp::LMHeadShape sh = make_shape(hidden, ld_h, weight, ld_w, T, h, V, targets, mask, temperature, tile_rows);
+  hipError_t e = lp::launch_lmhead_backward(sh, lse, entropy, grad_logprob, grad_entropy, grad_hidden,
+                                            grad_weight, static_cast<char*>(workspace), w, s);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return ok();
+}
+
+lp_status lp_kl_full_vocab(const void* student, const void* teacher, lp_dtype dtype, int64_t T, int64_t V,
+                           int64_t ld_s, int64_t ld_t, float* kl, const int64_t* targets,
+                           const uint8_t* diff_mask, float* lp_student, float* lp_teacher, float* prob_diff,
+                           void* stream) {
+  const char* fn = "lp_kl_full_vocab";
+  if (dtype != LP_BF16 && dtype != LP_FP16)
+    return fail(LP_ERR_INVALID_ARGUMENT, "%s: dtype must be LP_BF16 or LP_FP16", fn);
+  if (T < 0) return fail(LP_ERR_INVALID_ARGUMENT, "%s: T < 0", fn);
+  if (V <= 0 || V > kMaxV) return fail(LP_ERR_INVALID_ARGUMENT, "%s: V out of range (1..2^30)", fn);
+  if (ld_s < V || ld_t < V) return fail(LP_ERR_INVALID_ARGUMENT, "%s: ld_s and ld_t must be >= V", fn);
+  if (!targets && (lp_student || lp_teacher || prob_diff))
+    return fail(LP_ERR_INVALID_ARGUMENT, "%s: lp_student/lp_teacher/prob_diff need targets", fn);
+  if (T == 0) return ok();
+  if (T > 0x7fffffff) return fail(LP_ERR_UNSUPPORTED, "%s: more than 2^31-1 rows", fn);
+  if (!student || !teacher || !kl) return fail(LP_ERR_INVALID_ARGUMENT, "%s: student, teacher, kl required", fn);
+  if (!aligned(student, 2) || !aligned(teacher, 2) || (targets && !aligned(targets, 8)))
+    return fail(LP_ERR_INVALID_ARGUMENT, "%s: misaligned pointer", fn);
+  lp::KLArgs a;
+  a.student = student;
+  a.teacher = teacher;
+  a.ld_s = ld_s;
+  a.ld_t = ld_t;
+  a.V = static_cast<int>(V);
+  a.T = T;
+  a.c = static_cast<float>(kLog2eD);
+  a.kl = kl;
+  a.targets = targets;
+  a.diff_mask = diff_mask;
+  a.lp_student = lp_student;
+  a.lp_teacher = lp_teacher;
+  a.prob_diff = prob_diff;
+  hipError_t e = lp::launch_kl_full_vocab(static_cast<int>(dtype), a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return ok();
+}
+
+lp_status lp_prob_diff(const float* lp_a, const float* lp_b, const uint8_t* mask, int64_t n, float* out,
+                       void* stream) {
+  if (n < 0) return fail(LP_ERR_INVALID_ARGUMENT, "lp_prob_diff: n < 0");
+  if (n == 0) return ok();
+  if (!lp_a || !lp_b || !out) return fail(LP_ERR_INVALID_ARGUMENT, "lp_prob_diff: lp_a, lp_b, out required");
+  hipError_t e = lp::launch_prob_diff(lp_a, lp_b, mask, n, out, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "lp_prob_diff");
+  return ok();
+}
+
+}  // extern "C"

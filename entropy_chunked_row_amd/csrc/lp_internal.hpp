@@ -1,0 +1,105 @@
+// Internal interface between the C-ABI host layer (lp_api.cpp) and the kernel
+// translation units.  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lp {
+
+// RAII bracket around one kernel launch: records HIP events on the launch
+// stream when timing is enabled (lp_timing_enable), else does nothing.
+class TimedLaunch {
+ public:
+  TimedLaunch(const char* name, hipStream_t s);
+  ~TimedLaunch();
+  TimedLaunch(const TimedLaunch&) = delete;
+  TimedLaunch& operator=(const TimedLaunch&) = delete;
+
+ private:
+  const char* name_;
+  hipStream_t s_;
+  hipEvent_t a_;
+};
+
+// Logits-input rows [row0, row0 + rows) of a [T x ld] matrix.
+struct RowArgs {
+  const void* x;
+  int64_t ld;
+  int V;
+  int64_t row0;
+  int64_t rows;
+  const int64_t* targets;
+  const uint8_t* mask;
+  float c;  // log2(e) / tau_effective, rounded once on the host
+  float* logprob;
+  float* entropy;
+};
+
+struct KLArgs {
+  const void* student;
+  const void* teacher;
+  int64_t ld_s, ld_t;
+  int V;
+  int64_t T;
+  float c;  // log2(e)
+  float* kl;
+  const int64_t* targets;
+  const uint8_t* diff_mask;
+  float* lp_student;
+  float* lp_teacher;
+  float* prob_diff;
+};
+
+hipError_t launch_logprobs_entropy(int dtype, const RowArgs& a, hipStream_t s);
+hipError_t launch_kl_full_vocab(int dtype, const KLArgs& a, hipStream_t s);
+hipError_t launch_prob_diff(const float* a, const float* b, const uint8_t* mask, int64_t n, float* out,
+                            hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// fused LM head
+// ---------------------------------------------------------------------------
+
+struct LMHeadShape {
+  const uint16_t* hidden;  // bf16 bits [T x ld_h]
+  int64_t ld_h;
+  const uint16_t* weight;  // bf16 bits [V x ld_w]
+  int64_t ld_w;
+  int64_t T;
+  int h;
+  int V;
+  const int64_t* targets;
+  const uint8_t* mask;
+  float c;        // log2(e) / tau_effective
+  float inv_tau;  // 1 / tau_effective
+  int64_t tile_rows;
+};
+
+// Workspace carve-up shared by forward and backward (offsets in bytes from the
+// 256-byte aligned base).
+struct LMHeadWorkspace {
+  size_t idx_off;     // int32 [T]      scored-row indices, ascending
+  size_t count_off;   // int32 [1]      number of scored rows
+  size_t part_off;    // float [tile_rows x n_vblocks x 3]   (forward)
+  size_t zy_off;      // float [tile_rows]                   (forward)
+  size_t dz_off;      // bf16 [tile_rows x Vpad]             (backward)
+  size_t total;
+  int n_vblocks;
+  int64_t vpad;
+};
+
+bool lmhead_workspace_layout(int64_t T, int64_t h, int64_t V, int64_t tile_rows, int backward,
+                             LMHeadWorkspace* w);
+
+// Zero-fill with a kernel (not a memset node, so callers may capture it).
+hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s);
+
+hipError_t launch_lmhead_forward(const LMHeadShape& sh, float* logprob, float* entropy, float* lse,
+                                 char* ws, const LMHeadWorkspace& w, hipStream_t s);
+
+hipError_t launch_lmhead_backward(const LMHeadShape& sh, const float* lse, const float* entropy,
+                                  const float* grad_logprob, const float* grad_entropy, float* grad_hidden,
+                                  float* grad_weight, char* ws, const LMHeadWorkspace& w, hipStream_t s);
+
+}  // namespace lp

@@ -1,0 +1,703 @@
+// Fused LM head on gfx950: forward log-prob / entropy and the
+// recompute-based backward, without a [rows x vocab] logits buffer.
+//
+// miles PR #4645 ("How it works"): the scored rows are selected before the
+// output layer (prompt rows are never multiplied by the weight), processed a
+// tile of rows at a time, and the backward replays each tile.  Here:
+//
+//   k_compact       mask -> ascending scored-row list idx[] + count (device
+//                   side, so the host never waits); zero-fills the per-row
+//                   outputs of unscored rows.
+//   k_fwd_tile      per tile: MFMA GEMM logits^T = W . H_tile^T with vocab as
+//                   the MFMA row dimension, so each lane's accumulators hold
+//                   one token's logits for 16 vocab rows per 32x32 tile; the
+//                   epilogue folds them into that token's (mc, s, a) state in
+//                   registers, merges across lanes / waves and writes one
+//                   partial state per (row, vocab block), plus the target
+//                   logit from the block that owns the target column.
+//   k_fwd_merge     merges a row's partial states in a fixed order and writes
+//                   log-prob, entropy and log-sum-exp.
+//   backward        k_bwd_dz recomputes the tile's logits with the same GEMM
+//                   and writes dL/dlogits (bf16) in both [row][vocab] and
+//                   [vocab][row] order; k_bwd_dhidden (= dZ . W, K = vocab) and
+//                   k_bwd_dweight (dW += dZ^T . H_tile, K = tile rows) are
+//                   NT GEMMs on those buffers and on transposed copies of W
+//                   and of the tile's hidden rows.
+#include "lp_device.hpp"
+#include "lp_gemm.hpp"
+#include "lp_internal.hpp"
+
+namespace lp {
+
+namespace {
+
+constexpr float kLog2eF = 1.44269504088896340736f;
+
+using FwdCfg = GemmCfg<128, 128, 64, 2, 2>;
+using BwdCfg = GemmCfg<128, 128, 64, 2, 2>;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+// Logical tile -> (vocab block, token block): groups of kGroupV vocab blocks
+// sweep all token blocks, token-block-major inside a group, so consecutive
+// workgroups on one XCD share both weight and hidden strips in its L2.
+constexpr int kGroupV = 8;
+__device__ __forceinline__ void tile_coords(int L, int n_vb, int n_nb, int& vb, int& nb) {
+  const int full = n_vb / kGroupV;
+  const int g = L / (kGroupV * n_nb);
+  if (g < full) {
+    const int w = L - g * kGroupV * n_nb;
+    nb = w / kGroupV;
+    vb = g * kGroupV + w % kGroupV;
+  } else {
+    const int w = L - full * kGroupV * n_nb;
+    const int gsz = n_vb - full * kGroupV;
+    nb = w / gsz;
+    vb = full * kGroupV + w % gsz;
+  }
+}
+
+}  // namespace
+
+bool lmhead_workspace_layout(int64_t T, int64_t h, int64_t V, int64_t tile_rows, int backward,
+                             LMHeadWorkspace* w) {
+  if (T < 0 || h <= 0 || V <= 0 || tile_rows <= 0) return false;
+  if (T > 0x7fffffff || V > (int64_t(1) << 30) || h > (int64_t(1) << 30)) return false;
+  const int64_t tr = tile_rows < (T > 0 ? T : 1) ? tile_rows : (T > 0 ? T : 1);
+  w->n_vblocks = static_cast<int>((V + FwdCfg::BM - 1) / FwdCfg::BM);
+  w->vpad = static_cast<int64_t>(align_up(static_cast<size_t>(V), 64));
+  size_t off = 0;
+  w->idx_off = off;
+  off = align_up(off + static_cast<size_t>(T > 0 ? T : 1) * 4, 256);
+  w->count_off = off;
+  off += 256;
+  w->part_off = w->zy_off = w->dz_off = 0;
+  if (!backward) {
+    w->part_off = off;
+    off = align_up(off + static_cast<size_t>(tr) * w->n_vblocks * 3 * 4, 256);
+    w->zy_off = off;
+    off = align_up(off + static_cast<size_t>(tr) * 4, 256);
+  } else {
+    const size_t tpad = align_up(static_cast<size_t>(tr), 64);
+    w->dz_off = off;  // dZ [tpad x vpad], dZ^T [vpad x tpad], W^T [h x vpad], H_tile^T [h x tpad]
+    off = align_up(off + tpad * static_cast<size_t>(w->vpad) * 2, 256);
+    off = align_up(off + tpad * static_cast<size_t>(w->vpad) * 2, 256);
+    off = align_up(off + static_cast<size_t>(h) * static_cast<size_t>(w->vpad) * 2, 256);
+    off = align_up(off + static_cast<size_t>(h) * tpad * 2, 256);
+  }
+  w->total = off;
+  return true;
+}
+
+// ---------------------------------------------------------------------------
+// scored-row compaction
+// ---------------------------------------------------------------------------
+
+__global__ void __launch_bounds__(1024) k_compact(const uint8_t* __restrict__ mask, int64_t T, int* __restrict__ idx,
+                                                  int* __restrict__ count, float* o1, float* o2, float* o3) {
+  __shared__ int sums[1024];
+  const int tid = threadIdx.x;
+  const int64_t per = (T + 1023) / 1024;
+  const int64_t b = tid * per;
+  const int64_t e = (b + per < T) ? b + per : T;
+  int c = 0;
+  for (int64_t i = b; i < e; ++i) c += (mask == nullptr || mask[i] != 0) ? 1 : 0;
+  sums[tid] = c;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = tid >= off ? sums[tid - off] : 0;
+    __syncthreads();
+    sums[tid] += v;
+    __syncthreads();
+  }
+  int pos = sums[tid] - c;
+  for (int64_t i = b; i < e; ++i) {
+    if (mask == nullptr || mask[i] != 0) {
+      idx[pos++] = static_cast<int>(i);
+    } else {
+      if (o1) o1[i] = 0.f;
+      if (o2) o2[i] = 0.f;
+      if (o3) o3[i] = 0.f;
+    }
+  }
+  if (tid == 1023) *count = sums[1023];
+}
+
+// ---------------------------------------------------------------------------
+// forward
+// ---------------------------------------------------------------------------
+
+struct FwdArgs {
+  const uint16_t* weight;
+  int64_t ld_w;
+  const uint16_t* hidden;
+  int64_t ld_h;
+  int h, V;
+  const int* idx;
+  const int* count;
+  const int64_t* targets;
+  float c;
+  int64_t tile_base;
+  int tile_rows;
+  int n_vb, n_nb;
+  float* part;  // [tile_rows][n_vb][3]
+  float* zy;    // [tile_rows]
+};
+
+template <class C>
+__global__ void __launch_bounds__(C::NT) k_fwd_tile(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
+  int vb, nb;
+  tile_coords(xcd_remap(blockIdx.x, a.n_vb * a.n_nb), a.n_vb, a.n_nb, vb, nb);
+  const int count = *a.count;
+  const int64_t rem = static_cast<int64_t>(count) - a.tile_base;
+  const int rows = static_cast<int>(rem < a.tile_rows ? rem : a.tile_rows);
+  const int n0 = nb * C::BN;
+  if (n0 >= rows) return;
+  const int v0 = vb * C::BM;
+
+  GemmOperands op;
+  op.a = a.weight + static_cast<int64_t>(v0) * a.ld_w;
+  op.lda = a.ld_w;
+  op.M = a.V - v0;
+  op.b = a.hidden;
+  op.ldb = a.ld_h;
+  op.b_rows = a.idx + a.tile_base + n0;
+  op.N = rows - n0;
+  op.K = a.h;
+  f32x16_t acc[C::MI][C::NI];
+  gemm_tile<C>(op, 0, 0, lds, acc);
+
+  // epilogue: per token column, fold this block's vocab rows into a state
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave % C::WGM, wn = wave / C::WGM;
+  const int vlane = v0 + wm * C::WTM + 4 * (lane >> 5);
+  Stat* sm = reinterpret_cast<Stat*>(lds);  // [WGM][BN] states, reused after the K loop
+  const float c = a.c;
+#pragma unroll
+  for (int ni = 0; ni < C::NI; ++ni) {
+    const int nl = wn * C::WTN + ni * 32 + (lane & 31);
+    const int r = n0 + nl;  // row within the tile
+    const bool valid_row = r < rows;
+    int64_t y = -1;
+    if (valid_row) y = a.targets[a.idx[a.tile_base + r]];
+    float x[C::MI * 16];
+    Stat st = stat_empty();
+    float zsel = 0.f;
+    bool found = false;
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int v = vlane + mi * 32 + 8 * (i >> 2) + (i & 3);
+        const float z = acc[mi][ni][i];
+        // rows past V hold zeros from the GEMM: give them probability 0
+        // (-inf, folded with the clamped push below)
+        x[mi * 16 + i] = (v < a.V) ? z : -INFINITY;
+        if (v == y) {
+          zsel = z;
+          found = true;
+        }
+      }
+    stat_push<true, C::MI * 16, 16>(st, x, c);
+    Stat o;
+    o.mc = __shfl_xor(st.mc, 32, 64);
+    o.s = __shfl_xor(st.s, 32, 64);
+    o.a = __shfl_xor(st.a, 32, 64);
+    st = stat_merge(st, o);
+    if (found && valid_row) a.zy[r] = zsel;
+    if (lane < 32) sm[wm * C::BN + nl] = st;
+  }
+  __syncthreads();
+  if (wm == 0 && lane < 32) {
+#pragma unroll
+    for (int ni = 0; ni < C::NI; ++ni) {
+      const int nl = wn * C::WTN + ni * 32 + lane;
+      const int r = n0 + nl;
+      if (r < rows) {
+        Stat st = sm[nl];
+#pragma unroll
+        for (int k = 1; k < C::WGM; ++k) st = stat_merge(st, sm[k * C::BN + nl]);
+        float* p = a.part + (static_cast<int64_t>(r) * a.n_vb + vb) * 3;
+        p[0] = st.mc;
+        p[1] = st.s;
+        p[2] = st.a;
+      }
+    }
+  }
+}
+
+struct MergeArgs {
+  const float* part;
+  const float* zy;
+  int n_vb;
+  const int* idx;
+  const int* count;
+  const int64_t* targets;
+  int V;
+  float c;
+  int64_t tile_base;
+  int tile_rows;
+  float* logprob;
+  float* entropy;
+  float* lse;
+};
+
+__global__ void __launch_bounds__(256) k_fwd_merge(MergeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int count = *a.count;
+  const int64_t rem = static_cast<int64_t>(count) - a.tile_base;
+  const int rows = static_cast<int>(rem < a.tile_rows ? rem : a.tile_rows);
+  if (r >= rows) return;
+  const float* p = a.part + static_cast<int64_t>(r) * a.n_vb * 3;
+  Stat st = stat_empty();
+  for (int vb = lane; vb < a.n_vb; vb += 64) st = stat_merge(st, Stat{p[vb * 3], p[vb * 3 + 1], p[vb * 3 + 2]});
+  st = stat_wave_allreduce(st);
+  if (lane == 0) {
+    const int row = a.idx[a.tile_base + r];
+    const int64_t y = a.targets[row];
+    const float l2s = log2f(st.s);
+    float lp = __builtin_nanf("");
+    if (y >= 0 && y < a.V) lp = (fmaf(a.zy[r], a.c, -st.mc) - l2s) * kLn2;
+    a.logprob[row] = lp;
+    if (a.entropy) a.entropy[row] = (l2s - st.a / st.s) * kLn2;
+    if (a.lse) a.lse[row] = (st.mc + l2s) * kLn2;
+  }
+}
+
+hipError_t launch_lmhead_forward(const LMHeadShape& sh, float* logprob, float* entropy, float* lse, char* ws,
+                                 const LMHeadWorkspace& w, hipStream_t s) {
+  int* idx = reinterpret_cast<int*>(ws + w.idx_off);
+  int* count = reinterpret_cast<int*>(ws + w.count_off);
+  float* part = reinterpret_cast<float*>(ws + w.part_off);
+  float* zy = reinterpret_cast<float*>(ws + w.zy_off);
+  {
+    TimedLaunch tl("k_compact", s);
+    hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, s, sh.mask, sh.T, idx, count, logprob, entropy, lse);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t tr = sh.tile_rows < sh.T ? sh.tile_rows : sh.T;
+  const int n_vb = w.n_vblocks;
+  const int n_nb = static_cast<int>((tr + FwdCfg::BN - 1) / FwdCfg::BN);
+  for (int64_t base = 0; base < sh.T; base += tr) {
+    FwdArgs a;
+    a.weight = sh.weight;
+    a.ld_w = sh.ld_w;
+    a.hidden = sh.hidden;
+    a.ld_h = sh.ld_h;
+    a.h = sh.h;
+    a.V = sh.V;
+    a.idx = idx;
+    a.count = count;
+    a.targets = sh.targets;
+    a.c = sh.c;
+    a.tile_base = base;
+    a.tile_rows = static_cast<int>(tr);
+    a.n_vb = n_vb;
+    a.n_nb = n_nb;
+    a.part = part;
+    a.zy = zy;
+    {
+      TimedLaunch tl("k_fwd_tile", s);
+      hipLaunchKernelGGL(k_fwd_tile<FwdCfg>, dim3(static_cast<unsigned>(n_vb) * n_nb), dim3(FwdCfg::NT), 0, s, a);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    MergeArgs m;
+    m.part = part;
+    m.zy = zy;
+    m.n_vb = n_vb;
+    m.idx = idx;
+    m.count = count;
+    m.targets = sh.targets;
+    m.V = sh.V;
+    m.c = sh.c;
+    m.tile_base = base;
+    m.tile_rows = static_cast<int>(tr);
+    m.logprob = logprob;
+    m.entropy = entropy;
+    m.lse = lse;
+    {
+      TimedLaunch tl("k_fwd_merge", s);
+      hipLaunchKernelGGL(k_fwd_merge, dim3(static_cast<unsigned>((tr + 3) / 4)), dim3(256), 0, s, m);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// ---------------------------------------------------------------------------
+// backward
+// ---------------------------------------------------------------------------
+
+// Tiled transpose of bf16 rows: dst[c][r] = src_row(r)[c] for r < nr, c < nc;
+// zero for r in [nr, nr_pad), c < nc.  src_row(r) = src + rows[r] * ld (or r * ld).
+__global__ void __launch_bounds__(256) k_transpose_bf16(const uint16_t* __restrict__ src, int64_t ld,
+                                                        const int* __restrict__ rows, const int* __restrict__ count,
+                                                        int64_t row_base, int nr_static, int nr_cap, int nr_pad,
+                                                        int nc, uint16_t* __restrict__ dst, int64_t ldd) {
+  __shared__ uint16_t t[64][65];
+  int nr = nr_static;
+  if (count) {
+    const int64_t rem = static_cast<int64_t>(*count) - row_base;
+    nr = static_cast<int>(rem < nr_cap ? (rem > 0 ? rem : 0) : nr_cap);
+  }
+  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  if (r0 >= nr_pad) return;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int k = ty; k < 64; k += 4) {
+    const int r = r0 + k, cc = c0 + tx;
+    uint16_t v = 0;
+    if (r < nr && cc < nc) {
+      const int64_t sr = rows ? static_cast<int64_t>(rows[row_base + r]) : static_cast<int64_t>(r);
+      v = src[sr * ld + cc];
+    }
+    t[k][tx] = v;
+  }
+  __syncthreads();
+  for (int k = ty; k < 64; k += 4) {
+    const int cc = c0 + k, r = r0 + tx;
+    if (cc < nc && r < nr_pad) dst[static_cast<int64_t>(cc) * ldd + r] = t[tx][k];
+  }
+}
+
+__global__ void __launch_bounds__(256) k_zero_f32(float* __restrict__ p, int64_t n) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0.f;
+}
+
+hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  {
+    TimedLaunch tl("k_zero_f32", s);
+    hipLaunchKernelGGL(k_zero_f32, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, p, n);
+  }
+  return hipGetLastError();
+}
+
+__global__ void __launch_bounds__(256) k_zero_unscored_rows(const uint8_t* __restrict__ mask, int64_t T, int h,
+                                                            float* __restrict__ out) {
+  const int64_t row = blockIdx.x;
+  if (row >= T) return;
+  if (mask != nullptr && mask[row] == 0) {
+    float* p = out + row * h;
+    for (int j = threadIdx.x; j < h; j += 256) p[j] = 0.f;
+  }
+}
+
+struct DzArgs {
+  const uint16_t* weight;
+  int64_t ld_w;
+  const uint16_t* hidden;
+  int64_t ld_h;
+  int h, V;
+  int64_t vpad;
+  const int* idx;
+  const int* count;
+  const int64_t* targets;
+  const float* lse;
+  const float* entropy;
+  const float* g_lp;
+  const float* g_H;
+  float c, inv_tau;
+  int64_t tile_base;
+  int tile_rows;
+  int64_t tpad;
+  int n_vb, n_nb;
+  uint16_t* dz;   // [tpad][vpad]
+  uint16_t* dzt;  // [vpad][tpad] or nullptr
+};
+
+template <class C>
+__global__ void __launch_bounds__(C::NT) k_bwd_dz(DzArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
+  int vb, nb;
+  tile_coords(xcd_remap(blockIdx.x, a.n_vb * a.n_nb), a.n_vb, a.n_nb, vb, nb);
+  const int count = *a.count;
+  const int64_t rem = static_cast<int64_t>(count) - a.tile_base;
+  const int rows = static_cast<int>(rem < a.tile_rows ? rem : a.tile_rows);
+  const int rows8 = (rows + 7) & ~7;  // rows the K of the weight-gradient GEMM spans
+  const int n0 = nb * C::BN;
+  if (rows <= 0 || n0 >= rows8) return;
+  const int v0 = vb * C::BM;
+  GemmOperands op;
+  op.a = a.weight + static_cast<int64_t>(v0) * a.ld_w;
+  op.lda = a.ld_w;
+  op.M = a.V - v0;
+  op.b = a.hidden;
+  op.ldb = a.ld_h;
+  op.b_rows = a.idx + a.tile_base + n0;
+  op.N = rows - n0;
+  op.K = a.h;
+  f32x16_t acc[C::MI][C::NI];
+  gemm_tile<C>(op, 0, 0, lds, acc);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave % C::WGM, wn = wave / C::WGM;
+  const int vlane = v0 + wm * C::WTM + 4 * (lane >> 5);
+#pragma unroll
+  for (int ni = 0; ni < C::NI; ++ni) {
+    const int r = n0 + wn * C::WTN + ni * 32 + (lane & 31);
+    if (r >= rows8) continue;
+    const bool valid = r < rows;
+    int64_t y = -1;
+    float l2 = 0.f, mu = 0.f, glp = 0.f, gh = 0.f;
+    if (valid) {
+      const int row = a.idx[a.tile_base + r];
+      y = a.targets[row];
+      const float L = a.lse[row];
+      l2 = L * kLog2eF;
+      mu = L - a.entropy[row];
+      glp = a.g_lp[row];
+      gh = a.g_H ? a.g_H[row] : 0.f;
+    }
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int vq = vlane + mi * 32 + 8 * q;
+        uint16_t outv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int v = vq + j;
+          float d = 0.f;
+          if (valid && v < a.V) {
+            const float z = acc[mi][ni][q * 4 + j];
+            const float p = fast_exp2(fmaf(z, a.c, -l2));
+            const float zt = z * a.inv_tau;
+            const float onehot = (v == y) ? 1.f : 0.f;
+            d = a.inv_tau * (glp * (onehot - p) - gh * p * (zt - mu));
+          }
+          outv[j] = f32_to_bf16_rne(d);
+        }
+        if (vq < a.vpad) {
+          uint2 pk;
+          pk.x = static_cast<uint32_t>(outv[0]) | (static_cast<uint32_t>(outv[1]) << 16);
+          pk.y = static_cast<uint32_t>(outv[2]) | (static_cast<uint32_t>(outv[3]) << 16);
+          *reinterpret_cast<uint2*>(a.dz + static_cast<int64_t>(r) * a.vpad + vq) = pk;
+          if (a.dzt) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) a.dzt[static_cast<int64_t>(vq + j) * a.tpad + r] = outv[j];
+          }
+        }
+      }
+  }
+}
+
+// out rows: dst[row_of(m)][n] = D[m][n] (store) or += (accumulate).
+struct OutGemmArgs {
+  GemmOperands op;
+  const int* count;    // device count (tile-relative rows) or nullptr
+  int64_t tile_base;
+  int tile_rows;
+  int mode;            // 0: A rows = tile rows (M from count), K static; 1: K from count (rows8)
+  const int* out_rows; // gather for output rows (indexes into idx) or nullptr
+  float* out;
+  int64_t ldo;
+  int accumulate;
+  int n_mb, n_nb;
+};
+
+template <class C>
+__global__ void __launch_bounds__(C::NT) k_out_gemm(OutGemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
+  int mb, nb;
+  tile_coords(xcd_remap(blockIdx.x, g.n_mb * g.n_nb), g.n_mb, g.n_nb, mb, nb);
+  GemmOperands op = g.op;
+  int rows = 0;
+  if (g.count) {
+    const int64_t rem = static_cast<int64_t>(*g.count) - g.tile_base;
+    rows = static_cast<int>(rem < g.tile_rows ? (rem > 0 ? rem : 0) : g.tile_rows);
+  }
+  if (g.mode == 0) {
+    op.M = rows;
+  } else {
+    op.K = (rows + 7) & ~7;
+  }
+  const int m0 = mb * C::BM, n0 = nb * C::BN;
+  if (m0 >= op.M) return;
+  if (g.mode == 1 && op.K == 0 && g.accumulate) return;
+  GemmOperands opb = op;
+  opb.a = op.a + static_cast<int64_t>(m0) * op.lda;
+  opb.M = op.M - m0;
+  if (op.b_rows == nullptr) {
+    opb.b = op.b + static_cast<int64_t>(n0) * op.ldb;
+  } else {
+    opb.b_rows = op.b_rows + n0;
+  }
+  opb.N = op.N - n0;
+  f32x16_t acc[C::MI][C::NI];
+  gemm_tile<C>(opb, 0, 0, lds, acc);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave % C::WGM, wn = wave / C::WGM;
+#pragma unroll
+  for (int ni = 0; ni < C::NI; ++ni) {
+    const int n = n0 + wn * C::WTN + ni * 32 + (lane & 31);
+    if (n >= op.N) continue;
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int m = m0 + wm * C::WTM + mi * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+        if (m < op.M) {
+          const int64_t orow = g.out_rows ? static_cast<int64_t>(g.out_rows[g.tile_base + m]) : static_cast<int64_t>(m);
+          float* p = g.out + orow * g.ldo + n;
+          *p = g.accumulate ? (*p + acc[mi][ni][i]) : acc[mi][ni][i];
+        }
+      }
+  }
+}
+
+hipError_t launch_lmhead_backward(const LMHeadShape& sh, const float* lse, const float* entropy,
+                                  const float* grad_logprob, const float* grad_entropy, float* grad_hidden,
+                                  float* grad_weight, char* ws, const LMHeadWorkspace& w, hipStream_t s) {
+  using C = BwdCfg;
+  int* idx = reinterpret_cast<int*>(ws + w.idx_off);
+  int* count = reinterpret_cast<int*>(ws + w.count_off);
+  const int64_t tr = sh.tile_rows < sh.T ? sh.tile_rows : sh.T;
+  const int64_t tpad = static_cast<int64_t>(align_up(static_cast<size_t>(tr), 64));
+  const int64_t vpad = w.vpad;
+  uint16_t* dz = reinterpret_cast<uint16_t*>(ws + w.dz_off);
+  size_t off = align_up(w.dz_off + static_cast<size_t>(tpad) * vpad * 2, 256);
+  uint16_t* dzt = reinterpret_cast<uint16_t*>(ws + off);
+  off = align_up(off + static_cast<size_t>(tpad) * vpad * 2, 256);
+  uint16_t* wt = reinterpret_cast<uint16_t*>(ws + off);
+  off = align_up(off + static_cast<size_t>(sh.h) * vpad * 2, 256);
+  uint16_t* ht = reinterpret_cast<uint16_t*>(ws + off);
+
+  {
+    TimedLaunch tl("k_compact", s);
+    hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, s, sh.mask, sh.T, idx, count, static_cast<float*>(nullptr),
+                       static_cast<float*>(nullptr), static_cast<float*>(nullptr));
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (grad_hidden) {
+    {
+      TimedLaunch tl("k_zero_unscored_rows", s);
+      hipLaunchKernelGGL(k_zero_unscored_rows, dim3(static_cast<unsigned>(sh.T)), dim3(256), 0, s, sh.mask, sh.T, sh.h,
+                         grad_hidden);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // W^T [h x vpad], zero past V
+    dim3 g(static_cast<unsigned>((vpad + 63) / 64), static_cast<unsigned>((sh.h + 63) / 64));
+    {
+      TimedLaunch tl("k_transpose_bf16", s);
+      hipLaunchKernelGGL(k_transpose_bf16, g, dim3(256), 0, s, sh.weight, sh.ld_w, static_cast<const int*>(nullptr),
+                         static_cast<const int*>(nullptr), int64_t(0), sh.V, sh.V, static_cast<int>(vpad), sh.h, wt,
+                         vpad);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  const int n_vb = w.n_vblocks;
+  const int n_nb = static_cast<int>((tr + C::BN - 1) / C::BN);
+  for (int64_t base = 0; base < sh.T; base += tr) {
+    DzArgs d;
+    d.weight = sh.weight;
+    d.ld_w = sh.ld_w;
+    d.hidden = sh.hidden;
+    d.ld_h = sh.ld_h;
+    d.h = sh.h;
+    d.V = sh.V;
+    d.vpad = vpad;
+    d.idx = idx;
+    d.count = count;
+    d.targets = sh.targets;
+    d.lse = lse;
+    d.entropy = entropy;
+    d.g_lp = grad_logprob;
+    d.g_H = grad_entropy;
+    d.c = sh.c;
+    d.inv_tau = sh.inv_tau;
+    d.tile_base = base;
+    d.tile_rows = static_cast<int>(tr);
+    d.tpad = tpad;
+    d.n_vb = n_vb;
+    d.n_nb = n_nb;
+    d.dz = dz;
+    d.dzt = grad_weight ? dzt : nullptr;
+    {
+      TimedLaunch tl("k_bwd_dz", s);
+      hipLaunchKernelGGL(k_bwd_dz<C>, dim3(static_cast<unsigned>(n_vb) * n_nb), dim3(C::NT), 0, s, d);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+
+    if (grad_hidden) {
+      // dHidden[idx[r]] = dZ[r] . W  :  A = dZ [rows x vpad], B = W^T [h x vpad], K = vpad
+      OutGemmArgs g;
+      g.op.a = dz;
+      g.op.lda = vpad;
+      g.op.M = 0;
+      g.op.b = wt;
+      g.op.ldb = vpad;
+      g.op.b_rows = nullptr;
+      g.op.N = sh.h;
+      g.op.K = static_cast<int>(vpad);
+      g.count = count;
+      g.tile_base = base;
+      g.tile_rows = static_cast<int>(tr);
+      g.mode = 0;
+      g.out_rows = idx;
+      g.out = grad_hidden;
+      g.ldo = sh.h;
+      g.accumulate = 0;
+      g.n_mb = static_cast<int>((tr + C::BM - 1) / C::BM);
+      g.n_nb = (sh.h + C::BN - 1) / C::BN;
+      {
+        TimedLaunch tl("k_out_gemm_dhidden", s);
+        hipLaunchKernelGGL(k_out_gemm<C>, dim3(static_cast<unsigned>(g.n_mb) * g.n_nb), dim3(C::NT), 0, s, g);
+      }
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (grad_weight) {
+      // H_tile^T [h x tpad]
+      dim3 gt(static_cast<unsigned>(tpad / 64), static_cast<unsigned>((sh.h + 63) / 64));
+      {
+        TimedLaunch tl("k_transpose_bf16", s);
+        hipLaunchKernelGGL(k_transpose_bf16, gt, dim3(256), 0, s, sh.hidden, sh.ld_h, static_cast<const int*>(idx),
+                           static_cast<const int*>(count), base, 0, static_cast<int>(tr), static_cast<int>(tpad), sh.h,
+                           ht, tpad);
+      }
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      // dW (+)= dZ^T . H_tile : A = dZ^T [V x tpad], B = H_tile^T [h x tpad], K = rows8
+      OutGemmArgs g;
+      g.op.a = dzt;
+      g.op.lda = tpad;
+      g.op.M = sh.V;
+      g.op.b = ht;
+      g.op.ldb = tpad;
+      g.op.b_rows = nullptr;
+      g.op.N = sh.h;
+      g.op.K = 0;
+      g.count = count;
+      g.tile_base = base;
+      g.tile_rows = static_cast<int>(tr);
+      g.mode = 1;
+      g.out_rows = nullptr;
+      g.out = grad_weight;
+      g.ldo = sh.h;
+      g.accumulate = base == 0 ? 0 : 1;
+      g.n_mb = (sh.V + C::BM - 1) / C::BM;
+      g.n_nb = (sh.h + C::BN - 1) / C::BN;
+      {
+        TimedLaunch tl("k_out_gemm_dweight", s);
+        hipLaunchKernelGGL(k_out_gemm<C>, dim3(static_cast<unsigned>(g.n_mb) * g.n_nb), dim3(C::NT), 0, s, g);
+      }
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+}  // namespace lp

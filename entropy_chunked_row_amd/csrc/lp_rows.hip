@@ -1,0 +1,337 @@
+// Memory-bound row reductions over model-precision logits:
+//   * k_logprobs_entropy: log p(target) and entropy per scored row
+//     (miles PR #2764 summary, "关键源码片段": chunked upcast to fp32, then the
+//     temperature divide in fp32, then the log-softmax at the target).
+//   * k_kl_full_vocab: exact KL(teacher || student) per row plus both target
+//     log-probs and the masked |exp(a) - exp(b)| (DeepSeek-V4 book ch.19,
+//     "TileLang KL Kernel"; msprobe probs_diff page §3.2).
+//   * k_prob_diff: the same diff on two given log-prob arrays.
+//
+// One workgroup per row.  Each lane streams 16-byte vectors (8 bf16/fp16 or
+// 4 fp32) with non-temporal loads, U vectors in flight, widens them in
+// registers and folds them into its running (mc, s, a) state; the workgroup
+// then merges the lane states.  Nothing but the per-row outputs is written.
+#include "lp_device.hpp"
+#include "lp_internal.hpp"
+
+namespace lp {
+
+// ---------------------------------------------------------------------------
+// logits-input log-prob + entropy
+// ---------------------------------------------------------------------------
+
+template <class Tr, int NT, int U, bool GUARD>
+__device__ __forceinline__ Stat scan_row(const char* rowp, const RowSplit<Tr>& sp, float c) {
+  constexpr int P = Tr::kPerVec;
+  const int tid = threadIdx.x;
+  Stat st = stat_empty();
+  if (tid < sp.head) {
+    float x = Tr::load1(rowp, tid);
+    stat_push<GUARD, 1, 1>(st, &x, c);
+  }
+  const u32x4* vp = reinterpret_cast<const u32x4*>(rowp + sp.head * Tr::kBytes);
+  int i = tid;
+  for (; i + (U - 1) * NT < sp.nvec; i += U * NT) {
+    u32x4 w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) w[u] = __builtin_nontemporal_load(vp + i + u * NT);
+    float x[U * P];
+#pragma unroll
+    for (int u = 0; u < U; ++u) Tr::unpack(w[u], x + u * P);
+    stat_push<GUARD, U * P, P>(st, x, c);
+  }
+  for (; i < sp.nvec; i += NT) {
+    const u32x4 w = __builtin_nontemporal_load(vp + i);
+    float x[P];
+    Tr::unpack(w, x);
+    stat_push<GUARD, P, P>(st, x, c);
+  }
+  if (tid < sp.tail) {
+    float x = Tr::load1(rowp, sp.head + sp.nvec * P + tid);
+    stat_push<GUARD, 1, 1>(st, &x, c);
+  }
+  return st;
+}
+
+template <class Tr, int NT, int U>
+__global__ void __launch_bounds__(NT) k_logprobs_entropy(RowArgs args) {
+  __shared__ Stat sm[NT / 64];
+  const int64_t row = args.row0 + blockIdx.x;
+  if (args.mask && args.mask[row] == 0) {
+    if (threadIdx.x == 0) {
+      args.logprob[row] = 0.f;
+      if (args.entropy) args.entropy[row] = 0.f;
+    }
+    return;
+  }
+  const char* rowp = static_cast<const char*>(args.x) + row * args.ld * Tr::kBytes;
+  const int V = args.V;
+  const RowSplit<Tr> sp(rowp, V);
+  const float c = args.c;
+  Stat st = stat_block_allreduce<NT>(scan_row<Tr, NT, U, false>(rowp, sp, c), sm);
+  // A -inf logit makes `a` NaN (0 * -inf) while `s` stays finite: redo the
+  // row with the clamped fold.  Every thread holds the same merged state, so
+  // the branch is uniform.
+  if (__builtin_isnan(st.a) && !__builtin_isnan(st.s))
+    st = stat_block_allreduce<NT>(scan_row<Tr, NT, U, true>(rowp, sp, c), sm);
+  if (threadIdx.x == 0) {
+    const float l2s = log2f(st.s);
+    const int64_t y = args.targets[row];
+    float lp = __builtin_nanf("");
+    if (y >= 0 && y < V) {
+      const float ty = fmaf(Tr::load1(rowp, y), c, -st.mc);
+      lp = (ty - l2s) * kLn2;
+    }
+    args.logprob[row] = lp;
+    if (args.entropy) args.entropy[row] = (l2s - st.a / st.s) * kLn2;
+  }
+}
+
+template <class Tr>
+static hipError_t launch_rows_t(const RowArgs& a, hipStream_t s) {
+  const unsigned grid = static_cast<unsigned>(a.rows);
+  TimedLaunch tl("k_logprobs_entropy", s);
+  if (a.V <= 2048) {
+    hipLaunchKernelGGL((k_logprobs_entropy<Tr, 64, 2>), dim3(grid), dim3(64), 0, s, a);
+  } else if (a.V <= 16384) {
+    hipLaunchKernelGGL((k_logprobs_entropy<Tr, 128, 4>), dim3(grid), dim3(128), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((k_logprobs_entropy<Tr, 256, 4>), dim3(grid), dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_logprobs_entropy(int dtype, const RowArgs& a, hipStream_t s) {
+  if (a.rows <= 0) return hipSuccess;
+  switch (dtype) {
+    case 0: return launch_rows_t<Bf16>(a, s);
+    case 1: return launch_rows_t<Fp16>(a, s);
+    default: return launch_rows_t<Fp32>(a, s);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// exact KL(teacher || student) over the full vocabulary
+// ---------------------------------------------------------------------------
+// Student u: (mcu, su).  Teacher v: (mcv, sv) and C = sum_j 2^{tv_j} (v_j - u_j)
+// on the teacher's reference.  Then, with natural-log normalisers
+// lse = ln2 (mc + log2 s):  KL = C / sv - (lse_v - lse_u).
+
+struct KLState {
+  float mcu, su, mcv, sv, C;
+};
+
+template <bool GUARD, int N, int CH>
+__device__ __forceinline__ void kl_push(KLState& st, const float* xu, const float* xv, float c) {
+  float mu = xu[0], mv = xv[0];
+#pragma unroll
+  for (int k = 1; k < N; ++k) {
+    mu = fmaxf(mu, xu[k]);
+    mv = fmaxf(mv, xv[k]);
+  }
+  const float muc = mu * c, mvc = mv * c;
+  if (muc > st.mcu) {
+    if (st.su > 0.f) st.su *= fast_exp2(st.mcu - muc);
+    st.mcu = muc;
+  }
+  if (mvc > st.mcv) {
+    if (st.sv > 0.f) {
+      const float r = fast_exp2(st.mcv - mvc);
+      st.sv *= r;
+      st.C *= r;
+    }
+    st.mcv = mvc;
+  }
+  const float nu = -st.mcu, nv = -st.mcv;
+#pragma unroll
+  for (int g = 0; g < N; g += CH) {
+    float pu = 0.f, pv = 0.f, pc = 0.f;
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const float eu = fast_exp2(fmaf(xu[g + k], c, nu));
+      const float ev = fast_exp2(fmaf(xv[g + k], c, nv));
+      pu += eu;
+      pv += ev;
+      const float d = xv[g + k] - xu[g + k];
+      if (GUARD)
+        pc += (ev > 0.f) ? ev * d : 0.f;
+      else
+        pc = fmaf(ev, d, pc);
+    }
+    st.su += pu;
+    st.sv += pv;
+    st.C += pc;
+  }
+}
+
+__device__ __forceinline__ KLState kl_merge(KLState x, KLState y) {
+  KLState r;
+  r.mcu = fmaxf(x.mcu, y.mcu);
+  r.su = 0.f;
+  if (x.su > 0.f) r.su += x.su * fast_exp2(x.mcu - r.mcu);
+  if (y.su > 0.f) r.su += y.su * fast_exp2(y.mcu - r.mcu);
+  r.mcv = fmaxf(x.mcv, y.mcv);
+  r.sv = 0.f;
+  r.C = 0.f;
+  if (x.sv > 0.f) {
+    const float f = fast_exp2(x.mcv - r.mcv);
+    r.sv += x.sv * f;
+    r.C += x.C * f;
+  }
+  if (y.sv > 0.f) {
+    const float f = fast_exp2(y.mcv - r.mcv);
+    r.sv += y.sv * f;
+    r.C += y.C * f;
+  }
+  return r;
+}
+
+template <int NT>
+__device__ __forceinline__ KLState kl_block_allreduce(KLState st, KLState* sm) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    KLState o;
+    o.mcu = __shfl_xor(st.mcu, off, 64);
+    o.su = __shfl_xor(st.su, off, 64);
+    o.mcv = __shfl_xor(st.mcv, off, 64);
+    o.sv = __shfl_xor(st.sv, off, 64);
+    o.C = __shfl_xor(st.C, off, 64);
+    st = kl_merge(st, o);
+  }
+  constexpr int NW = NT / 64;
+  if (NW == 1) return st;
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) sm[w] = st;
+  __syncthreads();
+  KLState r = sm[0];
+#pragma unroll
+  for (int k = 1; k < NW; ++k) r = kl_merge(r, sm[k]);
+  __syncthreads();
+  return r;
+}
+
+template <class Tr, int NT, int U, bool GUARD>
+__device__ __forceinline__ KLState scan_kl(const char* up, const char* vp, int V, bool aligned_pair, float c) {
+  constexpr int P = Tr::kPerVec;
+  const int tid = threadIdx.x;
+  KLState st{kNegBig, 0.f, kNegBig, 0.f, 0.f};
+  if (aligned_pair) {
+    // both rows share the same 16-byte phase
+    const RowSplit<Tr> sp(up, V);
+    for (int j = tid; j < sp.head; j += NT) {
+      float xu = Tr::load1(up, j), xv = Tr::load1(vp, j);
+      kl_push<GUARD, 1, 1>(st, &xu, &xv, c);
+    }
+    const u32x4* uq = reinterpret_cast<const u32x4*>(up + sp.head * Tr::kBytes);
+    const u32x4* vq = reinterpret_cast<const u32x4*>(vp + sp.head * Tr::kBytes);
+    int i = tid;
+    for (; i + (U - 1) * NT < sp.nvec; i += U * NT) {
+      u32x4 wu[U], wv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        wu[u] = __builtin_nontemporal_load(uq + i + u * NT);
+        wv[u] = __builtin_nontemporal_load(vq + i + u * NT);
+      }
+      float xu[U * P], xv[U * P];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        Tr::unpack(wu[u], xu + u * P);
+        Tr::unpack(wv[u], xv + u * P);
+      }
+      kl_push<GUARD, U * P, P>(st, xu, xv, c);
+    }
+    for (; i < sp.nvec; i += NT) {
+      float xu[P], xv[P];
+      Tr::unpack(__builtin_nontemporal_load(uq + i), xu);
+      Tr::unpack(__builtin_nontemporal_load(vq + i), xv);
+      kl_push<GUARD, P, P>(st, xu, xv, c);
+    }
+    const int t0 = sp.head + sp.nvec * P;
+    for (int j = t0 + tid; j < V; j += NT) {
+      float xu = Tr::load1(up, j), xv = Tr::load1(vp, j);
+      kl_push<GUARD, 1, 1>(st, &xu, &xv, c);
+    }
+  } else {
+    for (int j = tid; j < V; j += NT) {
+      float xu = Tr::load1(up, j), xv = Tr::load1(vp, j);
+      kl_push<GUARD, 1, 1>(st, &xu, &xv, c);
+    }
+  }
+  return st;
+}
+
+template <class Tr, int NT, int U>
+__global__ void __launch_bounds__(NT) k_kl_full_vocab(KLArgs args) {
+  __shared__ KLState sm[NT / 64];
+  const int64_t row = blockIdx.x;
+  const char* up = static_cast<const char*>(args.student) + row * args.ld_s * Tr::kBytes;
+  const char* vp = static_cast<const char*>(args.teacher) + row * args.ld_t * Tr::kBytes;
+  const int V = args.V;
+  const bool aligned_pair = ((reinterpret_cast<uintptr_t>(up) ^ reinterpret_cast<uintptr_t>(vp)) & 15u) == 0;
+  const float c = args.c;
+  KLState st = kl_block_allreduce<NT>(scan_kl<Tr, NT, U, false>(up, vp, V, aligned_pair, c), sm);
+  if (__builtin_isnan(st.C) && !__builtin_isnan(st.su) && !__builtin_isnan(st.sv))
+    st = kl_block_allreduce<NT>(scan_kl<Tr, NT, U, true>(up, vp, V, aligned_pair, c), sm);
+  if (threadIdx.x == 0) {
+    const float l2u = log2f(st.su), l2v = log2f(st.sv);
+    const float dlse = ((st.mcv - st.mcu) + (l2v - l2u)) * kLn2;
+    args.kl[row] = st.C / st.sv - dlse;
+    if (args.targets) {
+      const int64_t y = args.targets[row];
+      float lpu = __builtin_nanf(""), lpv = __builtin_nanf("");
+      if (y >= 0 && y < V) {
+        lpu = (fmaf(Tr::load1(up, y), c, -st.mcu) - l2u) * kLn2;
+        lpv = (fmaf(Tr::load1(vp, y), c, -st.mcv) - l2v) * kLn2;
+      }
+      if (args.lp_student) args.lp_student[row] = lpu;
+      if (args.lp_teacher) args.lp_teacher[row] = lpv;
+      if (args.prob_diff) {
+        const bool keep = args.diff_mask == nullptr || args.diff_mask[row] != 0;
+        args.prob_diff[row] = keep ? fabsf(expf(lpu) - expf(lpv)) : 0.f;
+      }
+    }
+  }
+}
+
+template <class Tr>
+static hipError_t launch_kl_t(const KLArgs& a, hipStream_t s) {
+  const unsigned grid = static_cast<unsigned>(a.T);
+  TimedLaunch tl("k_kl_full_vocab", s);
+  if (a.V <= 2048) {
+    hipLaunchKernelGGL((k_kl_full_vocab<Tr, 64, 2>), dim3(grid), dim3(64), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((k_kl_full_vocab<Tr, 256, 2>), dim3(grid), dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_kl_full_vocab(int dtype, const KLArgs& a, hipStream_t s) {
+  if (a.T <= 0) return hipSuccess;
+  return dtype == 0 ? launch_kl_t<Bf16>(a, s) : launch_kl_t<Fp16>(a, s);
+}
+
+// ---------------------------------------------------------------------------
+// elementwise prob diff
+// ---------------------------------------------------------------------------
+
+__global__ void __launch_bounds__(256) k_prob_diff(const float* __restrict__ a, const float* __restrict__ b,
+                                                   const uint8_t* __restrict__ mask, int64_t n,
+                                                   float* __restrict__ out) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const bool keep = mask == nullptr || mask[i] != 0;
+    out[i] = keep ? fabsf(expf(a[i]) - expf(b[i])) : 0.f;
+  }
+}
+
+hipError_t launch_prob_diff(const float* a, const float* b, const uint8_t* mask, int64_t n, float* out,
+                            hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  TimedLaunch tl("k_prob_diff", s);
+  hipLaunchKernelGGL(k_prob_diff, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a, b, mask, n, out);
+  return hipGetLastError();
+}
+
+}  // namespace lp

@@ -1,0 +1,191 @@
+/*
+ * lp.h -- C ABI of liblp.so: per-token log-probabilities, entropy and exact
+ * full-vocabulary KL over a large vocabulary on MI355X (gfx950), computed a
+ * chunk (or tile) of rows at a time, never materialising [rows x vocab] fp32
+ * logits.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers: every tensor argument is a DEVICE pointer owned by the caller.
+ *   The library never allocates, frees or keeps device memory; scratch comes
+ *   only from the caller's `workspace`.  Inputs are read-only and are never
+ *   modified (unlike an in-place cross-entropy).
+ * Layout: row-major.  A [rows x cols] matrix has row r at base + r * ld
+ *   elements, ld >= cols.  Targets are int64, one per row.  A mask is uint8,
+ *   one per row, nonzero = the row is scored; NULL = every row is scored.
+ * Streams: `stream` is a hipStream_t (NULL = the null stream).  Calls are
+ *   asynchronous on it; outputs are valid once the stream reaches the call.
+ * Errors: every argument is checked on the host before anything is launched.
+ *   A non-LP_OK return launches nothing and leaves every output untouched;
+ *   lp_last_error() then holds a thread-local description.  No exception or
+ *   abort crosses this ABI.  A failure reported by the HIP runtime while
+ *   launching gives LP_ERR_HIP.
+ * Outputs are fp32.  Rows that are not scored get 0 in every per-row output
+ *   and their targets are never read.
+ * Temperature: applied to the fp32 values after the exact upcast, and only
+ *   when temperature > 0 and temperature != 1 (otherwise the scale is 1) --
+ *   the upcast helper `_upcast_chunk_to_fp32` on the miles PR #2764 summary
+ *   page (prhub.com.cn), sections "实现拆解" item 2 and "关键源码片段".
+ *   NaN or infinite temperatures are rejected.
+ * Targets: a scored row needs 0 <= target < V; otherwise its log-prob is NaN
+ *   (no device-to-host check is made); its entropy is still computed.
+ * Special values: -inf logits are zero-probability entries and add nothing to
+ *   the entropy; a row containing NaN or +inf, or only -inf, gives NaN.
+ */
+#ifndef LP_H_
+#define LP_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum lp_status {
+  LP_OK = 0,
+  LP_ERR_INVALID_ARGUMENT = 1,
+  LP_ERR_UNSUPPORTED = 2,
+  LP_ERR_WORKSPACE_TOO_SMALL = 3,
+  LP_ERR_HIP = 4
+} lp_status;
+
+typedef enum lp_dtype { LP_BF16 = 0, LP_FP16 = 1, LP_FP32 = 2 } lp_dtype;
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+int lp_version(void);
+
+/* Static text for a status code ("LP_OK", ...); "unknown status" otherwise. */
+const char* lp_status_string(int status);
+
+/* Thread-local description of the last non-OK return on this thread ("" if none). */
+const char* lp_last_error(void);
+
+/*
+ * Log-prob of the target and entropy of each scored row of model-precision
+ * logits.
+ *
+ * Follows calculate_log_probs_and_entropy on the miles PR #2764 summary page,
+ * "关键源码片段": the logits stay in model precision; each chunk of rows is
+ * widened to fp32 (here: in registers, never stored), divided by the
+ * temperature in fp32, and reduced to log softmax at the target and the
+ * Shannon entropy (nats) of softmax(z / temperature) over all V entries.
+ *
+ * logits      [T x ld] of `dtype` (LP_BF16, LP_FP16 or LP_FP32), ld >= V.
+ * targets     int64 [T].  mask: uint8 [T] or NULL.
+ * temperature see the file header.
+ * chunk_rows  rows per launch; <= 0 means all rows in one launch.  Chunks have
+ *             chunk_rows rows with a short last chunk (5 rows in chunks of 2
+ *             -> 2, 2, 1).  Results do not depend on chunk_rows, bit for bit.
+ * logprob     fp32 [T] (required).  entropy: fp32 [T] or NULL.
+ * T == 0 returns LP_OK without launching.  Needs no workspace.
+ */
+lp_status lp_logprobs_entropy(const void* logits, lp_dtype dtype, int64_t T, int64_t V, int64_t ld,
+                              const int64_t* targets, const uint8_t* mask, float temperature,
+                              int64_t chunk_rows, float* logprob, float* entropy, void* stream);
+
+/*
+ * Bytes of device workspace the fused LM-head calls need (256-byte aligned
+ * base required).  backward = 0 for lp_lm_head_logprobs_entropy, 1 for the
+ * backward.  Returns 0 for invalid sizes.
+ */
+size_t lp_lm_head_workspace_bytes(int64_t T, int64_t h, int64_t V, int64_t tile_rows, int backward);
+
+/*
+ * Fused LM head forward: log-prob and entropy of softmax(hidden @ weight^T /
+ * temperature) without writing the logits.
+ *
+ * Follows the fused_lm_head backend of miles PR #4645, "How it works": the
+ * scored rows are selected first (prompt rows are never multiplied by the
+ * output weight), then processed `tile_rows` at a time; here each tile's
+ * logits live only in MFMA accumulators (fp32, never rounded to bf16) and are
+ * folded straight into per-row running max / sum / entropy terms.
+ *
+ * hidden      bf16 [T x ld_h], ld_h >= h.  weight: bf16 [V x ld_w], ld_w >= h.
+ * targets     int64 [T].  mask: uint8 [T] or NULL.
+ * tile_rows   scored rows per tile, required, > 0 (no hidden default).
+ * logprob     fp32 [T] (required); entropy fp32 [T] or NULL; lse fp32 [T] or
+ *             NULL: log-sum-exp of the tempered logits, saved for the backward.
+ * workspace   >= lp_lm_head_workspace_bytes(T, h, V, tile_rows, 0) bytes.
+ * Restrictions (LP_ERR_UNSUPPORTED): h % 8 != 0, ld_h % 8 != 0, ld_w % 8 != 0,
+ *   misaligned (not 16-byte) hidden or weight pointers.
+ */
+lp_status lp_lm_head_logprobs_entropy(const void* hidden, int64_t ld_h, const void* weight, int64_t ld_w,
+                                      int64_t T, int64_t h, int64_t V, const int64_t* targets,
+                                      const uint8_t* mask, float temperature, int64_t tile_rows,
+                                      float* logprob, float* entropy, float* lse, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
+/*
+ * Backward of the fused LM head for the loss
+ *   L = sum over scored rows t of grad_logprob[t] * logprob[t] + grad_entropy[t] * entropy[t].
+ * Recompute-based, as miles PR #4645 "How it works" describes: each tile's
+ * logits are rebuilt by the same GEMM, turned into dL/dlogits in the
+ * epilogue, then multiplied back by the weight (hidden gradient) and by the
+ * tile's hidden rows (weight gradient).
+ *
+ * lse, entropy  fp32 [T] as written by the forward (same inputs, temperature).
+ * grad_logprob  fp32 [T] (required); grad_entropy fp32 [T] or NULL (= 0).
+ * grad_hidden   fp32 [T x h] or NULL: OVERWRITTEN; unscored rows get 0.
+ * grad_weight   fp32 [V x h] or NULL (frozen weight: that GEMM is skipped):
+ *               OVERWRITTEN with the sum over all scored rows.
+ * workspace     >= lp_lm_head_workspace_bytes(T, h, V, tile_rows, 1) bytes.
+ * With no scored rows both gradients are zero-filled.
+ */
+lp_status lp_lm_head_logprobs_entropy_backward(const void* hidden, int64_t ld_h, const void* weight,
+                                               int64_t ld_w, int64_t T, int64_t h, int64_t V,
+                                               const int64_t* targets, const uint8_t* mask,
+                                               float temperature, int64_t tile_rows, const float* lse,
+                                               const float* entropy, const float* grad_logprob,
+                                               const float* grad_entropy, float* grad_hidden,
+                                               float* grad_weight, void* workspace, size_t workspace_bytes,
+                                               void* stream);
+
+/*
+ * Exact full-vocabulary KL(teacher || student) per row, no temperature, in
+ * one pass over both rows.  DeepSeek-V4 book ch.19 "RL / OPD 工程", 名词速通:
+ * "不实例化 logits" and "TileLang KL Kernel" (exact student/teacher KL).
+ *
+ * student, teacher  [T x ld_s], [T x ld_t] of `dtype` (LP_BF16 or LP_FP16).
+ * kl                fp32 [T] (required), every row.
+ * targets           int64 [T] or NULL.  When given, lp_student / lp_teacher
+ *                   (fp32 [T] or NULL) receive log softmax at the target for
+ *                   every row, and prob_diff (fp32 [T] or NULL) receives
+ *                   diff_mask ? |exp(lp_student) - exp(lp_teacher)| : 0, the
+ *                   per-token measure of the msprobe page
+ *                   "逐Token级别的probs_diff监控", §3.2.  diff_mask NULL = all rows.
+ *                   With targets NULL those three outputs must be NULL.
+ * Accumulation is fp32 throughout, so fp16 rows whose plain sums overflow
+ * stay finite.  Needs no workspace.
+ */
+lp_status lp_kl_full_vocab(const void* student, const void* teacher, lp_dtype dtype, int64_t T, int64_t V,
+                           int64_t ld_s, int64_t ld_t, float* kl, const int64_t* targets,
+                           const uint8_t* diff_mask, float* lp_student, float* lp_teacher, float* prob_diff,
+                           void* stream);
+
+/*
+ * out[i] = mask[i] ? |exp(lp_a[i]) - exp(lp_b[i])| : 0 for i < n
+ * (msprobe page "逐Token级别的probs_diff监控", §3.2; an all-zero mask gives an
+ * all-zero result, as in its edge-case table).  mask NULL = all positions.
+ * All arrays fp32 / uint8, device, length n.
+ */
+lp_status lp_prob_diff(const float* lp_a, const float* lp_b, const uint8_t* mask, int64_t n, float* out,
+                       void* stream);
+
+/*
+ * Per-kernel timing (observability; not part of the method).  While enabled,
+ * each library launch is bracketed by two HIP events recorded on its own
+ * stream.  lp_timing_enable(1) clears earlier records and starts recording,
+ * lp_timing_enable(0) clears and stops.  lp_timing_read() waits for the
+ * recorded events of `kernel` (e.g. "k_fwd_tile", "k_logprobs_entropy",
+ * "k_kl_full_vocab") and returns the number of launches and their summed
+ * duration in milliseconds.  Records are process-wide and thread-safe.
+ */
+void lp_timing_enable(int on);
+lp_status lp_timing_read(const char* kernel, int64_t* launches, double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LP_H_ */

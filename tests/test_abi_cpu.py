@@ -1,0 +1,136 @@
+"""CPU checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host (no GPU involved:
+every call here returns before anything is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lp.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\*?(lp_[a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from entropy_chunked_row_amd import _lib
+    return _lib.load()
+
+
+def test_header_lists_the_entry_points():
+    names = header_functions()
+    for want in ("lp_logprobs_entropy", "lp_lm_head_logprobs_entropy", "lp_lm_head_logprobs_entropy_backward",
+                 "lp_lm_head_workspace_bytes", "lp_kl_full_vocab", "lp_prob_diff", "lp_version",
+                 "lp_status_string", "lp_last_error"):
+        assert want in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from entropy_chunked_row_amd import _lib
+    for name in header_functions():
+        assert hasattr(lib, name), name
+        assert name in _lib.SIGNATURES, f"{name} has no ctypes signature"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.lp_version() >= 100
+    assert lib.lp_status_string(0) == b"LP_OK"
+    assert lib.lp_status_string(3) == b"LP_ERR_WORKSPACE_TOO_SMALL"
+    assert lib.lp_status_string(99) == b"unknown status"
+
+
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(dtype=7), 1),
+    (dict(T=-1), 1),
+    (dict(V=0), 1),
+    (dict(ld=10), 1),             # ld < V
+    (dict(temperature=float("inf")), 1),
+    (dict(temperature=float("nan")), 1),
+    (dict(logits=None), 1),
+    (dict(targets=None), 1),
+    (dict(logprob=None), 1),
+])
+def test_logprobs_entropy_validation(lib, args, code):
+    a = dict(logits=FAKE, dtype=0, T=4, V=16, ld=16, targets=FAKE, mask=None, temperature=0.7, chunk=2,
+             logprob=FAKE, entropy=FAKE)
+    a.update(args)
+    st = lib.lp_logprobs_entropy(a["logits"], a["dtype"], a["T"], a["V"], a["ld"], a["targets"], a["mask"],
+                                 a["temperature"], a["chunk"], a["logprob"], a["entropy"], None)
+    assert st == code
+    assert lib.lp_last_error() != b""
+
+
+def test_empty_input_is_ok_without_launch(lib):
+    assert lib.lp_logprobs_entropy(None, 0, 0, 16, 16, None, None, 0.7, 4, None, None, None) == 0
+    assert lib.lp_last_error() == b""
+    assert lib.lp_kl_full_vocab(None, None, 1, 0, 16, 16, 16, None, None, None, None, None, None, None) == 0
+    assert lib.lp_prob_diff(None, None, None, 0, None, None) == 0
+
+
+def test_workspace_query(lib):
+    f = lib.lp_lm_head_workspace_bytes
+    assert f(0, 5120, 151936, 4096, 0) > 0
+    fw = f(32768, 5120, 151936, 4096, 0)
+    bw = f(32768, 5120, 151936, 4096, 1)
+    assert fw > 0 and bw > fw
+    # forward scratch is O(tile_rows x vocab blocks), far below a [T x V] fp32 buffer
+    assert fw < 32768 * 151936 * 4 / 50
+    assert f(10, 0, 100, 4, 0) == 0 and f(10, 8, 100, 0, 0) == 0 and f(-1, 8, 100, 4, 0) == 0
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(tile_rows=0), 1),
+    (dict(h=12, ld_h=16, ld_w=16), 2),     # h % 8
+    (dict(ld_h=4), 1),
+    (dict(temperature=float("nan")), 1),
+    (dict(ws_bytes=16), 3),
+    (dict(hidden=FAKE + 8), 2),             # not 16-byte aligned
+    (dict(targets=None), 1),
+])
+def test_lm_head_validation(lib, args, code):
+    a = dict(hidden=FAKE, ld_h=64, weight=FAKE, ld_w=64, T=8, h=64, V=100, targets=FAKE, mask=None,
+             temperature=0.7, tile_rows=4, ws=FAKE, ws_bytes=1 << 30)
+    a.update(args)
+    st = lib.lp_lm_head_logprobs_entropy(a["hidden"], a["ld_h"], a["weight"], a["ld_w"], a["T"], a["h"], a["V"],
+                                         a["targets"], a["mask"], a["temperature"], a["tile_rows"], FAKE, None, None,
+                                         a["ws"], a["ws_bytes"], None)
+    assert st == code, lib.lp_last_error()
+
+
+def test_kl_validation(lib):
+    assert lib.lp_kl_full_vocab(FAKE, FAKE, 2, 4, 16, 16, 16, FAKE, None, None, None, None, None, None) == 1
+    assert lib.lp_kl_full_vocab(FAKE, FAKE, 1, 4, 16, 8, 16, FAKE, None, None, None, None, None, None) == 1
+    # target outputs without targets
+    assert lib.lp_kl_full_vocab(FAKE, FAKE, 1, 4, 16, 16, 16, FAKE, None, None, FAKE, None, None, None) == 1
+    assert lib.lp_prob_diff(FAKE, FAKE, None, -1, FAKE, None) == 1
+
+
+def test_product_path_has_no_fallback(tmp_path):
+    """A missing library is an error, not a silent CPU path."""
+    from entropy_chunked_row_amd import _lib
+    with pytest.raises(RuntimeError, match="no CPU fallback"):
+        _lib._lib_backup = _lib._lib
+        _lib._lib = None
+        try:
+            _lib.load(str(tmp_path / "missing.so"))
+        finally:
+            _lib._lib = _lib._lib_backup
+
+
+def test_package_never_imports_the_oracle():
+    pkg = os.path.join(ROOT, "entropy_chunked_row_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.replace("Oracle", "").lower() or f.endswith((".hip", ".hpp")) and \
+                    "import" not in text, f

@@ -1,0 +1,184 @@
+"""GPU parity of the fused LM head (forward and recompute backward) against
+the fp64 oracle.  Tolerances: abs 2e-3 on log-prob / entropy; gradients
+relative Frobenius <= 1e-2 and max|diff| <= 1e-2 * max|ref| per tensor."""
+import numpy as np
+import pytest
+
+import synth
+from oracle import lp_oracle as O
+from tests.helpers import grad_errors, host, max_abs_err, to_dev, to_dev_bits
+
+pytestmark = pytest.mark.gpu
+TOL_FWD = 2e-3
+TOL_GRAD = 1e-2
+
+
+def _lp():
+    import entropy_chunked_row_amd as lp
+    return lp
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _case(T, h, V, seed, scored=0.7, w_sigma=0.05):
+    rng = np.random.default_rng(seed)
+    hid = synth.f32_to_bf16_bits(rng.normal(0, 1, size=(T, h)).astype(np.float32))
+    W = synth.f32_to_bf16_bits(rng.normal(0, w_sigma, size=(V, h)).astype(np.float32))
+    y = rng.integers(0, V, size=T).astype(np.int64)
+    m = (rng.random(T) < scored).astype(np.uint8)
+    return hid, W, y, m
+
+
+def _run_fwd(hid, W, y, m, tau, tile, **kw):
+    return _lp().lp_lm_head_logprobs_entropy(to_dev_bits(hid, "bf16"), to_dev_bits(W, "bf16"), to_dev(y),
+                                             None if m is None else to_dev(m), tau, tile, **kw)
+
+
+def test_tiny_config_forward():
+    cfg = synth.tiny_lm_head()
+    A = cfg.arrays
+    lp, H, lse = _run_fwd(A["hidden"], A["weight"], A["targets"], A["mask"], cfg.temperature, cfg.tile_rows)
+    lp_o, H_o, lse_o = O.lm_head_logprobs_entropy(O.widen_bf16(A["hidden"]), O.widen_bf16(A["weight"]),
+                                                  A["targets"], A["mask"], cfg.temperature)
+    assert max_abs_err(host(lp), lp_o) <= TOL_FWD
+    assert max_abs_err(host(H), H_o) <= TOL_FWD
+    assert max_abs_err(host(lse), lse_o) <= TOL_FWD
+
+
+@pytest.mark.parametrize("T,h,V,tile,tau", [
+    (37, 64, 1031, 16, 0.7),     # ragged vocab, several tiles, short last tile
+    (5, 8, 3, 2, 1.0),           # tiny everything
+    (130, 136, 257, 64, 1.3),    # K not a multiple of the K-step, rows > one block
+    (300, 256, 4099, 4096, 0.7), # one tile bigger than the rows
+    (1, 32, 1, 4, 0.7),          # V = 1
+    (64, 64, 300, 32, 3.0),      # high temperature: rows past V must stay at probability 0
+])
+def test_forward_ragged(T, h, V, tile, tau):
+    hid, W, y, m = _case(T, h, V, seed=T + h + V)
+    lp, H, lse = _run_fwd(hid, W, y, m, tau, tile)
+    lp_o, H_o, lse_o = O.lm_head_logprobs_entropy(O.widen_bf16(hid), O.widen_bf16(W), y, m, tau)
+    assert max_abs_err(host(lp), lp_o) <= TOL_FWD
+    assert max_abs_err(host(H), H_o) <= TOL_FWD
+    assert max_abs_err(host(lse), lse_o) <= TOL_FWD
+    assert np.all(host(lp)[m == 0] == 0)
+
+
+def test_forward_tile_rows_bitwise_invariant():
+    hid, W, y, m = _case(150, 96, 2000, seed=3)
+    ref = [host(t) for t in _run_fwd(hid, W, y, m, 0.7, 4096)]
+    for tile in (1, 7, 64, 149):
+        got = [host(t) for t in _run_fwd(hid, W, y, m, 0.7, tile)]
+        assert all(np.array_equal(a, b) for a, b in zip(ref, got)), tile
+
+
+def test_forward_strided_hidden_and_no_scored_rows():
+    torch = _torch()
+    hid, W, y, m = _case(40, 64, 500, seed=4)
+    big = np.zeros((40, 80), dtype=np.uint16)
+    big[:, :64] = hid
+    hd = to_dev_bits(big, "bf16")[:, :64]
+    lp, H, _ = _lp().lp_lm_head_logprobs_entropy(hd, to_dev_bits(W, "bf16"), to_dev(y), to_dev(m), 0.7, 16)
+    lp_o, H_o, _ = O.lm_head_logprobs_entropy(O.widen_bf16(hid), O.widen_bf16(W), y, m, 0.7)
+    assert max_abs_err(host(lp), lp_o) <= TOL_FWD and max_abs_err(host(H), H_o) <= TOL_FWD
+    z = np.zeros(40, dtype=np.uint8)
+    lp, H, lse = _run_fwd(hid, W, y, z, 0.7, 16)
+    assert not host(lp).any() and not host(H).any() and not host(lse).any()
+    del torch
+
+
+def _backward_case(T, h, V, tile, tau, seed, frozen=False, scored=0.7, with_gH=True):
+    hid, W, y, m = _case(T, h, V, seed, scored=scored)
+    rng = np.random.default_rng(seed + 1)
+    g_lp = rng.normal(0, 1, size=T).astype(np.float32)
+    g_H = rng.normal(0, 0.1, size=T).astype(np.float32) if with_gH else None
+    lp, H, lse = _run_fwd(hid, W, y, m, tau, tile)
+    dH, dW = _lp().lp_lm_head_logprobs_entropy_backward(
+        to_dev_bits(hid, "bf16"), to_dev_bits(W, "bf16"), to_dev(y), to_dev(m), tau, tile, lse, H, to_dev(g_lp),
+        None if g_H is None else to_dev(g_H), need_grad_weight=not frozen)
+    dH_o, dW_o = O.lm_head_backward(O.widen_bf16(hid), O.widen_bf16(W), y, m, tau, g_lp, g_H)
+    return host(dH), (None if dW is None else host(dW)), dH_o, dW_o, m
+
+
+def test_tiny_config_backward():
+    cfg = synth.tiny_lm_head()
+    A = cfg.arrays
+    rng = np.random.default_rng(21)
+    g_lp = rng.normal(0, 1, size=cfg.T).astype(np.float32)
+    g_H = rng.normal(0, 0.1, size=cfg.T).astype(np.float32)
+    lp, H, lse = _run_fwd(A["hidden"], A["weight"], A["targets"], A["mask"], cfg.temperature, cfg.tile_rows)
+    dH, dW = _lp().lp_lm_head_logprobs_entropy_backward(
+        to_dev_bits(A["hidden"], "bf16"), to_dev_bits(A["weight"], "bf16"), to_dev(A["targets"]), to_dev(A["mask"]),
+        cfg.temperature, cfg.tile_rows, lse, H, to_dev(g_lp), to_dev(g_H))
+    dH_o, dW_o = O.lm_head_backward(O.widen_bf16(A["hidden"]), O.widen_bf16(A["weight"]), A["targets"], A["mask"],
+                                    cfg.temperature, g_lp, g_H)
+    for got, want in ((host(dH), dH_o), (host(dW), dW_o)):
+        fro, mad = grad_errors(got, want)
+        assert fro <= TOL_GRAD and mad <= TOL_GRAD, (fro, mad)
+
+
+@pytest.mark.parametrize("T,h,V,tile,tau", [
+    (37, 64, 1031, 16, 0.7),
+    (130, 136, 257, 64, 1.0),
+    (70, 32, 5000, 4096, 1.3),
+])
+def test_backward_ragged(T, h, V, tile, tau):
+    dH, dW, dH_o, dW_o, m = _backward_case(T, h, V, tile, tau, seed=T * 3 + V)
+    for got, want in ((dH, dH_o), (dW, dW_o)):
+        fro, mad = grad_errors(got, want)
+        assert fro <= TOL_GRAD and mad <= TOL_GRAD, (fro, mad)
+    assert not dH[m == 0].any()
+
+
+def test_backward_frozen_weight_and_no_entropy_grad():
+    dH, dW, dH_o, dW_o, m = _backward_case(50, 64, 700, 16, 0.7, seed=5, frozen=True, with_gH=False)
+    assert dW is None
+    fro, mad = grad_errors(dH, dH_o)
+    assert fro <= TOL_GRAD and mad <= TOL_GRAD
+
+
+def test_backward_no_scored_rows():
+    dH, dW, dH_o, dW_o, m = _backward_case(20, 32, 300, 8, 0.7, seed=6, scored=0.0)
+    assert not dH.any() and not dW.any()
+
+
+# ---------------------------------------------------------------------------
+# full-size fused forward: T=32768 packed rows, h=5120, V=151936, tau 0.7, tile 4096
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def lm_full():
+    cfg = synth.LMHead().build()
+    A = cfg.arrays
+    return cfg, A, to_dev_bits(A["hidden"], "bf16"), to_dev_bits(A["weight"], "bf16"), to_dev(A["targets"]), \
+        to_dev(A["mask"])
+
+
+@pytest.mark.timeout(900)
+def test_full_size_forward_sampled_rows(lm_full):
+    cfg, A, hd, Wd, y, m = lm_full
+    lp, H, lse = (host(t) for t in _lp().lp_lm_head_logprobs_entropy(hd, Wd, y, m, cfg.temperature, cfg.tile_rows))
+    scored = np.nonzero(A["mask"])[0]
+    rows = np.unique(np.concatenate([np.random.default_rng(8).choice(scored, 12, replace=False),
+                                     scored[:1], scored[-1:], scored[4095:4097]]))
+    lp_o, H_o, lse_o = _oracle_rows(A, rows, cfg.temperature)
+    assert max_abs_err(lp[rows], lp_o) <= TOL_FWD
+    assert max_abs_err(H[rows], H_o) <= TOL_FWD
+    assert max_abs_err(lse[rows], lse_o) <= TOL_FWD
+    assert np.all(lp[A["mask"] == 0] == 0)
+    assert np.all(np.isfinite(lp[scored])) and np.all(lp[scored] <= 1e-3)
+
+
+def _oracle_rows(A, rows, tau):
+    """Oracle on a subset of rows; the weight is widened block by block inside."""
+    Wbits = A["weight"]
+
+    class _W:
+        shape = Wbits.shape
+
+        def __getitem__(self, sl):
+            return O.widen_bf16(Wbits[sl])
+
+    return O.lm_head_logprobs_entropy(O.widen_bf16(A["hidden"][rows]), _W(), A["targets"][rows], None, tau)

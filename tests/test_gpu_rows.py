@@ -1,0 +1,244 @@
+"""GPU parity of the logits-input path, exact KL and prob diff against the
+fp64 oracle.  Tolerances: abs 1e-5 on log-prob / entropy / KL / diff (the
+logits-input bar; KL and diff take the same bar as a reading)."""
+import math
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import lp_oracle as O
+from tests.helpers import host, max_abs_err, to_dev, to_dev_bits
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-5
+
+
+def _lp():
+    import entropy_chunked_row_amd as lp
+    return lp
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _random_case(T, V, dtype, sigma, seed, scored=0.75):
+    rng = np.random.default_rng(seed)
+    x = rng.normal(0, sigma, size=(T, V)).astype(np.float32)
+    if dtype == "bf16":
+        bits = synth.f32_to_bf16_bits(x)
+    elif dtype == "fp16":
+        bits = synth.f32_to_fp16_bits(x)
+    else:
+        bits = x
+    targets = rng.integers(0, V, size=T).astype(np.int64)
+    mask = (rng.random(T) < scored).astype(np.uint8)
+    return bits, targets, mask
+
+
+def _widen(bits, dtype):
+    return O.widen(bits, dtype)
+
+
+def _dev_logits(bits, dtype):
+    if dtype == "fp32":
+        return to_dev(bits)
+    return to_dev_bits(bits, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("V", [1, 2, 3, 7, 16, 1000, 1031, 4099, 20011])
+@pytest.mark.parametrize("tau", [1.0, 0.7])
+def test_logprobs_entropy_small(dtype, V, tau):
+    T = 37
+    bits, targets, mask = _random_case(T, V, dtype, 3.0, seed=V * 7 + int(tau * 10))
+    lp, H = _lp().lp_logprobs_entropy(_dev_logits(bits, dtype), to_dev(targets), to_dev(mask), tau, 5)
+    lp_o, H_o, _ = O.logprobs_entropy(_widen(bits, dtype), targets, mask, tau)
+    assert max_abs_err(host(lp), lp_o) <= TOL
+    assert max_abs_err(host(H), H_o) <= TOL
+    assert np.all(host(lp)[mask == 0] == 0) and np.all(host(H)[mask == 0] == 0)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_padded_and_misaligned_rows(dtype):
+    """ld > V and a row start off the 16-byte grid exercise head/tail handling."""
+    torch = _torch()
+    T, V, ld = 9, 3001, 3011
+    bits, targets, mask = _random_case(T, ld, dtype, 3.0, seed=11)
+    full = _dev_logits(bits, dtype)
+    view = full[:, 3:3 + V]  # starts 6 bytes into the row, ld = 3011
+    lp, H = _lp().lp_logprobs_entropy(view, to_dev(targets % V), to_dev(mask), 0.7, 4)
+    lp_o, H_o, _ = O.logprobs_entropy(_widen(bits, dtype)[:, 3:3 + V], targets % V, mask, 0.7)
+    assert max_abs_err(host(lp), lp_o) <= TOL and max_abs_err(host(H), H_o) <= TOL
+    del torch
+
+
+def test_chunking_is_bitwise_invariant():
+    T, V = 29, 5003
+    bits, targets, mask = _random_case(T, V, "bf16", 3.0, seed=12)
+    x = _dev_logits(bits, "bf16")
+    y, m = to_dev(targets), to_dev(mask)
+    ref = [host(t) for t in _lp().lp_logprobs_entropy(x, y, m, 0.7, -1)]
+    for c in (0, 1, 3, 4, 28, 29, 100):
+        got = [host(t) for t in _lp().lp_logprobs_entropy(x, y, m, 0.7, c)]
+        assert all(np.array_equal(a, b) for a, b in zip(ref, got)), c
+
+
+def test_temperature_literal_reading_and_repeatability():
+    T, V = 8, 777
+    bits, targets, _ = _random_case(T, V, "bf16", 3.0, seed=13)
+    x, y = _dev_logits(bits, "bf16"), to_dev(targets)
+    base = [host(t) for t in _lp().lp_logprobs_entropy(x, y, None, 1.0)]
+    for tau in (-1.0, 0.0, -3.0):
+        got = [host(t) for t in _lp().lp_logprobs_entropy(x, y, None, tau)]
+        assert all(np.array_equal(a, b) for a, b in zip(base, got))
+    again = [host(t) for t in _lp().lp_logprobs_entropy(x, y, None, 1.0)]
+    assert all(np.array_equal(a, b) for a, b in zip(base, again))
+
+
+def test_uniform_rows_closed_form():
+    torch = _torch()
+    V = 151936
+    x = torch.full((3, V), 2.5, dtype=torch.bfloat16, device="cuda")
+    lp, H = _lp().lp_logprobs_entropy(x, to_dev(np.array([0, 5, V - 1])), None, 0.7)
+    assert np.allclose(host(lp), -math.log(V), atol=TOL, rtol=0)
+    assert np.allclose(host(H), math.log(V), atol=TOL, rtol=0)
+
+
+def test_special_values_and_targets():
+    torch = _torch()
+    x = np.zeros((4, 10), dtype=np.float32)
+    x[0, 3:] = -np.inf            # 3 equal live entries
+    x[1, :] = 5.0
+    x[1, 9] = -np.inf
+    x[2, 0] = 100.0               # one-hot limit
+    bits = synth.f32_to_bf16_bits(x)
+    targets = np.array([0, 9, 0, 10], dtype=np.int64)  # row 3: out of range
+    lp, H = _lp().lp_logprobs_entropy(_dev_logits(bits, "bf16"), to_dev(targets), None, 1.0)
+    lp, H = host(lp), host(H)
+    assert abs(lp[0] + math.log(3)) <= TOL and abs(H[0] - math.log(3)) <= TOL
+    assert lp[1] == -np.inf or lp[1] < -1e30 or np.isneginf(lp[1])
+    assert abs(H[1] - math.log(9)) <= TOL
+    assert abs(lp[2]) <= TOL and abs(H[2]) <= TOL
+    assert np.isnan(lp[3]) and abs(H[3] - math.log(10)) <= TOL
+    del torch
+
+
+def test_empty_and_input_untouched():
+    torch = _torch()
+    lp = _lp()
+    x = torch.zeros((0, 100), dtype=torch.bfloat16, device="cuda")
+    a, b = lp.lp_logprobs_entropy(x, torch.zeros(0, dtype=torch.int64, device="cuda"), None, 0.7, 4)
+    assert a.numel() == 0 and b.numel() == 0
+    bits, targets, mask = _random_case(16, 999, "bf16", 3.0, seed=14)
+    xd = _dev_logits(bits, "bf16")
+    before = xd.clone()
+    lp.lp_logprobs_entropy(xd, to_dev(targets), to_dev(mask), 0.7, 3)
+    assert torch.equal(before.view(torch.int16), xd.view(torch.int16))
+
+
+def test_invalid_arguments_launch_nothing():
+    torch = _torch()
+    lp = _lp()
+    x = torch.zeros((4, 8), dtype=torch.bfloat16, device="cuda")
+    y = torch.zeros(4, dtype=torch.int64, device="cuda")
+    out = torch.full((4,), 7.0, device="cuda")
+    with pytest.raises(lp.LPError):
+        lp.lp_logprobs_entropy(x, y, None, float("nan"), logprob=out)
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
+
+
+# ---------------------------------------------------------------------------
+# full-size logits-input workload: 8192 x 151936 bf16, tau 0.7, chunk 4096
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def logits_full():
+    cfg = synth.LogitsInput().build()
+    A = cfg.arrays
+    return cfg, A, _dev_logits(A["logits"], "bf16"), to_dev(A["targets"]), to_dev(A["mask"])
+
+
+@pytest.mark.timeout(600)
+def test_full_size_logits_sampled_rows(logits_full):
+    cfg, A, x, y, m = logits_full
+    lp, H = _lp().lp_logprobs_entropy(x, y, m, cfg.temperature, cfg.chunk_rows)
+    lp, H = host(lp), host(H)
+    scored = np.nonzero(A["mask"])[0]
+    rng = np.random.default_rng(5)
+    spikes = np.nonzero(A["spike_rows"] & (A["mask"] == 1))[0]
+    rows = np.unique(np.concatenate([rng.choice(scored, 48, replace=False), spikes[:16], scored[:2], scored[-2:]]))
+    lp_o, H_o, _ = O.logprobs_entropy(O.widen_bf16(A["logits"][rows]), A["targets"][rows], None, cfg.temperature)
+    assert max_abs_err(lp[rows], lp_o) <= TOL
+    assert max_abs_err(H[rows], H_o) <= TOL
+    assert np.all(lp[A["mask"] == 0] == 0) and np.all(H[A["mask"] == 0] == 0)
+    assert np.all(lp[scored] <= 1e-6) and np.all(H[scored] >= -1e-6)
+    assert np.all(H[scored] <= math.log(cfg.V) + 1e-5)
+
+
+# ---------------------------------------------------------------------------
+# KL + prob diff
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("V", [1, 2, 5, 16, 1000, 4097, 129280])
+def test_kl_small(dtype, V):
+    T = 6 if V > 5000 else 23
+    rng = np.random.default_rng(V)
+    u = rng.normal(0, 4, size=(T, V)).astype(np.float32)
+    v = u + rng.normal(0, 0.5, size=u.shape).astype(np.float32)
+    conv = synth.f32_to_fp16_bits if dtype == "fp16" else synth.f32_to_bf16_bits
+    ub, vb = conv(u), conv(v)
+    targets = rng.integers(0, V, size=T).astype(np.int64)
+    dm = (rng.random(T) < 0.6).astype(np.uint8)
+    kl, lpu, lpv, d = _lp().lp_kl_full_vocab(to_dev_bits(ub, dtype), to_dev_bits(vb, dtype), to_dev(targets),
+                                             to_dev(dm))
+    kl_o, lpu_o, lpv_o, d_o = O.kl_and_prob_diff(O.widen(ub, dtype), O.widen(vb, dtype), targets, dm)
+    assert max_abs_err(host(kl), kl_o) <= TOL
+    assert max_abs_err(host(lpu), lpu_o) <= TOL and max_abs_err(host(lpv), lpv_o) <= TOL
+    assert max_abs_err(host(d), d_o) <= TOL
+    assert np.all(host(d)[dm == 0] == 0)
+
+
+def test_kl_self_exactly_zero_and_no_targets():
+    rng = np.random.default_rng(3)
+    ub = synth.f32_to_fp16_bits(rng.normal(0, 4, size=(5, 3333)).astype(np.float32))
+    x = to_dev_bits(ub, "fp16")
+    kl, a, b, c = _lp().lp_kl_full_vocab(x, x.clone())
+    assert np.all(host(kl) == 0.0) and a is None and b is None and c is None
+
+
+@pytest.fixture(scope="module")
+def kl_full():
+    cfg = synth.KLPair().build()
+    A = cfg.arrays
+    return cfg, A, to_dev_bits(A["student"], "fp16"), to_dev_bits(A["teacher"], "fp16"), \
+        to_dev(A["targets"]), to_dev(A["diff_mask"])
+
+
+@pytest.mark.timeout(900)
+def test_kl_full_size_sampled_rows(kl_full):
+    cfg, A, u, v, y, dm = kl_full
+    kl, lpu, lpv, d = (host(t) for t in _lp().lp_kl_full_vocab(u, v, y, dm))
+    rows = np.unique(np.random.default_rng(9).choice(cfg.T, 40, replace=False))
+    kl_o, lpu_o, lpv_o, d_o = O.kl_and_prob_diff(O.widen_fp16(A["student"][rows]), O.widen_fp16(A["teacher"][rows]),
+                                                 A["targets"][rows], A["diff_mask"][rows])
+    assert max_abs_err(kl[rows], kl_o) <= TOL
+    assert max_abs_err(lpu[rows], lpu_o) <= TOL and max_abs_err(lpv[rows], lpv_o) <= TOL
+    assert max_abs_err(d[rows], d_o) <= TOL
+    assert np.all(np.isfinite(kl)) and np.all(kl >= -1e-5)
+    assert np.all(d[A["diff_mask"] == 0] == 0)
+
+
+def test_prob_diff_elementwise():
+    rng = np.random.default_rng(4)
+    n = 100003
+    a = -np.abs(rng.normal(0, 3, n)).astype(np.float32)
+    b = -np.abs(rng.normal(0, 3, n)).astype(np.float32)
+    m = (rng.random(n) < 0.6).astype(np.uint8)
+    got = host(_lp().lp_prob_diff(to_dev(a), to_dev(b), to_dev(m)))
+    assert max_abs_err(got, O.prob_diff(a.astype(np.float64), b.astype(np.float64), m)) <= 1e-6
+    assert np.all(host(_lp().lp_prob_diff(to_dev(a), to_dev(b), to_dev(np.zeros(n, np.uint8)))) == 0)
