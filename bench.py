@@ -272,6 +272,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--paths", default="all", help="comma list of " + ",".join(ALL_PATHS))
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline (0 = skip)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run one plain device-to-device copy of this many MiB (reference for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
@@ -290,6 +292,16 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     lp.load()
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy of {args.copy_calibration_mib} MiB done")
+        del src, dst
+        torch.cuda.empty_cache()
     results = {}
     for p in paths:
         log(f"path {p}: building inputs and timing")

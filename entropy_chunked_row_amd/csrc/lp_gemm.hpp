@@ -196,4 +196,250 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
   return (x < rem) ? x * (q + 1) + j : rem * (q + 1) + (x - rem) * q + j;
 }
 
+
+// ---------------------------------------------------------------------------
+// Fast NT mainloop for K % BK == 0: global -> LDS with global_load_lds_dwordx4
+// (no register staging), XOR-swizzled LDS rows, two LDS stages, fragment
+// prefetch one K-substep ahead.
+//
+// LDS row = BK bf16 = 8 chunks of 16 bytes; the chunk holding logical 16-byte
+// column kc of row r sits at position kc ^ swz(r), swz(r) = (r & 7) ^ ((r >> 3) & 1),
+// so the 32 lanes reading one fragment column (rows r..r+31, same kc) spread
+// over all banks.  Each wave-wide load instruction fills 64 consecutive chunk
+// slots (1 KB), so every lane loads the global chunk that belongs in its slot.
+// Rows past the valid range are clamped to the last valid row (their results
+// are discarded by the caller); K must be a multiple of BK.
+// ---------------------------------------------------------------------------
+
+#ifndef LP_SCHED_HINTS
+#define LP_SCHED_HINTS 0
+#endif
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void gbl_void_t;
+
+template <int BM_, int BN_, int WGM_, int WGN_>
+struct DtlCfg {
+  static constexpr int BM = BM_, BN = BN_, BK = 64, WGM = WGM_, WGN = WGN_;
+  static constexpr int NT = 64 * WGM * WGN;
+  static constexpr int NW = WGM * WGN;
+  static constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  static constexpr int MI = WTM / 32, NI = WTN / 32;
+  static constexpr int KC = BK / 8;                   // 8 chunks per row
+  // Waves that issue the global loads.  With two waves per SIMD, letting only
+  // one of them load keeps the other free to feed the matrix unit while the
+  // loads queue.
+#ifdef LP_LOADER_WAVES
+  static constexpr int LW = LP_LOADER_WAVES < NW ? LP_LOADER_WAVES : NW;
+#else
+  static constexpr int LW = NW >= 8 ? NW / 2 : NW;
+#endif
+  static constexpr int A_INST = BM * KC / 64 / LW;    // load instructions per loading wave per stage (A)
+  static constexpr int B_INST = BN * KC / 64 / LW;
+  static constexpr int STAGE_ELEMS = (BM + BN) * BK;
+  static constexpr int LDS_ELEMS = 2 * STAGE_ELEMS;
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
+  static_assert((BM * KC) % (64 * LW) == 0 && (BN * KC) % (64 * LW) == 0, "tile not divisible among waves");
+};
+
+__device__ __forceinline__ int lds_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// Row sources of one operand for this thread: byte offsets of the global chunk
+// each of its load instructions moves (K offset added per stage).
+template <int NINST>
+struct DtlRows {
+  uint32_t off[NINST];  // byte offsets from the operand base (the caller checks they fit in 32 bits)
+};
+
+// A operand: rows m0 + r of a row-major matrix (clamped to M - 1).
+template <class C, int NINST>
+__device__ __forceinline__ void dtl_rows_dense(DtlRows<NINST>& rw, int64_t ld, int M) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int j = 0; j < NINST; ++j) {
+    const int slot = (j * C::LW + wave) * 64 + lane;
+    const int r = slot / C::KC, pc = slot % C::KC;
+    const int kc = pc ^ lds_swz(r);
+    const int rr = r < M ? r : M - 1;
+    rw.off[j] = static_cast<uint32_t>((static_cast<int64_t>(rr) * ld + kc * 8) * 2);
+  }
+}
+
+// B operand: gathered rows rows[r] (clamped to N - 1).
+template <class C, int NINST>
+__device__ __forceinline__ void dtl_rows_gather(DtlRows<NINST>& rw, int64_t ld, const int* rows, int N) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int j = 0; j < NINST; ++j) {
+    const int slot = (j * C::LW + wave) * 64 + lane;
+    const int r = slot / C::KC, pc = slot % C::KC;
+    const int kc = pc ^ lds_swz(r);
+    const int rr = r < N ? r : N - 1;
+    rw.off[j] = static_cast<uint32_t>((static_cast<int64_t>(rows[rr]) * ld + kc * 8) * 2);
+  }
+}
+
+template <class C, int NINST>
+__device__ __forceinline__ void dtl_issue(const char* base, const DtlRows<NINST>& rw, int64_t kbytes,
+                                          uint16_t* lds_region) {
+  const int wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int j = 0; j < NINST; ++j) {
+    uint16_t* dst = lds_region + (j * C::NW + wave) * 64 * 8;
+    // C-style casts: generic -> global / LDS address spaces
+    __builtin_amdgcn_global_load_lds((gbl_void_t*)(base + rw.off[j] + kbytes), (lds_void_t*)(dst), 16, 0, 0);
+  }
+}
+
+// One 16-byte fragment read: piece q < MI reads A fragment q, else B fragment q - MI.
+template <class C>
+__device__ __forceinline__ void dtl_frag_piece(const uint16_t* stage, int kk, int wm, int wn, int q,
+                                               bf16x8_t (&af)[C::MI], bf16x8_t (&bfr)[C::NI]) {
+  const int lane = threadIdx.x & 63;
+  const int r32 = lane & 31;
+  const int pc = ((kk >> 3) + (lane >> 5)) ^ lds_swz(r32);
+  if (q < C::MI) {
+    af[q] = *reinterpret_cast<const bf16x8_t*>(stage + (wm * C::WTM + q * 32 + r32) * C::BK + pc * 8);
+  } else {
+    const int ni = q - C::MI;
+    bfr[ni] = *reinterpret_cast<const bf16x8_t*>(stage + (C::BM + wn * C::WTN + ni * 32 + r32) * C::BK + pc * 8);
+  }
+}
+
+// Issue global load instruction j (A for j < A_INST, else B) of a stage; the
+// bases already include the stage's K offset (uniform), the per-lane part is a
+// 32-bit offset.  Only the first LW waves load (see DtlCfg::LW).
+template <class C, int NA, int NB>
+__device__ __forceinline__ void dtl_issue_one(int j, const char* abase, const DtlRows<NA>& ra, const char* bbase,
+                                              const DtlRows<NB>& rb, uint16_t* stage) {
+  const int wave = threadIdx.x >> 6;
+  if (j < NA) {
+    uint16_t* dst = stage + (j * C::LW + wave) * 64 * 8;
+    __builtin_amdgcn_global_load_lds((gbl_void_t*)(abase + ra.off[j]), (lds_void_t*)(dst), 16, 0, 0);
+  } else {
+    const int jb = j - NA;
+    uint16_t* dst = stage + C::BM * C::BK + (jb * C::LW + wave) * 64 * 8;
+    __builtin_amdgcn_global_load_lds((gbl_void_t*)(bbase + rb.off[jb]), (lds_void_t*)(dst), 16, 0, 0);
+  }
+}
+
+// One K-step on stage X (the other stage is Y).  Instruction order, fixed with
+// scheduling barriers so that an MFMA never waits on a fragment read issued
+// just before it:
+//   substeps 0 .. S-2: MFMAs on X; between them, the fragment reads of the next
+//                      substep (from X).
+//   end of S-2:        wait for this wave's loads of the next stage, barrier
+//                      (next stage complete in Y; every wave is done reading X).
+//   substep S-1:       MFMAs on X (fragments already in registers); between them,
+//                      the first fragments of the next stage (from Y) and the
+//                      global loads of the stage after next (into X).
+template <class C, bool NEXT, bool NEXT2>
+__device__ __forceinline__ void dtl_kstep(uint16_t* X, uint16_t* Y, const char* abase2, const DtlRows<C::A_INST>& ra,
+                                          const char* bbase2, const DtlRows<C::B_INST>& rb, int wm, int wn,
+                                          bf16x8_t (&fa)[2][C::MI], bf16x8_t (&fb)[2][C::NI],
+                                          f32x16_t (&acc)[C::MI][C::NI]) {
+  constexpr int S = C::BK / 16;
+  constexpr int NQ = C::MI * C::NI;
+  constexpr int NF = C::MI + C::NI;
+  constexpr int NL = C::A_INST + C::B_INST;
+  static_assert(S % 2 == 0, "substep 0 of every stage must use fragment buffer 0");
+  static_assert(NF <= 2 * NQ, "not enough MFMA slots to interleave fragment reads");
+  const bool loader = (threadIdx.x >> 6) < C::LW;
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int cur = s & 1;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      // fragment reads of the next substep, two per MFMA slot from the start
+      // of the substep, so they have most of it to land
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int f = 2 * q + u;
+        if (f < NF) {
+          if (s + 1 < S)
+            dtl_frag_piece<C>(X, (s + 1) * 16, wm, wn, f, fa[cur ^ 1], fb[cur ^ 1]);
+          else if (NEXT)
+            dtl_frag_piece<C>(Y, 0, wm, wn, f, fa[cur ^ 1], fb[cur ^ 1]);
+        }
+      }
+      if (s + 1 == S && NEXT2 && loader) {
+        // the loads of the stage after next, spread over this substep
+#pragma unroll
+        for (int u = 0; u < (NL + NQ - 1) / NQ; ++u) {
+          const int j = q * ((NL + NQ - 1) / NQ) + u;
+          if (j < NL) dtl_issue_one<C, C::A_INST, C::B_INST>(j, abase2, ra, bbase2, rb, X);
+        }
+      }
+      const int mi = q / C::NI, ni = q % C::NI;
+      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][mi], fb[cur][ni], acc[mi][ni], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (NEXT && s == S - 2) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
+  }
+}
+
+// D[m][n] = sum_k A[m][k] * B[rows[n]][k] over K (multiple of 64).
+// a: bf16 rows of the block (row 0 = the block's first row), M valid rows;
+// b: bf16 base of the gathered matrix, b_rows the gather list, N valid rows.
+// Byte offsets of every row read from a and b must fit in 32 bits.
+template <class C>
+__device__ __forceinline__ void gemm_tile_dtl(const uint16_t* a, int64_t lda, int M, const uint16_t* b,
+                                              int64_t ldb, const int* b_rows, int N, int K, uint16_t* lds,
+                                              f32x16_t (&acc)[C::MI][C::NI]) {
+  constexpr int NF = C::MI + C::NI;
+  constexpr int NL = C::A_INST + C::B_INST;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave % C::WGM, wn = wave / C::WGM;
+#pragma unroll
+  for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < C::NI; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
+
+  DtlRows<C::A_INST> ra;
+  DtlRows<C::B_INST> rb;
+  dtl_rows_dense<C, C::A_INST>(ra, lda, M);
+  dtl_rows_gather<C, C::B_INST>(rb, ldb, b_rows, N);
+  const char* abase = reinterpret_cast<const char*>(a);
+  const char* bbase = reinterpret_cast<const char*>(b);
+  constexpr int KB = C::BK * 2;  // bytes per stage along K
+  const int nk = K / C::BK;
+  uint16_t* L0 = lds;
+  uint16_t* L1 = lds + C::STAGE_ELEMS;
+
+  // prologue: stages 0 and 1 in flight, wait for stage 0, read its first fragments
+  if ((threadIdx.x >> 6) < C::LW) {
+#pragma unroll
+    for (int j = 0; j < NL; ++j) dtl_issue_one<C, C::A_INST, C::B_INST>(j, abase, ra, bbase, rb, L0);
+    if (nk > 1) {
+#pragma unroll
+      for (int j = 0; j < NL; ++j) dtl_issue_one<C, C::A_INST, C::B_INST>(j, abase + KB, ra, bbase + KB, rb, L1);
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NL) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+  }
+  __syncthreads();
+  bf16x8_t fa[2][C::MI], fb[2][C::NI];
+#pragma unroll
+  for (int q = 0; q < NF; ++q) dtl_frag_piece<C>(L0, 0, wm, wn, q, fa[0], fb[0]);
+
+  int kt = 0;
+  for (; kt + 2 < nk; ++kt) {
+    const int64_t kb2 = static_cast<int64_t>(kt + 2) * KB;
+    dtl_kstep<C, true, true>((kt & 1) ? L1 : L0, (kt & 1) ? L0 : L1, abase + kb2, ra, bbase + kb2, rb, wm, wn, fa, fb,
+                             acc);
+  }
+  if (kt + 1 < nk) {
+    dtl_kstep<C, true, false>((kt & 1) ? L1 : L0, (kt & 1) ? L0 : L1, abase, ra, bbase, rb, wm, wn, fa, fb, acc);
+    ++kt;
+  }
+  dtl_kstep<C, false, false>((kt & 1) ? L1 : L0, (kt & 1) ? L0 : L1, abase, ra, bbase, rb, wm, wn, fa, fb, acc);
+  __syncthreads();
+}
+
 }  // namespace lp

@@ -33,8 +33,19 @@ namespace {
 
 constexpr float kLog2eF = 1.44269504088896340736f;
 
-using FwdCfg = GemmCfg<128, 128, 64, 2, 2>;
-using BwdCfg = GemmCfg<128, 128, 64, 2, 2>;
+// Block tiles (BM, BN, BK, waves along M, waves along N); build-time knobs.
+#ifndef LP_FWD_TILE
+#define LP_FWD_TILE 128, 128, 64, 2, 2
+#endif
+#ifndef LP_BWD_TILE
+#define LP_BWD_TILE 128, 128, 64, 2, 2
+#endif
+using FwdCfg = GemmCfg<LP_FWD_TILE>;
+#ifndef LP_FWD_DTL_TILE
+#define LP_FWD_DTL_TILE 256, 256, 4, 2
+#endif
+using FwdDtlCfg = DtlCfg<LP_FWD_DTL_TILE>;
+using BwdCfg = GemmCfg<LP_BWD_TILE>;
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -46,7 +57,10 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 // Logical tile -> (vocab block, token block): groups of kGroupV vocab blocks
 // sweep all token blocks, token-block-major inside a group, so consecutive
 // workgroups on one XCD share both weight and hidden strips in its L2.
-constexpr int kGroupV = 8;
+#ifndef LP_GROUP_V
+#define LP_GROUP_V 8
+#endif
+constexpr int kGroupV = LP_GROUP_V;
 __device__ __forceinline__ void tile_coords(int L, int n_vb, int n_nb, int& vb, int& nb) {
   const int full = n_vb / kGroupV;
   const int g = L / (kGroupV * n_nb);
@@ -69,7 +83,8 @@ bool lmhead_workspace_layout(int64_t T, int64_t h, int64_t V, int64_t tile_rows,
   if (T < 0 || h <= 0 || V <= 0 || tile_rows <= 0) return false;
   if (T > 0x7fffffff || V > (int64_t(1) << 30) || h > (int64_t(1) << 30)) return false;
   const int64_t tr = tile_rows < (T > 0 ? T : 1) ? tile_rows : (T > 0 ? T : 1);
-  w->n_vblocks = static_cast<int>((V + FwdCfg::BM - 1) / FwdCfg::BM);
+  const int bm_min = FwdCfg::BM < FwdDtlCfg::BM ? FwdCfg::BM : FwdDtlCfg::BM;
+  w->n_vblocks = static_cast<int>((V + bm_min - 1) / bm_min);  // enough partials for either forward tile
   w->vpad = static_cast<int64_t>(align_up(static_cast<size_t>(V), 64));
   size_t off = 0;
   w->idx_off = off;
@@ -149,35 +164,17 @@ struct FwdArgs {
   float* zy;    // [tile_rows]
 };
 
+// Forward epilogue shared by both GEMM mainloops: per token column, fold the
+// block's vocab rows into one (mc, s, a) state, pick up the target logit if
+// its column lies in this block, and write one partial per (row, vocab block).
 template <class C>
-__global__ void __launch_bounds__(C::NT) k_fwd_tile(FwdArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
-  int vb, nb;
-  tile_coords(xcd_remap(blockIdx.x, a.n_vb * a.n_nb), a.n_vb, a.n_nb, vb, nb);
-  const int count = *a.count;
-  const int64_t rem = static_cast<int64_t>(count) - a.tile_base;
-  const int rows = static_cast<int>(rem < a.tile_rows ? rem : a.tile_rows);
-  const int n0 = nb * C::BN;
-  if (n0 >= rows) return;
-  const int v0 = vb * C::BM;
-
-  GemmOperands op;
-  op.a = a.weight + static_cast<int64_t>(v0) * a.ld_w;
-  op.lda = a.ld_w;
-  op.M = a.V - v0;
-  op.b = a.hidden;
-  op.ldb = a.ld_h;
-  op.b_rows = a.idx + a.tile_base + n0;
-  op.N = rows - n0;
-  op.K = a.h;
-  f32x16_t acc[C::MI][C::NI];
-  gemm_tile<C>(op, 0, 0, lds, acc);
-
-  // epilogue: per token column, fold this block's vocab rows into a state
+__device__ __forceinline__ void fwd_epilogue(const FwdArgs& a, f32x16_t (&acc)[C::MI][C::NI], int vb, int n0, int rows,
+                                             uint16_t* lds) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave % C::WGM, wn = wave / C::WGM;
-  const int vlane = v0 + wm * C::WTM + 4 * (lane >> 5);
+  const int vwave = vb * C::BM + wm * C::WTM;  // first vocab row of this wave
+  const int half = lane >> 5;
   Stat* sm = reinterpret_cast<Stat*>(lds);  // [WGM][BN] states, reused after the K loop
   const float c = a.c;
 #pragma unroll
@@ -187,31 +184,39 @@ __global__ void __launch_bounds__(C::NT) k_fwd_tile(FwdArgs a) {
     const bool valid_row = r < rows;
     int64_t y = -1;
     if (valid_row) y = a.targets[a.idx[a.tile_base + r]];
-    float x[C::MI * 16];
+    const int64_t yrel = y - vwave;
     Stat st = stat_empty();
-    float zsel = 0.f;
-    bool found = false;
 #pragma unroll
-    for (int mi = 0; mi < C::MI; ++mi)
+    for (int mi = 0; mi < C::MI; ++mi) {
+      float x[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int v = vlane + mi * 32 + 8 * (i >> 2) + (i & 3);
-        const float z = acc[mi][ni][i];
-        // rows past V hold zeros from the GEMM: give them probability 0
-        // (-inf, folded with the clamped push below)
-        x[mi * 16 + i] = (v < a.V) ? z : -INFINITY;
-        if (v == y) {
-          zsel = z;
-          found = true;
-        }
+        const int v = vwave + mi * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+        // rows past V hold zeros from the GEMM: probability 0 (-inf with the clamped fold)
+        x[i] = (v < a.V) ? acc[mi][ni][i] : -INFINITY;
       }
-    stat_push<true, C::MI * 16, 16>(st, x, c);
+      stat_push<true, 16, 16>(st, x, c);
+    }
+    if (valid_row && yrel >= 0 && yrel < C::WTM) {
+      float zsel = 0.f;
+      bool found = false;
+#pragma unroll
+      for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int vr = mi * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+          if (yrel == vr) {
+            zsel = acc[mi][ni][i];
+            found = true;
+          }
+        }
+      if (found) a.zy[r] = zsel;
+    }
     Stat o;
     o.mc = __shfl_xor(st.mc, 32, 64);
     o.s = __shfl_xor(st.s, 32, 64);
     o.a = __shfl_xor(st.a, 32, 64);
     st = stat_merge(st, o);
-    if (found && valid_row) a.zy[r] = zsel;
     if (lane < 32) sm[wm * C::BN + nl] = st;
   }
   __syncthreads();
@@ -231,6 +236,50 @@ __global__ void __launch_bounds__(C::NT) k_fwd_tile(FwdArgs a) {
       }
     }
   }
+}
+
+// Generic forward tile (any h % 8 == 0): register-staged, zero-filled loads.
+template <class C>
+__global__ void __launch_bounds__(C::NT) k_fwd_tile(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
+  int vb, nb;
+  tile_coords(xcd_remap(blockIdx.x, a.n_vb * a.n_nb), a.n_vb, a.n_nb, vb, nb);
+  const int count = *a.count;
+  const int64_t rem = static_cast<int64_t>(count) - a.tile_base;
+  const int rows = static_cast<int>(rem < a.tile_rows ? rem : a.tile_rows);
+  const int n0 = nb * C::BN;
+  if (n0 >= rows) return;
+  const int v0 = vb * C::BM;
+  GemmOperands op;
+  op.a = a.weight + static_cast<int64_t>(v0) * a.ld_w;
+  op.lda = a.ld_w;
+  op.M = a.V - v0;
+  op.b = a.hidden;
+  op.ldb = a.ld_h;
+  op.b_rows = a.idx + a.tile_base + n0;
+  op.N = rows - n0;
+  op.K = a.h;
+  f32x16_t acc[C::MI][C::NI];
+  gemm_tile<C>(op, 0, 0, lds, acc);
+  fwd_epilogue<C>(a, acc, vb, n0, rows, lds);
+}
+
+// Fast forward tile (h % 64 == 0): direct-to-LDS loads, 256 x 256 block.
+template <class C>
+__global__ void __launch_bounds__(C::NT) k_fwd_tile_dtl(FwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[C::LDS_ELEMS];
+  int vb, nb;
+  tile_coords(xcd_remap(blockIdx.x, a.n_vb * a.n_nb), a.n_vb, a.n_nb, vb, nb);
+  const int count = *a.count;
+  const int64_t rem = static_cast<int64_t>(count) - a.tile_base;
+  const int rows = static_cast<int>(rem < a.tile_rows ? rem : a.tile_rows);
+  const int n0 = nb * C::BN;
+  if (n0 >= rows) return;
+  const int v0 = vb * C::BM;
+  f32x16_t acc[C::MI][C::NI];
+  gemm_tile_dtl<C>(a.weight + static_cast<int64_t>(v0) * a.ld_w, a.ld_w, a.V - v0, a.hidden, a.ld_h,
+                   a.idx + a.tile_base + n0, rows - n0, a.h, lds, acc);
+  fwd_epilogue<C>(a, acc, vb, n0, rows, lds);
 }
 
 struct MergeArgs {
@@ -285,8 +334,12 @@ hipError_t launch_lmhead_forward(const LMHeadShape& sh, float* logprob, float* e
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t tr = sh.tile_rows < sh.T ? sh.tile_rows : sh.T;
-  const int n_vb = w.n_vblocks;
-  const int n_nb = static_cast<int>((tr + FwdCfg::BN - 1) / FwdCfg::BN);
+  // K multiple of 64: direct-to-LDS 256 x 256 tiles; otherwise the generic tile
+  const bool fast = (sh.h % FwdDtlCfg::BK) == 0;
+  const int bm = fast ? FwdDtlCfg::BM : FwdCfg::BM;
+  const int bn = fast ? FwdDtlCfg::BN : FwdCfg::BN;
+  const int n_vb = (sh.V + bm - 1) / bm;
+  const int n_nb = static_cast<int>((tr + bn - 1) / bn);
   for (int64_t base = 0; base < sh.T; base += tr) {
     FwdArgs a;
     a.weight = sh.weight;
@@ -307,7 +360,11 @@ hipError_t launch_lmhead_forward(const LMHeadShape& sh, float* logprob, float* e
     a.zy = zy;
     {
       TimedLaunch tl("k_fwd_tile", s);
-      hipLaunchKernelGGL(k_fwd_tile<FwdCfg>, dim3(static_cast<unsigned>(n_vb) * n_nb), dim3(FwdCfg::NT), 0, s, a);
+      const dim3 grid(static_cast<unsigned>(n_vb) * n_nb);
+      if (fast)
+        hipLaunchKernelGGL(k_fwd_tile_dtl<FwdDtlCfg>, grid, dim3(FwdDtlCfg::NT), 0, s, a);
+      else
+        hipLaunchKernelGGL(k_fwd_tile<FwdCfg>, grid, dim3(FwdCfg::NT), 0, s, a);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     MergeArgs m;
