@@ -265,7 +265,7 @@ __device__ __forceinline__ void dtl_rows_dense(DtlRows<NINST>& rw, int64_t ld, i
   }
 }
 
-// B operand: gathered rows rows[r] (clamped to N - 1).
+// B operand: gathered rows rows[r], or rows r when rows is null (clamped to N - 1).
 template <class C, int NINST>
 __device__ __forceinline__ void dtl_rows_gather(DtlRows<NINST>& rw, int64_t ld, const int* rows, int N) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -275,7 +275,8 @@ __device__ __forceinline__ void dtl_rows_gather(DtlRows<NINST>& rw, int64_t ld, 
     const int r = slot / C::KC, pc = slot % C::KC;
     const int kc = pc ^ lds_swz(r);
     const int rr = r < N ? r : N - 1;
-    rw.off[j] = static_cast<uint32_t>((static_cast<int64_t>(rows[rr]) * ld + kc * 8) * 2);
+    const int64_t src = rows ? static_cast<int64_t>(rows[rr]) : static_cast<int64_t>(rr);
+    rw.off[j] = static_cast<uint32_t>((src * ld + kc * 8) * 2);
   }
 }
 
@@ -381,10 +382,11 @@ __device__ __forceinline__ void dtl_kstep(uint16_t* X, uint16_t* Y, const char* 
   }
 }
 
-// D[m][n] = sum_k A[m][k] * B[rows[n]][k] over K (multiple of 64).
-// a: bf16 rows of the block (row 0 = the block's first row), M valid rows;
-// b: bf16 base of the gathered matrix, b_rows the gather list, N valid rows.
-// Byte offsets of every row read from a and b must fit in 32 bits.
+// D[m][n] = sum_k A[m][k] * B[rows[n]][k] over K (multiple of 64, may be 0).
+// a: bf16 rows of the block (row 0 = the block's first row, column 0 = the
+// first K column used), M valid rows; b: bf16 base of the gathered matrix,
+// b_rows the gather list (null: rows 0..N-1 of b), N valid rows.  Byte
+// offsets of every row read from a and b must fit in 32 bits.
 template <class C>
 __device__ __forceinline__ void gemm_tile_dtl(const uint16_t* a, int64_t lda, int M, const uint16_t* b,
                                               int64_t ldb, const int* b_rows, int N, int K, uint16_t* lds,
@@ -408,6 +410,7 @@ __device__ __forceinline__ void gemm_tile_dtl(const uint16_t* a, int64_t lda, in
   const char* bbase = reinterpret_cast<const char*>(b);
   constexpr int KB = C::BK * 2;  // bytes per stage along K
   const int nk = K / C::BK;
+  if (nk <= 0) return;  // empty K: D = 0
   uint16_t* L0 = lds;
   uint16_t* L1 = lds + C::STAGE_ELEMS;
 

@@ -45,6 +45,10 @@ using FwdCfg = GemmCfg<LP_FWD_TILE>;
 #define LP_FWD_DTL_TILE 256, 256, 4, 2
 #endif
 using FwdDtlCfg = DtlCfg<LP_FWD_DTL_TILE>;
+
+// K splits of the dHidden GEMM (its output is only tile_rows x h, too few
+// blocks to fill the chip without splitting K = V).
+constexpr int kSplitK = 4;
 using BwdCfg = GemmCfg<LP_BWD_TILE>;
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -76,6 +80,12 @@ __device__ __forceinline__ void tile_coords(int L, int n_vb, int n_nb, int& vb, 
   }
 }
 
+// The direct-to-LDS kernels need K = h in steps of 64 and 32-bit byte offsets
+// from the hidden base to every gathered row.
+bool lmhead_fast_path(const LMHeadShape& sh) {
+  return (sh.h % FwdDtlCfg::BK) == 0 && static_cast<uint64_t>(sh.T) * static_cast<uint64_t>(sh.ld_h) * 2u < (1ull << 32);
+}
+
 }  // namespace
 
 bool lmhead_workspace_layout(int64_t T, int64_t h, int64_t V, int64_t tile_rows, int backward,
@@ -104,6 +114,7 @@ bool lmhead_workspace_layout(int64_t T, int64_t h, int64_t V, int64_t tile_rows,
     off = align_up(off + tpad * static_cast<size_t>(w->vpad) * 2, 256);
     off = align_up(off + static_cast<size_t>(h) * static_cast<size_t>(w->vpad) * 2, 256);
     off = align_up(off + static_cast<size_t>(h) * tpad * 2, 256);
+    off = align_up(off + static_cast<size_t>(kSplitK) * tr * static_cast<size_t>(h) * 4, 256);  // dHidden partials
   }
   w->total = off;
   return true;
@@ -335,7 +346,7 @@ hipError_t launch_lmhead_forward(const LMHeadShape& sh, float* logprob, float* e
   if (e != hipSuccess) return e;
   const int64_t tr = sh.tile_rows < sh.T ? sh.tile_rows : sh.T;
   // K multiple of 64: direct-to-LDS 256 x 256 tiles; otherwise the generic tile
-  const bool fast = (sh.h % FwdDtlCfg::BK) == 0;
+  const bool fast = lmhead_fast_path(sh);
   const int bm = fast ? FwdDtlCfg::BM : FwdCfg::BM;
   const int bn = fast ? FwdDtlCfg::BN : FwdCfg::BN;
   const int n_vb = (sh.V + bm - 1) / bm;
@@ -474,30 +485,12 @@ struct DzArgs {
   uint16_t* dzt;  // [vpad][tpad] or nullptr
 };
 
+// dL/dlogits epilogue: for tile rows r < rowsK (the K span of the
+// weight-gradient GEMM; rows past the tile's valid rows get 0) and vocab
+// columns v < vpad (0 past V), writes bf16 dZ[r][v] and, if requested, dZ^T[v][r].
 template <class C>
-__global__ void __launch_bounds__(C::NT) k_bwd_dz(DzArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
-  int vb, nb;
-  tile_coords(xcd_remap(blockIdx.x, a.n_vb * a.n_nb), a.n_vb, a.n_nb, vb, nb);
-  const int count = *a.count;
-  const int64_t rem = static_cast<int64_t>(count) - a.tile_base;
-  const int rows = static_cast<int>(rem < a.tile_rows ? rem : a.tile_rows);
-  const int rows8 = (rows + 7) & ~7;  // rows the K of the weight-gradient GEMM spans
-  const int n0 = nb * C::BN;
-  if (rows <= 0 || n0 >= rows8) return;
-  const int v0 = vb * C::BM;
-  GemmOperands op;
-  op.a = a.weight + static_cast<int64_t>(v0) * a.ld_w;
-  op.lda = a.ld_w;
-  op.M = a.V - v0;
-  op.b = a.hidden;
-  op.ldb = a.ld_h;
-  op.b_rows = a.idx + a.tile_base + n0;
-  op.N = rows - n0;
-  op.K = a.h;
-  f32x16_t acc[C::MI][C::NI];
-  gemm_tile<C>(op, 0, 0, lds, acc);
-
+__device__ __forceinline__ void dz_epilogue(const DzArgs& a, f32x16_t (&acc)[C::MI][C::NI], int v0, int n0, int rows,
+                                            int rowsK) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave % C::WGM, wn = wave / C::WGM;
@@ -505,7 +498,7 @@ __global__ void __launch_bounds__(C::NT) k_bwd_dz(DzArgs a) {
 #pragma unroll
   for (int ni = 0; ni < C::NI; ++ni) {
     const int r = n0 + wn * C::WTN + ni * 32 + (lane & 31);
-    if (r >= rows8) continue;
+    if (r >= rowsK) continue;
     const bool valid = r < rows;
     int64_t y = -1;
     float l2 = 0.f, mu = 0.f, glp = 0.f, gh = 0.f;
@@ -548,6 +541,150 @@ __global__ void __launch_bounds__(C::NT) k_bwd_dz(DzArgs a) {
           }
         }
       }
+  }
+}
+
+// Generic recompute tile (any h % 8 == 0).
+template <class C>
+__global__ void __launch_bounds__(C::NT) k_bwd_dz(DzArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
+  int vb, nb;
+  tile_coords(xcd_remap(blockIdx.x, a.n_vb * a.n_nb), a.n_vb, a.n_nb, vb, nb);
+  const int count = *a.count;
+  const int64_t rem = static_cast<int64_t>(count) - a.tile_base;
+  const int rows = static_cast<int>(rem < a.tile_rows ? rem : a.tile_rows);
+  const int rowsK = (rows + 7) & ~7;
+  const int n0 = nb * C::BN;
+  if (rows <= 0 || n0 >= rowsK) return;
+  const int v0 = vb * C::BM;
+  GemmOperands op;
+  op.a = a.weight + static_cast<int64_t>(v0) * a.ld_w;
+  op.lda = a.ld_w;
+  op.M = a.V - v0;
+  op.b = a.hidden;
+  op.ldb = a.ld_h;
+  op.b_rows = a.idx + a.tile_base + n0;
+  op.N = rows - n0;
+  op.K = a.h;
+  f32x16_t acc[C::MI][C::NI];
+  gemm_tile<C>(op, 0, 0, lds, acc);
+  dz_epilogue<C>(a, acc, v0, n0, rows, rowsK);
+}
+
+// Fast recompute tile (h % 64 == 0): the forward's direct-to-LDS mainloop.
+// Rows up to the next multiple of 64 are written (zeros past the valid rows)
+// because the fast weight-gradient GEMM takes K in steps of 64.
+template <class C>
+__global__ void __launch_bounds__(C::NT) k_bwd_dz_dtl(DzArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[C::LDS_ELEMS];
+  int vb, nb;
+  tile_coords(xcd_remap(blockIdx.x, a.n_vb * a.n_nb), a.n_vb, a.n_nb, vb, nb);
+  const int count = *a.count;
+  const int64_t rem = static_cast<int64_t>(count) - a.tile_base;
+  const int rows = static_cast<int>(rem < a.tile_rows ? rem : a.tile_rows);
+  const int rowsK = (rows + 63) & ~63;
+  const int n0 = nb * C::BN;
+  if (rows <= 0 || n0 >= rowsK) return;
+  const int v0 = vb * C::BM;
+  f32x16_t acc[C::MI][C::NI];
+  gemm_tile_dtl<C>(a.weight + static_cast<int64_t>(v0) * a.ld_w, a.ld_w, a.V - v0, a.hidden, a.ld_h,
+                   a.idx + a.tile_base + n0, rows - n0, a.h, lds, acc);
+  dz_epilogue<C>(a, acc, v0, n0, rows, rowsK);
+}
+
+// Fast gradient GEMMs on dense K-contiguous operands (K multiple of 64):
+//   dHidden: A = dZ [rows x vpad], B = W^T [h x vpad], K split into `splits`
+//            ranges; each split writes an fp32 partial [rows x h] that
+//            k_splitk_reduce sums in a fixed order.
+//   dW:      A = dZ^T [V x tpad], B = H_tile^T [h x tpad], K = the tile's rows
+//            rounded up to 64; dW is written (first tile) or accumulated.
+struct DenseGemmArgs {
+  const uint16_t* a;
+  int64_t lda;
+  int M;              // A rows; if count != nullptr: the tile's valid rows instead
+  const uint16_t* b;
+  int64_t ldb;
+  int N;
+  int K;              // if k_from_count: rows of the tile rounded up to 64
+  const int* count;
+  int64_t tile_base;
+  int tile_rows;
+  int m_from_count, k_from_count;
+  int splits;         // K ranges (blockIdx spans n_mb * n_nb * splits)
+  int ksplit;         // K per split (multiple of 64)
+  float* out;         // dW [M x ldo] or partials [splits][tile_rows][ldo]
+  int64_t ldo;
+  int accumulate;
+  int n_mb, n_nb;
+};
+
+template <class C>
+__global__ void __launch_bounds__(C::NT) k_dense_gemm_dtl(DenseGemmArgs g) {
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[C::LDS_ELEMS];
+  const int per = g.n_mb * g.n_nb;
+  const int ks = blockIdx.x / per;
+  int mb, nb;
+  tile_coords(xcd_remap(blockIdx.x - ks * per, per), g.n_mb, g.n_nb, mb, nb);
+  int rows = 0;
+  if (g.count) {
+    const int64_t rem = static_cast<int64_t>(*g.count) - g.tile_base;
+    rows = static_cast<int>(rem < g.tile_rows ? (rem > 0 ? rem : 0) : g.tile_rows);
+  }
+  const int M = g.m_from_count ? rows : g.M;
+  const int K = g.k_from_count ? ((rows + 63) & ~63) : g.K;
+  const int m0 = mb * C::BM, n0 = nb * C::BN;
+  if (m0 >= M) return;
+  if (g.k_from_count && K == 0 && g.accumulate) return;
+  const int kbeg = ks * g.ksplit;
+  const int klen = (K - kbeg < g.ksplit) ? (K - kbeg) : g.ksplit;
+  f32x16_t acc[C::MI][C::NI];
+  gemm_tile_dtl<C>(g.a + static_cast<int64_t>(m0) * g.lda + kbeg, g.lda, M - m0,
+                   g.b + static_cast<int64_t>(n0) * g.ldb + kbeg, g.ldb, nullptr, g.N - n0, klen > 0 ? klen : 0, lds,
+                   acc);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave % C::WGM, wn = wave / C::WGM;
+  float* out = g.out + static_cast<int64_t>(ks) * g.tile_rows * g.ldo;  // splits > 1: partial ks
+#pragma unroll
+  for (int ni = 0; ni < C::NI; ++ni) {
+    const int n = n0 + wn * C::WTN + ni * 32 + (lane & 31);
+    if (n >= g.N) continue;
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int m = m0 + wm * C::WTM + mi * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+        if (m < M) {
+          float* p = out + static_cast<int64_t>(m) * g.ldo + n;
+          *p = g.accumulate ? (*p + acc[mi][ni][i]) : acc[mi][ni][i];
+        }
+      }
+  }
+}
+
+// dHidden[idx[base + m]][n] = sum over splits (in order) of partial[s][m][n].
+__global__ void __launch_bounds__(256) k_splitk_reduce(const float* __restrict__ part, int splits, int tile_rows,
+                                                       int h, const int* __restrict__ idx,
+                                                       const int* __restrict__ count, int64_t tile_base,
+                                                       float* __restrict__ out) {
+  const int64_t rem = static_cast<int64_t>(*count) - tile_base;
+  const int rows = static_cast<int>(rem < tile_rows ? (rem > 0 ? rem : 0) : tile_rows);
+  const int64_t n = static_cast<int64_t>(rows) * h;
+  const int64_t plane = static_cast<int64_t>(tile_rows) * h;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x * 4;
+  for (int64_t e = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 4; e < n; e += stride) {
+    // h % 8 == 0, so the 4 elements stay in one row
+    float4 acc = *reinterpret_cast<const float4*>(part + e);
+    for (int sp = 1; sp < splits; ++sp) {
+      const float4 v = *reinterpret_cast<const float4*>(part + sp * plane + e);
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
+    const int64_t m = e / h;
+    const int64_t col = e - m * h;
+    *reinterpret_cast<float4*>(out + static_cast<int64_t>(idx[tile_base + m]) * h + col) = acc;
   }
 }
 
@@ -620,6 +757,7 @@ hipError_t launch_lmhead_backward(const LMHeadShape& sh, const float* lse, const
                                   const float* grad_logprob, const float* grad_entropy, float* grad_hidden,
                                   float* grad_weight, char* ws, const LMHeadWorkspace& w, hipStream_t s) {
   using C = BwdCfg;
+  using F = FwdDtlCfg;
   int* idx = reinterpret_cast<int*>(ws + w.idx_off);
   int* count = reinterpret_cast<int*>(ws + w.count_off);
   const int64_t tr = sh.tile_rows < sh.T ? sh.tile_rows : sh.T;
@@ -632,6 +770,9 @@ hipError_t launch_lmhead_backward(const LMHeadShape& sh, const float* lse, const
   uint16_t* wt = reinterpret_cast<uint16_t*>(ws + off);
   off = align_up(off + static_cast<size_t>(sh.h) * vpad * 2, 256);
   uint16_t* ht = reinterpret_cast<uint16_t*>(ws + off);
+  off = align_up(off + static_cast<size_t>(sh.h) * tpad * 2, 256);
+  float* hpart = reinterpret_cast<float*>(ws + off);  // split-K partials of dHidden (fast path)
+  const bool fast = lmhead_fast_path(sh) && (reinterpret_cast<uintptr_t>(grad_hidden) & 15u) == 0;
 
   {
     TimedLaunch tl("k_compact", s);
@@ -657,8 +798,10 @@ hipError_t launch_lmhead_backward(const LMHeadShape& sh, const float* lse, const
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  const int n_vb = w.n_vblocks;
-  const int n_nb = static_cast<int>((tr + C::BN - 1) / C::BN);
+  const int bm = fast ? F::BM : C::BM;
+  const int bn = fast ? F::BN : C::BN;
+  const int n_vb = (sh.V + bm - 1) / bm;
+  const int n_nb = static_cast<int>((tr + bn - 1) / bn);
   for (int64_t base = 0; base < sh.T; base += tr) {
     DzArgs d;
     d.weight = sh.weight;
@@ -686,11 +829,51 @@ hipError_t launch_lmhead_backward(const LMHeadShape& sh, const float* lse, const
     d.dzt = grad_weight ? dzt : nullptr;
     {
       TimedLaunch tl("k_bwd_dz", s);
-      hipLaunchKernelGGL(k_bwd_dz<C>, dim3(static_cast<unsigned>(n_vb) * n_nb), dim3(C::NT), 0, s, d);
+      const dim3 grid(static_cast<unsigned>(n_vb) * n_nb);
+      if (fast)
+        hipLaunchKernelGGL(k_bwd_dz_dtl<F>, grid, dim3(F::NT), 0, s, d);
+      else
+        hipLaunchKernelGGL(k_bwd_dz<C>, grid, dim3(C::NT), 0, s, d);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
-    if (grad_hidden) {
+    if (grad_hidden && fast) {
+      // dHidden[idx[r]] = dZ[r] . W : K = vpad split into kSplitK ranges, then a fixed-order sum
+      DenseGemmArgs g;
+      g.a = dz;
+      g.lda = vpad;
+      g.M = 0;
+      g.b = wt;
+      g.ldb = vpad;
+      g.N = sh.h;
+      g.K = static_cast<int>(vpad);
+      g.count = count;
+      g.tile_base = base;
+      g.tile_rows = static_cast<int>(tr);
+      g.m_from_count = 1;
+      g.k_from_count = 0;
+      g.splits = kSplitK;
+      g.ksplit = static_cast<int>(align_up(static_cast<size_t>((vpad + kSplitK - 1) / kSplitK), 64));
+      g.out = hpart;
+      g.ldo = sh.h;
+      g.accumulate = 0;
+      g.n_mb = static_cast<int>((tr + F::BM - 1) / F::BM);
+      g.n_nb = (sh.h + F::BN - 1) / F::BN;
+      {
+        TimedLaunch tl("k_out_gemm_dhidden", s);
+        hipLaunchKernelGGL(k_dense_gemm_dtl<F>, dim3(static_cast<unsigned>(g.n_mb) * g.n_nb * kSplitK), dim3(F::NT),
+                           0, s, g);
+      }
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      {
+        TimedLaunch tl("k_splitk_reduce", s);
+        const int64_t n4 = tr * sh.h / 4;
+        const unsigned blocks = static_cast<unsigned>(n4 < 65536 * 256 ? (n4 + 255) / 256 : 65536);
+        hipLaunchKernelGGL(k_splitk_reduce, dim3(blocks), dim3(256), 0, s, hpart, kSplitK, static_cast<int>(tr), sh.h,
+                           static_cast<const int*>(idx), static_cast<const int*>(count), base, grad_hidden);
+      }
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    } else if (grad_hidden) {
       // dHidden[idx[r]] = dZ[r] . W  :  A = dZ [rows x vpad], B = W^T [h x vpad], K = vpad
       OutGemmArgs g;
       g.op.a = dz;
@@ -718,7 +901,7 @@ hipError_t launch_lmhead_backward(const LMHeadShape& sh, const float* lse, const
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (grad_weight) {
-      // H_tile^T [h x tpad]
+      // H_tile^T [h x tpad], zero past the tile's rows
       dim3 gt(static_cast<unsigned>(tpad / 64), static_cast<unsigned>((sh.h + 63) / 64));
       {
         TimedLaunch tl("k_transpose_bf16", s);
@@ -727,29 +910,57 @@ hipError_t launch_lmhead_backward(const LMHeadShape& sh, const float* lse, const
                            ht, tpad);
       }
       if ((e = hipGetLastError()) != hipSuccess) return e;
-      // dW (+)= dZ^T . H_tile : A = dZ^T [V x tpad], B = H_tile^T [h x tpad], K = rows8
-      OutGemmArgs g;
-      g.op.a = dzt;
-      g.op.lda = tpad;
-      g.op.M = sh.V;
-      g.op.b = ht;
-      g.op.ldb = tpad;
-      g.op.b_rows = nullptr;
-      g.op.N = sh.h;
-      g.op.K = 0;
-      g.count = count;
-      g.tile_base = base;
-      g.tile_rows = static_cast<int>(tr);
-      g.mode = 1;
-      g.out_rows = nullptr;
-      g.out = grad_weight;
-      g.ldo = sh.h;
-      g.accumulate = base == 0 ? 0 : 1;
-      g.n_mb = (sh.V + C::BM - 1) / C::BM;
-      g.n_nb = (sh.h + C::BN - 1) / C::BN;
-      {
-        TimedLaunch tl("k_out_gemm_dweight", s);
-        hipLaunchKernelGGL(k_out_gemm<C>, dim3(static_cast<unsigned>(g.n_mb) * g.n_nb), dim3(C::NT), 0, s, g);
+      if (fast) {
+        // dW (+)= dZ^T . H_tile : A = dZ^T [V x tpad], B = H_tile^T [h x tpad], K = rows rounded up to 64
+        DenseGemmArgs g;
+        g.a = dzt;
+        g.lda = tpad;
+        g.M = sh.V;
+        g.b = ht;
+        g.ldb = tpad;
+        g.N = sh.h;
+        g.K = 0;
+        g.count = count;
+        g.tile_base = base;
+        g.tile_rows = static_cast<int>(tr);
+        g.m_from_count = 0;
+        g.k_from_count = 1;
+        g.splits = 1;
+        g.ksplit = static_cast<int>(tpad);
+        g.out = grad_weight;
+        g.ldo = sh.h;
+        g.accumulate = base == 0 ? 0 : 1;
+        g.n_mb = (sh.V + F::BM - 1) / F::BM;
+        g.n_nb = (sh.h + F::BN - 1) / F::BN;
+        {
+          TimedLaunch tl("k_out_gemm_dweight", s);
+          hipLaunchKernelGGL(k_dense_gemm_dtl<F>, dim3(static_cast<unsigned>(g.n_mb) * g.n_nb), dim3(F::NT), 0, s, g);
+        }
+      } else {
+        // dW (+)= dZ^T . H_tile : A = dZ^T [V x tpad], B = H_tile^T [h x tpad], K = rows8
+        OutGemmArgs g;
+        g.op.a = dzt;
+        g.op.lda = tpad;
+        g.op.M = sh.V;
+        g.op.b = ht;
+        g.op.ldb = tpad;
+        g.op.b_rows = nullptr;
+        g.op.N = sh.h;
+        g.op.K = 0;
+        g.count = count;
+        g.tile_base = base;
+        g.tile_rows = static_cast<int>(tr);
+        g.mode = 1;
+        g.out_rows = nullptr;
+        g.out = grad_weight;
+        g.ldo = sh.h;
+        g.accumulate = base == 0 ? 0 : 1;
+        g.n_mb = (sh.V + C::BM - 1) / C::BM;
+        g.n_nb = (sh.h + C::BN - 1) / C::BN;
+        {
+          TimedLaunch tl("k_out_gemm_dweight", s);
+          hipLaunchKernelGGL(k_out_gemm<C>, dim3(static_cast<unsigned>(g.n_mb) * g.n_nb), dim3(C::NT), 0, s, g);
+        }
       }
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }

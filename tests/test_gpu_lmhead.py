@@ -182,3 +182,86 @@ def _oracle_rows(A, rows, tau):
             return O.widen_bf16(Wbits[sl])
 
     return O.lm_head_logprobs_entropy(O.widen_bf16(A["hidden"][rows]), _W(), A["targets"][rows], None, tau)
+
+
+@pytest.mark.parametrize("T,h,V,tile,tau", [
+    (600, 256, 5000, 256, 0.7),   # fast path (h % 64 == 0), several tiles, ragged vocab block
+    (97, 128, 1031, 32, 1.0),     # fast path, tile smaller than one 256-row block
+])
+def test_backward_fast_path_shapes(T, h, V, tile, tau):
+    dH, dW, dH_o, dW_o, m = _backward_case(T, h, V, tile, tau, seed=T + V)
+    for got, want in ((dH, dH_o), (dW, dW_o)):
+        fro, mad = grad_errors(got, want)
+        assert fro <= TOL_GRAD and mad <= TOL_GRAD, (fro, mad)
+    assert not dH[m == 0].any()
+
+
+class _LazyW:
+    def __init__(self, bits):
+        self.bits, self.shape = bits, bits.shape
+
+    def __getitem__(self, sl):
+        return O.widen_bf16(self.bits[sl])
+
+
+@pytest.mark.timeout(900)
+def test_backward_full_width_few_rows_exact():
+    """h = 5120 and V = 151936 at their real sizes, 100 scored rows spread
+    over 4 tiles of 32: the oracle's dW and dHidden are exact here."""
+    torch = _torch()
+    cfg = synth.LMHead(T=2048, grads=True, temperature=1.0, workload=synth.W_LM_HEAD_BWD).build()
+    A = cfg.arrays
+    rng = np.random.default_rng(17)
+    mask = np.zeros(cfg.T, dtype=np.uint8)
+    mask[np.sort(rng.choice(cfg.T, 100, replace=False))] = 1
+    hd, Wd = to_dev_bits(A["hidden"], "bf16"), to_dev_bits(A["weight"], "bf16")
+    y, md = to_dev(A["targets"]), to_dev(mask)
+    lp, H, lse = _lp().lp_lm_head_logprobs_entropy(hd, Wd, y, md, 1.0, 32)
+    dH, dW = _lp().lp_lm_head_logprobs_entropy_backward(hd, Wd, y, md, 1.0, 32, lse, H,
+                                                        to_dev(A["grad_logprob"]), to_dev(A["grad_entropy"]))
+    rows = np.nonzero(mask)[0]
+    Wl = _LazyW(A["weight"])
+    _, dZ = O.lm_head_logit_grad(O.widen_bf16(A["hidden"][rows]), Wl, A["targets"][rows], None, 1.0,
+                                 A["grad_logprob"][rows], A["grad_entropy"][rows])
+    dW_o = dZ.T @ O.widen_bf16(A["hidden"][rows])
+    dH_o = np.zeros((len(rows), cfg.h))
+    for j0 in range(0, cfg.V, 16384):
+        dH_o += dZ[:, j0:j0 + 16384] @ Wl[j0:j0 + 16384]
+    fro, mad = grad_errors(host(dW), dW_o)
+    assert fro <= TOL_GRAD and mad <= TOL_GRAD, ("dW", fro, mad)
+    dHh = host(dH)
+    fro, mad = grad_errors(dHh[rows], dH_o)
+    assert fro <= TOL_GRAD and mad <= TOL_GRAD, ("dH", fro, mad)
+    assert not dHh[mask == 0].any()
+    del torch
+
+
+@pytest.mark.timeout(900)
+def test_backward_full_size_sampled():
+    """T = 114688 packed rows (80 % scored), h = 5120, V = 151936, tile 4096:
+    sampled dHidden rows against the oracle; dW against the identity
+    sum_v dW[v, :] = sum_t (sum_v dZ[t, v]) hidden[t] = 0 (rows of dZ sum to 0)."""
+    torch = _torch()
+    cfg = synth.LMHead(T=114688, prompt_frac=0.2, temperature=1.0, grads=True, workload=synth.W_LM_HEAD_BWD).build()
+    A = cfg.arrays
+    hd, Wd = to_dev_bits(A["hidden"], "bf16"), to_dev_bits(A["weight"], "bf16")
+    y, md = to_dev(A["targets"]), to_dev(A["mask"])
+    lp, H, lse = _lp().lp_lm_head_logprobs_entropy(hd, Wd, y, md, cfg.temperature, cfg.tile_rows)
+    dH, dW = _lp().lp_lm_head_logprobs_entropy_backward(hd, Wd, y, md, cfg.temperature, cfg.tile_rows, lse, H,
+                                                        to_dev(A["grad_logprob"]), to_dev(A["grad_entropy"]))
+    scored = np.nonzero(A["mask"])[0]
+    rows = np.array([scored[0], scored[4095], scored[4096], scored[len(scored) // 2], scored[-1]])
+    Wl = _LazyW(A["weight"])
+    _, dZ = O.lm_head_logit_grad(O.widen_bf16(A["hidden"][rows]), Wl, A["targets"][rows], None, cfg.temperature,
+                                 A["grad_logprob"][rows], A["grad_entropy"][rows])
+    want = np.zeros((len(rows), cfg.h))
+    for j0 in range(0, cfg.V, 16384):
+        want += dZ[:, j0:j0 + 16384] @ Wl[j0:j0 + 16384]
+    got = dH[torch.as_tensor(rows)].cpu().numpy()
+    fro, mad = grad_errors(got, want)
+    assert fro <= TOL_GRAD and mad <= TOL_GRAD, (fro, mad)
+    assert not dH[torch.as_tensor(np.nonzero(A["mask"] == 0)[0][:1000])].any().item()
+    colsum = dW.double().sum(0)
+    scale = dW.double().abs().sum(0)
+    assert torch.isfinite(dW).all().item()
+    assert (colsum.abs() <= 1e-2 * scale).all().item()
