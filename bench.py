@@ -46,6 +46,33 @@ def to_dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
 
 
+def _csrc_sha256():
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "entropy_chunked_row_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed PMC summary, or None
+    when the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+    try:
+        text = open(path).read()
+        blob = text.split("```json", 1)[1].split("```", 1)[0]
+        doc = json.loads(blob)
+    except (OSError, IndexError, ValueError):
+        return None
+    if doc.get("source_sha256") != _csrc_sha256():
+        return None
+    k = doc.get("kernels", {}).get(kernel)
+    return None if k is None else k["bytes_per_launch"]
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -90,6 +117,7 @@ def bench_lm_head_fwd(lp, torch, np, synth, O, steps, warmup, cpu_seconds):
     ms, kt = _timed(lp, torch, step, steps, warmup, ["k_fwd_tile", "k_fwd_merge", "k_compact"])
     flop_step = 2.0 * Ts * cfg.V * cfg.h
     n_launch, gemm_ms = kt["k_fwd_tile"]
+    n_tiles = (Ts + cfg.tile_rows - 1) // cfg.tile_rows
     achieved = flop_step * steps / (gemm_ms * 1e-3) / 1e12
     # parity on sampled rows
     lpv, Hv, _ = (t.cpu().numpy() for t in out["r"])
@@ -104,9 +132,12 @@ def bench_lm_head_fwd(lp, torch, np, synth, O, steps, warmup, cpu_seconds):
         T=cfg.T, scored_rows=Ts, h=cfg.h, V=cfg.V, temperature=cfg.temperature, tile_rows=cfg.tile_rows,
         ms_per_step=ms / steps, tokens_per_s=Ts * steps / (ms * 1e-3),
         roofline=dict(bound="mfma", kernel="k_fwd_tile", achieved=achieved, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                      frac=achieved / BF16_PEAK_TFLOPS, traffic=None,
+                      frac=achieved / BF16_PEAK_TFLOPS, traffic=measured_traffic("k_fwd_tile"),
+                      traffic_unit="HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                      algorithmic_hbm_bytes_per_launch=(n_tiles * cfg.V * cfg.h * 2 + Ts * cfg.h * 2) / (n_launch / steps),
                       launches_per_step=n_launch / steps, kernel_ms_per_step=gemm_ms / steps,
-                      algorithmic_flop_per_step=flop_step),
+                      algorithmic_flop_per_step=flop_step,
+                      algorithmic_flop_per_launch=flop_step / (n_launch / steps)),
         parity_max_abs_err_sampled=err, parity_tol=2e-3,
         kernel_ms_per_step={k: v[1] / steps for k, v in kt.items()},
     )
@@ -178,8 +209,10 @@ def bench_logits_input(lp, torch, np, synth, O, steps, warmup):
                  f"chunk {cfg.chunk_rows}",
         ms_per_step=ms / steps, tokens_per_s=Ts * steps / (ms * 1e-3),
         roofline=dict(bound="hbm", kernel="k_logprobs_entropy", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
-                      frac=achieved / HBM_PEAK_GBS, traffic=None, launches_per_step=n_launch / steps,
-                      algorithmic_bytes_per_step=bytes_step),
+                      frac=achieved / HBM_PEAK_GBS, traffic=measured_traffic("k_logprobs_entropy"),
+                      traffic_unit="HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                      algorithmic_bytes_per_launch=bytes_step / (n_launch / steps),
+                      launches_per_step=n_launch / steps, algorithmic_bytes_per_step=bytes_step),
         parity_max_abs_err_sampled=err, parity_tol=1e-5)
     del x, y, m, lpo, Ho
     torch.cuda.empty_cache()
@@ -207,8 +240,10 @@ def bench_kl(lp, torch, np, synth, O, steps, warmup):
         workload=f"exact KL(teacher||student) + target log-probs + masked prob diff: fp16 [{cfg.T}, {cfg.V}] x 2",
         ms_per_step=ms / steps, tokens_per_s=cfg.T * steps / (ms * 1e-3),
         roofline=dict(bound="hbm", kernel="k_kl_full_vocab", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
-                      frac=achieved / HBM_PEAK_GBS, traffic=None, launches_per_step=n_launch / steps,
-                      algorithmic_bytes_per_step=bytes_step),
+                      frac=achieved / HBM_PEAK_GBS, traffic=measured_traffic("k_kl_full_vocab"),
+                      traffic_unit="HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                      algorithmic_bytes_per_launch=bytes_step / (n_launch / steps),
+                      launches_per_step=n_launch / steps, algorithmic_bytes_per_step=bytes_step),
         parity_max_abs_err_sampled=float(np.abs(kl[rows] - kl_o).max()), parity_tol=1e-5)
     del u, v, y, dm, out
     torch.cuda.empty_cache()

@@ -44,7 +44,16 @@ using FwdCfg = GemmCfg<LP_FWD_TILE>;
 #ifndef LP_FWD_DTL_TILE
 #define LP_FWD_DTL_TILE 256, 256, 4, 2
 #endif
+#ifndef LP_FWD_RS
+#define LP_FWD_RS 0
+#endif
+#if LP_FWD_RS
+using FwdDtlCfg = RsCfg<256, 256, 2, 2>;
+#define LP_FWD_MAINLOOP gemm_tile_rs
+#else
 using FwdDtlCfg = DtlCfg<LP_FWD_DTL_TILE>;
+#define LP_FWD_MAINLOOP gemm_tile_dtl
+#endif
 
 // K splits of the dHidden GEMM (its output is only tile_rows x h, too few
 // blocks to fill the chip without splitting K = V).
@@ -62,7 +71,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 // sweep all token blocks, token-block-major inside a group, so consecutive
 // workgroups on one XCD share both weight and hidden strips in its L2.
 #ifndef LP_GROUP_V
-#define LP_GROUP_V 8
+#define LP_GROUP_V 4
 #endif
 constexpr int kGroupV = LP_GROUP_V;
 __device__ __forceinline__ void tile_coords(int L, int n_vb, int n_nb, int& vb, int& nb) {
@@ -288,8 +297,8 @@ __global__ void __launch_bounds__(C::NT) k_fwd_tile_dtl(FwdArgs a) {
   if (n0 >= rows) return;
   const int v0 = vb * C::BM;
   f32x16_t acc[C::MI][C::NI];
-  gemm_tile_dtl<C>(a.weight + static_cast<int64_t>(v0) * a.ld_w, a.ld_w, a.V - v0, a.hidden, a.ld_h,
-                   a.idx + a.tile_base + n0, rows - n0, a.h, lds, acc);
+  LP_FWD_MAINLOOP<C>(a.weight + static_cast<int64_t>(v0) * a.ld_w, a.ld_w, a.V - v0, a.hidden, a.ld_h,
+                     a.idx + a.tile_base + n0, rows - n0, a.h, lds, acc);
   fwd_epilogue<C>(a, acc, vb, n0, rows, lds);
 }
 
@@ -587,7 +596,7 @@ __global__ void __launch_bounds__(C::NT) k_bwd_dz_dtl(DzArgs a) {
   if (rows <= 0 || n0 >= rowsK) return;
   const int v0 = vb * C::BM;
   f32x16_t acc[C::MI][C::NI];
-  gemm_tile_dtl<C>(a.weight + static_cast<int64_t>(v0) * a.ld_w, a.ld_w, a.V - v0, a.hidden, a.ld_h,
+  LP_FWD_MAINLOOP<C>(a.weight + static_cast<int64_t>(v0) * a.ld_w, a.ld_w, a.V - v0, a.hidden, a.ld_h,
                    a.idx + a.tile_base + n0, rows - n0, a.h, lds, acc);
   dz_epilogue<C>(a, acc, v0, n0, rows, rowsK);
 }
@@ -638,7 +647,7 @@ __global__ void __launch_bounds__(C::NT) k_dense_gemm_dtl(DenseGemmArgs g) {
   const int kbeg = ks * g.ksplit;
   const int klen = (K - kbeg < g.ksplit) ? (K - kbeg) : g.ksplit;
   f32x16_t acc[C::MI][C::NI];
-  gemm_tile_dtl<C>(g.a + static_cast<int64_t>(m0) * g.lda + kbeg, g.lda, M - m0,
+  LP_FWD_MAINLOOP<C>(g.a + static_cast<int64_t>(m0) * g.lda + kbeg, g.lda, M - m0,
                    g.b + static_cast<int64_t>(n0) * g.ldb + kbeg, g.ldb, nullptr, g.N - n0, klen > 0 ? klen : 0, lds,
                    acc);
   const int lane = threadIdx.x & 63;
