@@ -17,7 +17,8 @@ from ._lib import LP_BF16, LP_FP16, LP_FP32, LPError, check, load
 __all__ = [
     "lp_logprobs_entropy", "lp_lm_head_logprobs_entropy", "lp_lm_head_logprobs_entropy_backward",
     "lp_lm_head_workspace_bytes", "lp_kl_full_vocab", "lp_prob_diff", "lp_version", "lp_timing_enable",
-    "lp_timing_read", "LPError", "load",
+    "lp_timing_read", "lp_logprobs_entropy_k", "lp_lm_head_logprobs_entropy_k",
+    "lp_lm_head_logprobs_entropy_backward_k", "lp_prob_diff_stats", "LPError", "load",
 ]
 
 
@@ -224,4 +225,97 @@ def lp_prob_diff(lp_a, lp_b, mask=None, *, out=None, stream=None):
         out = torch.empty(n, dtype=torch.float32, device=lp_a.device)
     st = lib.lp_prob_diff(_ptr(lp_a), _ptr(lp_b), _ptr(mask), n, _ptr(out), _stream(stream))
     check("lp_prob_diff", st)
+    return out
+
+
+def _targets_k(targets, T):
+    torch = _torch()
+    t = _vec(targets, "targets", torch.int64)
+    if t.dim() != 2 or t.size(0) != T:
+        raise ValueError("targets must be [T, K]")
+    return t, t.size(1)
+
+
+def lp_logprobs_entropy_k(logits, targets, mask=None, temperature: float = 1.0, chunk_rows: int = -1, *,
+                          want_entropy: bool = True, stream=None):
+    """(logprob [T, K], entropy [T] or None) with K targets per row (targets [T, K] int64)."""
+    torch = _torch()
+    lib = load()
+    _dev(logits, "logits")
+    T, V = logits.shape
+    targets, K = _targets_k(targets, T)
+    mask = _vec(mask, "mask", torch.uint8)
+    lp = torch.empty((T, K), dtype=torch.float32, device=logits.device)
+    H = torch.empty(T, dtype=torch.float32, device=logits.device) if want_entropy else None
+    st = lib.lp_logprobs_entropy_k(_ptr(logits), _dtype_code(logits), T, V, _rows(logits, "logits"), _ptr(targets), K,
+                                   _ptr(mask), float(temperature), int(chunk_rows), _ptr(lp), _ptr(H),
+                                   _stream(stream))
+    check("lp_logprobs_entropy_k", st)
+    return lp, H
+
+
+def lp_lm_head_logprobs_entropy_k(hidden, weight, targets, mask=None, temperature: float = 1.0,
+                                  tile_rows: int = 4096, *, workspace=None, stream=None):
+    """(logprob [T, K], entropy [T], lse [T]) of the fused LM head with K targets per row."""
+    torch = _torch()
+    lib = load()
+    _dev(hidden, "hidden")
+    _dev(weight, "weight")
+    T, h = hidden.shape
+    V = weight.shape[0]
+    targets, K = _targets_k(targets, T)
+    mask = _vec(mask, "mask", torch.uint8)
+    dev = hidden.device
+    lp = torch.empty((T, K), dtype=torch.float32, device=dev)
+    H = torch.empty(T, dtype=torch.float32, device=dev)
+    lse = torch.empty(T, dtype=torch.float32, device=dev)
+    ws = _workspace(lp_lm_head_workspace_bytes(T, h, V, tile_rows, False), dev, workspace)
+    st = lib.lp_lm_head_logprobs_entropy_k(_ptr(hidden), _rows(hidden, "hidden"), _ptr(weight),
+                                           _rows(weight, "weight"), T, h, V, _ptr(targets), K, _ptr(mask),
+                                           float(temperature), int(tile_rows), _ptr(lp), _ptr(H), _ptr(lse), _ptr(ws),
+                                           ws.numel(), _stream(stream))
+    check("lp_lm_head_logprobs_entropy_k", st)
+    return lp, H, lse
+
+
+def lp_lm_head_logprobs_entropy_backward_k(hidden, weight, targets, mask, temperature: float, tile_rows: int,
+                                           lse, entropy, grad_logprob, grad_entropy=None, *,
+                                           need_grad_hidden: bool = True, need_grad_weight: bool = True,
+                                           workspace=None, stream=None):
+    """Backward of the K-target fused LM head; grad_logprob is [T, K]."""
+    torch = _torch()
+    lib = load()
+    T, h = hidden.shape
+    V = weight.shape[0]
+    targets, K = _targets_k(targets, T)
+    mask = _vec(mask, "mask", torch.uint8)
+    grad_logprob = _vec(grad_logprob, "grad_logprob", torch.float32)
+    if grad_logprob.shape != (T, K):
+        raise ValueError("grad_logprob must be [T, K]")
+    grad_entropy = _vec(grad_entropy, "grad_entropy", torch.float32)
+    dev = hidden.device
+    dH = torch.empty((T, h), dtype=torch.float32, device=dev) if need_grad_hidden else None
+    dW = torch.empty((V, h), dtype=torch.float32, device=dev) if need_grad_weight else None
+    ws = _workspace(lp_lm_head_workspace_bytes(T, h, V, tile_rows, True), dev, workspace)
+    st = lib.lp_lm_head_logprobs_entropy_backward_k(
+        _ptr(hidden), _rows(hidden, "hidden"), _ptr(weight), _rows(weight, "weight"), T, h, V, _ptr(targets), K,
+        _ptr(mask), float(temperature), int(tile_rows), _ptr(_vec(lse, "lse", torch.float32)),
+        _ptr(_vec(entropy, "entropy", torch.float32)), _ptr(grad_logprob), _ptr(grad_entropy), _ptr(dH), _ptr(dW),
+        _ptr(ws), ws.numel(), _stream(stream))
+    check("lp_lm_head_logprobs_entropy_backward_k", st)
+    return dH, dW
+
+
+def lp_prob_diff_stats(lp_a, lp_b, mask=None, *, stream=None):
+    """Device float64 [5]: count, max, mean, std of mask * |exp(a) - exp(b)| and Pearson(exp(a), exp(b))."""
+    torch = _torch()
+    lib = load()
+    lp_a = _vec(lp_a, "lp_a", torch.float32)
+    lp_b = _vec(lp_b, "lp_b", torch.float32)
+    mask = _vec(mask, "mask", torch.uint8)
+    out = torch.empty(5, dtype=torch.float64, device=lp_a.device)
+    ws = torch.empty(max(int(lib.lp_prob_diff_stats_workspace_bytes()), 256), dtype=torch.uint8, device=lp_a.device)
+    st = lib.lp_prob_diff_stats(_ptr(lp_a), _ptr(lp_b), _ptr(mask), lp_a.numel(), _ptr(out), _ptr(ws), ws.numel(),
+                                _stream(stream))
+    check("lp_prob_diff_stats", st)
     return out

@@ -31,6 +31,15 @@ SIGNATURES = {
     "lp_kl_full_vocab": (c_int, [c_vp, c_vp, c_int, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                  c_vp]),
     "lp_prob_diff": (c_int, [c_vp, c_vp, c_vp, c_i64, c_vp, c_vp]),
+    "lp_logprobs_entropy_k": (c_int, [c_vp, c_int, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_f, c_i64, c_vp, c_vp,
+                                      c_vp]),
+    "lp_lm_head_logprobs_entropy_k": (c_int, [c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_f,
+                                              c_i64, c_vp, c_vp, c_vp, c_vp, ctypes.c_size_t, c_vp]),
+    "lp_lm_head_logprobs_entropy_backward_k": (c_int, [c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_i64, c_vp, c_i64,
+                                                       c_vp, c_f, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                                       ctypes.c_size_t, c_vp]),
+    "lp_prob_diff_stats_workspace_bytes": (ctypes.c_size_t, []),
+    "lp_prob_diff_stats": (c_int, [c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, ctypes.c_size_t, c_vp]),
     "lp_timing_enable": (None, [c_int]),
     "lp_timing_read": (c_int, [ctypes.c_char_p, ctypes.POINTER(c_i64), ctypes.POINTER(ctypes.c_double)]),
 }

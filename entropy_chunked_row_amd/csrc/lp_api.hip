@@ -64,9 +64,11 @@ const char* lp_status_string(int status) {
 
 const char* lp_last_error(void) { return g_err; }
 
-lp_status lp_logprobs_entropy(const void* logits, lp_dtype dtype, int64_t T, int64_t V, int64_t ld,
-                              const int64_t* targets, const uint8_t* mask, float temperature,
-                              int64_t chunk_rows, float* logprob, float* entropy, void* stream) {
+static lp_status logprobs_entropy_impl(const void* logits, lp_dtype dtype, int64_t T, int64_t V, int64_t ld,
+                                       const int64_t* targets, int64_t K, const uint8_t* mask, float temperature,
+                                       int64_t chunk_rows, float* logprob, float* entropy, void* stream) {
+  if (K < 1 || K > lp::kMaxTargets)
+    return fail(LP_ERR_INVALID_ARGUMENT, "lp_logprobs_entropy: K must be in 1..%d", lp::kMaxTargets);
   if (dtype != LP_BF16 && dtype != LP_FP16 && dtype != LP_FP32)
     return fail(LP_ERR_INVALID_ARGUMENT, "lp_logprobs_entropy: unknown dtype %d", static_cast<int>(dtype));
   if (T < 0) return fail(LP_ERR_INVALID_ARGUMENT, "lp_logprobs_entropy: T < 0");
@@ -87,6 +89,7 @@ lp_status lp_logprobs_entropy(const void* logits, lp_dtype dtype, int64_t T, int
   a.ld = ld;
   a.V = static_cast<int>(V);
   a.targets = targets;
+  a.K = static_cast<int>(K);
   a.mask = mask;
   a.c = exp2_scale(temperature);
   a.logprob = logprob;
@@ -98,6 +101,20 @@ lp_status lp_logprobs_entropy(const void* logits, lp_dtype dtype, int64_t T, int
     if (e != hipSuccess) return hip_fail(e, "lp_logprobs_entropy launch");
   }
   return ok();
+}
+
+lp_status lp_logprobs_entropy(const void* logits, lp_dtype dtype, int64_t T, int64_t V, int64_t ld,
+                              const int64_t* targets, const uint8_t* mask, float temperature,
+                              int64_t chunk_rows, float* logprob, float* entropy, void* stream) {
+  return logprobs_entropy_impl(logits, dtype, T, V, ld, targets, 1, mask, temperature, chunk_rows, logprob, entropy,
+                               stream);
+}
+
+lp_status lp_logprobs_entropy_k(const void* logits, lp_dtype dtype, int64_t T, int64_t V, int64_t ld,
+                                const int64_t* targets, int64_t K, const uint8_t* mask, float temperature,
+                                int64_t chunk_rows, float* logprob, float* entropy, void* stream) {
+  return logprobs_entropy_impl(logits, dtype, T, V, ld, targets, K, mask, temperature, chunk_rows, logprob, entropy,
+                               stream);
 }
 
 size_t lp_lm_head_workspace_bytes(int64_t T, int64_t h, int64_t V, int64_t tile_rows, int backward) {
@@ -133,7 +150,7 @@ static lp_status check_lmhead(const char* fn, const void* hidden, int64_t ld_h, 
 }
 
 static lp::LMHeadShape make_shape(const void* hidden, int64_t ld_h, const void* weight, int64_t ld_w, int64_t T,
-                                  int64_t h, int64_t V, const int64_t* targets, const uint8_t* mask,
+                                  int64_t h, int64_t V, const int64_t* targets, int64_t K, const uint8_t* mask,
                                   float temperature, int64_t tile_rows) {
   lp::LMHeadShape sh;
   sh.hidden = static_cast<const uint16_t*>(hidden);
@@ -144,6 +161,7 @@ static lp::LMHeadShape make_shape(const void* hidden, int64_t ld_h, const void* 
   sh.h = static_cast<int>(h);
   sh.V = static_cast<int>(V);
   sh.targets = targets;
+  sh.K = static_cast<int>(K);
   sh.mask = mask;
   sh.c = exp2_scale(temperature);
   sh.inv_tau = temperature_applies(temperature) ? 1.0f / temperature : 1.0f;
@@ -151,34 +169,50 @@ static lp::LMHeadShape make_shape(const void* hidden, int64_t ld_h, const void* 
   return sh;
 }
 
-lp_status lp_lm_head_logprobs_entropy(const void* hidden, int64_t ld_h, const void* weight, int64_t ld_w,
-                                      int64_t T, int64_t h, int64_t V, const int64_t* targets,
-                                      const uint8_t* mask, float temperature, int64_t tile_rows,
+static lp_status lm_head_forward_impl(const char* fn, const void* hidden, int64_t ld_h, const void* weight,
+                                      int64_t ld_w, int64_t T, int64_t h, int64_t V, const int64_t* targets,
+                                      int64_t K, const uint8_t* mask, float temperature, int64_t tile_rows,
                                       float* logprob, float* entropy, float* lse, void* workspace,
                                       size_t workspace_bytes, void* stream) {
-  const char* fn = "lp_lm_head_logprobs_entropy";
+  if (K < 1 || K > lp::kMaxTargets) return fail(LP_ERR_INVALID_ARGUMENT, "%s: K must be in 1..%d", fn, lp::kMaxTargets);
   lp::LMHeadWorkspace w;
   lp_status st = check_lmhead(fn, hidden, ld_h, weight, ld_w, T, h, V, targets, temperature, tile_rows,
                               workspace, workspace_bytes, 0, &w);
   if (st != LP_OK) return st;
   if (T == 0) return ok();
   if (!logprob) return fail(LP_ERR_INVALID_ARGUMENT, "%s: logprob is required", fn);
-  lp::LMHeadShape sh = make_shape(hidden, ld_h, weight, ld_w, T, h, V, targets, mask, temperature, tile_rows);
+  lp::LMHeadShape sh = make_shape(hidden, ld_h, weight, ld_w, T, h, V, targets, K, mask, temperature, tile_rows);
   hipError_t e = lp::launch_lmhead_forward(sh, logprob, entropy, lse, static_cast<char*>(workspace), w,
                                            static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, fn);
   return ok();
 }
 
-lp_status lp_lm_head_logprobs_entropy_backward(const void* hidden, int64_t ld_h, const void* weight,
-                                               int64_t ld_w, int64_t T, int64_t h, int64_t V,
-                                               const int64_t* targets, const uint8_t* mask,
-                                               float temperature, int64_t tile_rows, const float* lse,
-                                               const float* entropy, const float* grad_logprob,
-                                               const float* grad_entropy, float* grad_hidden,
-                                               float* grad_weight, void* workspace, size_t workspace_bytes,
-                                               void* stream) {
-  const char* fn = "lp_lm_head_logprobs_entropy_backward";
+lp_status lp_lm_head_logprobs_entropy(const void* hidden, int64_t ld_h, const void* weight, int64_t ld_w,
+                                      int64_t T, int64_t h, int64_t V, const int64_t* targets,
+                                      const uint8_t* mask, float temperature, int64_t tile_rows,
+                                      float* logprob, float* entropy, float* lse, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  return lm_head_forward_impl("lp_lm_head_logprobs_entropy", hidden, ld_h, weight, ld_w, T, h, V, targets, 1, mask,
+                              temperature, tile_rows, logprob, entropy, lse, workspace, workspace_bytes, stream);
+}
+
+lp_status lp_lm_head_logprobs_entropy_k(const void* hidden, int64_t ld_h, const void* weight, int64_t ld_w,
+                                        int64_t T, int64_t h, int64_t V, const int64_t* targets, int64_t K,
+                                        const uint8_t* mask, float temperature, int64_t tile_rows, float* logprob,
+                                        float* entropy, float* lse, void* workspace, size_t workspace_bytes,
+                                        void* stream) {
+  return lm_head_forward_impl("lp_lm_head_logprobs_entropy_k", hidden, ld_h, weight, ld_w, T, h, V, targets, K, mask,
+                              temperature, tile_rows, logprob, entropy, lse, workspace, workspace_bytes, stream);
+}
+
+static lp_status lm_head_backward_impl(const char* fn, const void* hidden, int64_t ld_h, const void* weight,
+                                       int64_t ld_w, int64_t T, int64_t h, int64_t V, const int64_t* targets,
+                                       int64_t K, const uint8_t* mask, float temperature, int64_t tile_rows,
+                                       const float* lse, const float* entropy, const float* grad_logprob,
+                                       const float* grad_entropy, float* grad_hidden, float* grad_weight,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (K < 1 || K > lp::kMaxTargets) return fail(LP_ERR_INVALID_ARGUMENT, "%s: K must be in 1..%d", fn, lp::kMaxTargets);
   lp::LMHeadWorkspace w;
   lp_status st = check_lmhead(fn, hidden, ld_h, weight, ld_w, T, h, V, targets, temperature, tile_rows,
                               workspace, workspace_bytes, 1, &w);
@@ -194,11 +228,36 @@ lp_status lp_lm_head_logprobs_entropy_backward(const void* hidden, int64_t ld_h,
   }
   if (!lse || !entropy || !grad_logprob)
     return fail(LP_ERR_INVALID_ARGUMENT, "%s: lse, entropy and grad_logprob are required", fn);
-  lp::LMHeadShape sh = make_shape(hidden, ld_h, weight, ld_w, T, h, V, targets, mask, temperature, tile_rows);
+  lp::LMHeadShape sh = make_shape(hidden, ld_h, weight, ld_w, T, h, V, targets, K, mask, temperature, tile_rows);
   hipError_t e = lp::launch_lmhead_backward(sh, lse, entropy, grad_logprob, grad_entropy, grad_hidden,
                                             grad_weight, static_cast<char*>(workspace), w, s);
   if (e != hipSuccess) return hip_fail(e, fn);
   return ok();
+}
+
+lp_status lp_lm_head_logprobs_entropy_backward(const void* hidden, int64_t ld_h, const void* weight,
+                                               int64_t ld_w, int64_t T, int64_t h, int64_t V,
+                                               const int64_t* targets, const uint8_t* mask,
+                                               float temperature, int64_t tile_rows, const float* lse,
+                                               const float* entropy, const float* grad_logprob,
+                                               const float* grad_entropy, float* grad_hidden,
+                                               float* grad_weight, void* workspace, size_t workspace_bytes,
+                                               void* stream) {
+  return lm_head_backward_impl("lp_lm_head_logprobs_entropy_backward", hidden, ld_h, weight, ld_w, T, h, V, targets,
+                               1, mask, temperature, tile_rows, lse, entropy, grad_logprob, grad_entropy, grad_hidden,
+                               grad_weight, workspace, workspace_bytes, stream);
+}
+
+lp_status lp_lm_head_logprobs_entropy_backward_k(const void* hidden, int64_t ld_h, const void* weight,
+                                                 int64_t ld_w, int64_t T, int64_t h, int64_t V,
+                                                 const int64_t* targets, int64_t K, const uint8_t* mask,
+                                                 float temperature, int64_t tile_rows, const float* lse,
+                                                 const float* entropy, const float* grad_logprob,
+                                                 const float* grad_entropy, float* grad_hidden, float* grad_weight,
+                                                 void* workspace, size_t workspace_bytes, void* stream) {
+  return lm_head_backward_impl("lp_lm_head_logprobs_entropy_backward_k", hidden, ld_h, weight, ld_w, T, h, V, targets,
+                               K, mask, temperature, tile_rows, lse, entropy, grad_logprob, grad_entropy, grad_hidden,
+                               grad_weight, workspace, workspace_bytes, stream);
 }
 
 lp_status lp_kl_full_vocab(const void* student, const void* teacher, lp_dtype dtype, int64_t T, int64_t V,
@@ -244,6 +303,23 @@ lp_status lp_prob_diff(const float* lp_a, const float* lp_b, const uint8_t* mask
   if (!lp_a || !lp_b || !out) return fail(LP_ERR_INVALID_ARGUMENT, "lp_prob_diff: lp_a, lp_b, out required");
   hipError_t e = lp::launch_prob_diff(lp_a, lp_b, mask, n, out, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "lp_prob_diff");
+  return ok();
+}
+
+size_t lp_prob_diff_stats_workspace_bytes(void) { return lp::prob_diff_stats_workspace_bytes(); }
+
+lp_status lp_prob_diff_stats(const float* lp_a, const float* lp_b, const uint8_t* mask, int64_t n, double* out,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "lp_prob_diff_stats";
+  if (n < 0) return fail(LP_ERR_INVALID_ARGUMENT, "%s: n < 0", fn);
+  if (!out) return fail(LP_ERR_INVALID_ARGUMENT, "%s: out is required", fn);
+  if (n > 0 && (!lp_a || !lp_b)) return fail(LP_ERR_INVALID_ARGUMENT, "%s: lp_a and lp_b are required", fn);
+  if (!workspace || workspace_bytes < lp::prob_diff_stats_workspace_bytes())
+    return fail(LP_ERR_WORKSPACE_TOO_SMALL, "%s: workspace needs %zu bytes", fn, lp::prob_diff_stats_workspace_bytes());
+  if (!aligned(workspace, 256) || !aligned(out, 8))
+    return fail(LP_ERR_INVALID_ARGUMENT, "%s: misaligned workspace or out", fn);
+  hipError_t e = lp::launch_prob_diff_stats(lp_a, lp_b, mask, n, out, workspace, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, fn);
   return ok();
 }
 

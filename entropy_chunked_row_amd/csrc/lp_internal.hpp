@@ -8,6 +8,9 @@
 
 namespace lp {
 
+// Most targets per row the K-target entry points accept.
+constexpr int kMaxTargets = 64;
+
 // RAII bracket around one kernel launch: records HIP events on the launch
 // stream when timing is enabled (lp_timing_enable), else does nothing.
 class TimedLaunch {
@@ -30,10 +33,11 @@ struct RowArgs {
   int V;
   int64_t row0;
   int64_t rows;
-  const int64_t* targets;
+  const int64_t* targets;  // [T x K]
+  int K;                   // targets per row
   const uint8_t* mask;
   float c;  // log2(e) / tau_effective, rounded once on the host
-  float* logprob;
+  float* logprob;          // [T x K]
   float* entropy;
 };
 
@@ -57,6 +61,11 @@ hipError_t launch_kl_full_vocab(int dtype, const KLArgs& a, hipStream_t s);
 hipError_t launch_prob_diff(const float* a, const float* b, const uint8_t* mask, int64_t n, float* out,
                             hipStream_t s);
 
+// Aggregates of the masked prob diff: out[0..4] = count, max, mean, std, pearson.
+size_t prob_diff_stats_workspace_bytes();
+hipError_t launch_prob_diff_stats(const float* a, const float* b, const uint8_t* mask, int64_t n, double* out,
+                                  void* ws, hipStream_t s);
+
 // ---------------------------------------------------------------------------
 // fused LM head
 // ---------------------------------------------------------------------------
@@ -69,7 +78,8 @@ struct LMHeadShape {
   int64_t T;
   int h;
   int V;
-  const int64_t* targets;
+  const int64_t* targets;  // [T x K]
+  int K;                   // targets per row (1 .. kMaxTargets)
   const uint8_t* mask;
   float c;        // log2(e) / tau_effective
   float inv_tau;  // 1 / tau_effective

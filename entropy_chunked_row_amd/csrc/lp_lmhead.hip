@@ -115,7 +115,7 @@ bool lmhead_workspace_layout(int64_t T, int64_t h, int64_t V, int64_t tile_rows,
     w->part_off = off;
     off = align_up(off + static_cast<size_t>(tr) * w->n_vblocks * 3 * 4, 256);
     w->zy_off = off;
-    off = align_up(off + static_cast<size_t>(tr) * 4, 256);
+    off = align_up(off + static_cast<size_t>(tr) * kMaxTargets * 4, 256);
   } else {
     const size_t tpad = align_up(static_cast<size_t>(tr), 64);
     w->dz_off = off;  // dZ [tpad x vpad], dZ^T [vpad x tpad], W^T [h x vpad], H_tile^T [h x tpad]
@@ -134,7 +134,7 @@ bool lmhead_workspace_layout(int64_t T, int64_t h, int64_t V, int64_t tile_rows,
 // ---------------------------------------------------------------------------
 
 __global__ void __launch_bounds__(1024) k_compact(const uint8_t* __restrict__ mask, int64_t T, int* __restrict__ idx,
-                                                  int* __restrict__ count, float* o1, float* o2, float* o3) {
+                                                  int* __restrict__ count, float* o1, int k1, float* o2, float* o3) {
   __shared__ int sums[1024];
   const int tid = threadIdx.x;
   const int64_t per = (T + 1023) / 1024;
@@ -155,7 +155,8 @@ __global__ void __launch_bounds__(1024) k_compact(const uint8_t* __restrict__ ma
     if (mask == nullptr || mask[i] != 0) {
       idx[pos++] = static_cast<int>(i);
     } else {
-      if (o1) o1[i] = 0.f;
+      if (o1)
+        for (int k = 0; k < k1; ++k) o1[i * k1 + k] = 0.f;
       if (o2) o2[i] = 0.f;
       if (o3) o3[i] = 0.f;
     }
@@ -175,13 +176,14 @@ struct FwdArgs {
   int h, V;
   const int* idx;
   const int* count;
-  const int64_t* targets;
+  const int64_t* targets;  // [T x K]
+  int K;
   float c;
   int64_t tile_base;
   int tile_rows;
   int n_vb, n_nb;
   float* part;  // [tile_rows][n_vb][3]
-  float* zy;    // [tile_rows]
+  float* zy;    // [tile_rows][K]
 };
 
 // Forward epilogue shared by both GEMM mainloops: per token column, fold the
@@ -197,40 +199,54 @@ __device__ __forceinline__ void fwd_epilogue(const FwdArgs& a, f32x16_t (&acc)[C
   const int half = lane >> 5;
   Stat* sm = reinterpret_cast<Stat*>(lds);  // [WGM][BN] states, reused after the K loop
   const float c = a.c;
+  const bool full_block = (vb + 1) * C::BM <= a.V;  // uniform
 #pragma unroll
   for (int ni = 0; ni < C::NI; ++ni) {
     const int nl = wn * C::WTN + ni * 32 + (lane & 31);
     const int r = n0 + nl;  // row within the tile
     const bool valid_row = r < rows;
-    int64_t y = -1;
-    if (valid_row) y = a.targets[a.idx[a.tile_base + r]];
-    const int64_t yrel = y - vwave;
+    const int64_t row = valid_row ? a.idx[a.tile_base + r] : 0;
     Stat st = stat_empty();
+    if (full_block) {
+      // every vocab row of this block exists: plain fold
 #pragma unroll
-    for (int mi = 0; mi < C::MI; ++mi) {
-      float x[16];
+      for (int mi = 0; mi < C::MI; ++mi) {
+        float x[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int v = vwave + mi * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-        // rows past V hold zeros from the GEMM: probability 0 (-inf with the clamped fold)
-        x[i] = (v < a.V) ? acc[mi][ni][i] : -INFINITY;
+        for (int i = 0; i < 16; ++i) x[i] = acc[mi][ni][i];
+        stat_push<false, 16, 16>(st, x, c);
       }
-      stat_push<true, 16, 16>(st, x, c);
-    }
-    if (valid_row && yrel >= 0 && yrel < C::WTM) {
-      float zsel = 0.f;
-      bool found = false;
+    } else {
 #pragma unroll
-      for (int mi = 0; mi < C::MI; ++mi)
+      for (int mi = 0; mi < C::MI; ++mi) {
+        float x[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int vr = mi * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-          if (yrel == vr) {
-            zsel = acc[mi][ni][i];
-            found = true;
-          }
+          const int v = vwave + mi * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+          // rows past V hold zeros from the GEMM: probability 0 (-inf with the clamped fold)
+          x[i] = (v < a.V) ? acc[mi][ni][i] : -INFINITY;
         }
-      if (found) a.zy[r] = zsel;
+        stat_push<true, 16, 16>(st, x, c);
+      }
+    }
+    // target logits whose column lies in this wave's vocab rows
+    for (int k = 0; valid_row && k < a.K; ++k) {
+      const int64_t yrel = a.targets[row * a.K + k] - vwave;
+      if (yrel >= 0 && yrel < C::WTM) {
+        float zsel = 0.f;
+        bool found = false;
+#pragma unroll
+        for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int vr = mi * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+            if (yrel == vr) {
+              zsel = acc[mi][ni][i];
+              found = true;
+            }
+          }
+        if (found) a.zy[static_cast<int64_t>(r) * a.K + k] = zsel;
+      }
     }
     Stat o;
     o.mc = __shfl_xor(st.mc, 32, 64);
@@ -308,12 +324,13 @@ struct MergeArgs {
   int n_vb;
   const int* idx;
   const int* count;
-  const int64_t* targets;
+  const int64_t* targets;  // [T x K]
+  int K;
   int V;
   float c;
   int64_t tile_base;
   int tile_rows;
-  float* logprob;
+  float* logprob;  // [T x K]
   float* entropy;
   float* lse;
 };
@@ -329,13 +346,15 @@ __global__ void __launch_bounds__(256) k_fwd_merge(MergeArgs a) {
   Stat st = stat_empty();
   for (int vb = lane; vb < a.n_vb; vb += 64) st = stat_merge(st, Stat{p[vb * 3], p[vb * 3 + 1], p[vb * 3 + 2]});
   st = stat_wave_allreduce(st);
-  if (lane == 0) {
-    const int row = a.idx[a.tile_base + r];
-    const int64_t y = a.targets[row];
-    const float l2s = log2f(st.s);
+  const int64_t row = a.idx[a.tile_base + r];
+  const float l2s = log2f(st.s);
+  for (int k = lane; k < a.K; k += 64) {
+    const int64_t y = a.targets[row * a.K + k];
     float lp = __builtin_nanf("");
-    if (y >= 0 && y < a.V) lp = (fmaf(a.zy[r], a.c, -st.mc) - l2s) * kLn2;
-    a.logprob[row] = lp;
+    if (y >= 0 && y < a.V) lp = (fmaf(a.zy[static_cast<int64_t>(r) * a.K + k], a.c, -st.mc) - l2s) * kLn2;
+    a.logprob[row * a.K + k] = lp;
+  }
+  if (lane == 0) {
     if (a.entropy) a.entropy[row] = (l2s - st.a / st.s) * kLn2;
     if (a.lse) a.lse[row] = (st.mc + l2s) * kLn2;
   }
@@ -349,7 +368,7 @@ hipError_t launch_lmhead_forward(const LMHeadShape& sh, float* logprob, float* e
   float* zy = reinterpret_cast<float*>(ws + w.zy_off);
   {
     TimedLaunch tl("k_compact", s);
-    hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, s, sh.mask, sh.T, idx, count, logprob, entropy, lse);
+    hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, s, sh.mask, sh.T, idx, count, logprob, sh.K, entropy, lse);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -371,6 +390,7 @@ hipError_t launch_lmhead_forward(const LMHeadShape& sh, float* logprob, float* e
     a.idx = idx;
     a.count = count;
     a.targets = sh.targets;
+    a.K = sh.K;
     a.c = sh.c;
     a.tile_base = base;
     a.tile_rows = static_cast<int>(tr);
@@ -394,6 +414,7 @@ hipError_t launch_lmhead_forward(const LMHeadShape& sh, float* logprob, float* e
     m.idx = idx;
     m.count = count;
     m.targets = sh.targets;
+    m.K = sh.K;
     m.V = sh.V;
     m.c = sh.c;
     m.tile_base = base;
@@ -480,10 +501,11 @@ struct DzArgs {
   int64_t vpad;
   const int* idx;
   const int* count;
-  const int64_t* targets;
+  const int64_t* targets;  // [T x K]
+  int K;
   const float* lse;
   const float* entropy;
-  const float* g_lp;
+  const float* g_lp;  // [T x K]
   const float* g_H;
   float c, inv_tau;
   int64_t tile_base;
@@ -509,15 +531,17 @@ __device__ __forceinline__ void dz_epilogue(const DzArgs& a, f32x16_t (&acc)[C::
     const int r = n0 + wn * C::WTN + ni * 32 + (lane & 31);
     if (r >= rowsK) continue;
     const bool valid = r < rows;
-    int64_t y = -1;
-    float l2 = 0.f, mu = 0.f, glp = 0.f, gh = 0.f;
+    int64_t row = 0, y0 = -1;
+    float l2 = 0.f, mu = 0.f, g0 = 0.f, gsum = 0.f, gh = 0.f;
     if (valid) {
-      const int row = a.idx[a.tile_base + r];
-      y = a.targets[row];
+      row = a.idx[a.tile_base + r];
       const float L = a.lse[row];
       l2 = L * kLog2eF;
       mu = L - a.entropy[row];
-      glp = a.g_lp[row];
+      y0 = a.targets[row * a.K];
+      g0 = a.g_lp[row * a.K];
+      gsum = g0;
+      for (int k = 1; k < a.K; ++k) gsum += a.g_lp[row * a.K + k];
       gh = a.g_H ? a.g_H[row] : 0.f;
     }
 #pragma unroll
@@ -531,11 +555,14 @@ __device__ __forceinline__ void dz_epilogue(const DzArgs& a, f32x16_t (&acc)[C::
           const int v = vq + j;
           float d = 0.f;
           if (valid && v < a.V) {
+            // sum of g_lp over the row's targets that sit in this column (usually none)
+            float onehot = (v == y0) ? g0 : 0.f;
+            for (int k = 1; k < a.K; ++k)
+              if (a.targets[row * a.K + k] == v) onehot += a.g_lp[row * a.K + k];
             const float z = acc[mi][ni][q * 4 + j];
             const float p = fast_exp2(fmaf(z, a.c, -l2));
             const float zt = z * a.inv_tau;
-            const float onehot = (v == y) ? 1.f : 0.f;
-            d = a.inv_tau * (glp * (onehot - p) - gh * p * (zt - mu));
+            d = a.inv_tau * (onehot - gsum * p - gh * p * (zt - mu));
           }
           outv[j] = f32_to_bf16_rne(d);
         }
@@ -786,7 +813,7 @@ hipError_t launch_lmhead_backward(const LMHeadShape& sh, const float* lse, const
   {
     TimedLaunch tl("k_compact", s);
     hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, s, sh.mask, sh.T, idx, count, static_cast<float*>(nullptr),
-                       static_cast<float*>(nullptr), static_cast<float*>(nullptr));
+                       0, static_cast<float*>(nullptr), static_cast<float*>(nullptr));
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -823,6 +850,7 @@ hipError_t launch_lmhead_backward(const LMHeadShape& sh, const float* lse, const
     d.idx = idx;
     d.count = count;
     d.targets = sh.targets;
+    d.K = sh.K;
     d.lse = lse;
     d.entropy = entropy;
     d.g_lp = grad_logprob;

@@ -58,10 +58,8 @@ __global__ void __launch_bounds__(NT) k_logprobs_entropy(RowArgs args) {
   __shared__ Stat sm[NT / 64];
   const int64_t row = args.row0 + blockIdx.x;
   if (args.mask && args.mask[row] == 0) {
-    if (threadIdx.x == 0) {
-      args.logprob[row] = 0.f;
-      if (args.entropy) args.entropy[row] = 0.f;
-    }
+    for (int k = threadIdx.x; k < args.K; k += NT) args.logprob[row * args.K + k] = 0.f;
+    if (threadIdx.x == 0 && args.entropy) args.entropy[row] = 0.f;
     return;
   }
   const char* rowp = static_cast<const char*>(args.x) + row * args.ld * Tr::kBytes;
@@ -74,17 +72,17 @@ __global__ void __launch_bounds__(NT) k_logprobs_entropy(RowArgs args) {
   // the branch is uniform.
   if (__builtin_isnan(st.a) && !__builtin_isnan(st.s))
     st = stat_block_allreduce<NT>(scan_row<Tr, NT, U, true>(rowp, sp, c), sm);
-  if (threadIdx.x == 0) {
-    const float l2s = log2f(st.s);
-    const int64_t y = args.targets[row];
+  const float l2s = log2f(st.s);
+  for (int k = threadIdx.x; k < args.K; k += NT) {
+    const int64_t y = args.targets[row * args.K + k];
     float lp = __builtin_nanf("");
     if (y >= 0 && y < V) {
       const float ty = fmaf(Tr::load1(rowp, y), c, -st.mc);
       lp = (ty - l2s) * kLn2;
     }
-    args.logprob[row] = lp;
-    if (args.entropy) args.entropy[row] = (l2s - st.a / st.s) * kLn2;
+    args.logprob[row * args.K + k] = lp;
   }
+  if (threadIdx.x == 0 && args.entropy) args.entropy[row] = (l2s - st.a / st.s) * kLn2;
 }
 
 template <class Tr>
@@ -331,6 +329,139 @@ hipError_t launch_prob_diff(const float* a, const float* b, const uint8_t* mask,
   if (blocks > 4096) blocks = 4096;
   TimedLaunch tl("k_prob_diff", s);
   hipLaunchKernelGGL(k_prob_diff, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a, b, mask, n, out);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// aggregates of the masked prob diff (two deterministic passes, fp64)
+// ---------------------------------------------------------------------------
+// Each thread sums its strided positions shifted by the first value it kept
+// (so a lone or constant series has exactly zero spread), turns the sums into
+// (count, mean, centred second moments), and the partials are combined with
+// the pairwise update for means and co-moments (Chan, Golub and LeVeque) in a
+// fixed order: the result is the same on every call.
+
+constexpr int kStatsBlocks = 512;
+constexpr int kStatsFields = 9;
+
+size_t prob_diff_stats_workspace_bytes() { return sizeof(double) * kStatsBlocks * kStatsFields; }
+
+// n, mean d, M2 d, max d, mean pa, mean pb, M2 pa, M2 pb, co-moment pa pb
+struct Moments {
+  double n, md, m2d, mx, ma, mb, m2a, m2b, cab;
+};
+
+__device__ inline Moments moments_merge(const Moments& x, const Moments& y) {
+  if (y.n == 0.0) return x;
+  if (x.n == 0.0) return y;
+  Moments r;
+  r.n = x.n + y.n;
+  const double f = y.n / r.n, w = x.n * y.n / r.n;
+  const double dd = y.md - x.md, da = y.ma - x.ma, db = y.mb - x.mb;
+  r.md = x.md + dd * f;
+  r.ma = x.ma + da * f;
+  r.mb = x.mb + db * f;
+  r.m2d = x.m2d + y.m2d + dd * dd * w;
+  r.m2a = x.m2a + y.m2a + da * da * w;
+  r.m2b = x.m2b + y.m2b + db * db * w;
+  r.cab = x.cab + y.cab + da * db * w;
+  r.mx = x.mx > y.mx ? x.mx : y.mx;
+  return r;
+}
+
+__device__ inline void moments_store(double* p, const Moments& m) {
+  p[0] = m.n; p[1] = m.md; p[2] = m.m2d; p[3] = m.mx; p[4] = m.ma;
+  p[5] = m.mb; p[6] = m.m2a; p[7] = m.m2b; p[8] = m.cab;
+}
+
+__device__ inline Moments moments_load(const double* p) {
+  return Moments{p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7], p[8]};
+}
+
+__global__ void __launch_bounds__(256) k_prob_diff_stats_partial(const float* __restrict__ a,
+                                                                 const float* __restrict__ b,
+                                                                 const uint8_t* __restrict__ mask, int64_t n,
+                                                                 double* __restrict__ part) {
+  __shared__ double sm[256 * kStatsFields];
+  double cnt = 0, kd = 0, ka = 0, kb = 0, sd = 0, sdd = 0, sa = 0, saa = 0, sb = 0, sbb = 0, sab = 0, mx = 0;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
+    if (mask != nullptr && mask[i] == 0) continue;
+    const double pa = exp(static_cast<double>(a[i]));
+    const double pb = exp(static_cast<double>(b[i]));
+    const double d = fabs(pa - pb);
+    if (cnt == 0.0) {
+      kd = d;
+      ka = pa;
+      kb = pb;
+    }
+    cnt += 1.0;
+    const double xd = d - kd, xa = pa - ka, xb = pb - kb;
+    sd += xd;
+    sdd += xd * xd;
+    sa += xa;
+    saa += xa * xa;
+    sb += xb;
+    sbb += xb * xb;
+    sab += xa * xb;
+    mx = d > mx ? d : mx;
+  }
+  Moments m{0, 0, 0, 0, 0, 0, 0, 0, 0};
+  if (cnt > 0.0) {
+    m.n = cnt;
+    m.md = kd + sd / cnt;
+    m.ma = ka + sa / cnt;
+    m.mb = kb + sb / cnt;
+    m.m2d = fmax(sdd - sd * sd / cnt, 0.0);
+    m.m2a = fmax(saa - sa * sa / cnt, 0.0);
+    m.m2b = fmax(sbb - sb * sb / cnt, 0.0);
+    m.cab = sab - sa * sb / cnt;
+    m.mx = mx;
+  }
+  moments_store(sm + threadIdx.x * kStatsFields, m);
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (threadIdx.x < off) {
+      const Moments x = moments_load(sm + threadIdx.x * kStatsFields);
+      const Moments y = moments_load(sm + (threadIdx.x + off) * kStatsFields);
+      moments_store(sm + threadIdx.x * kStatsFields, moments_merge(x, y));
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x < kStatsFields) part[blockIdx.x * kStatsFields + threadIdx.x] = sm[threadIdx.x];
+}
+
+__global__ void __launch_bounds__(64) k_prob_diff_stats_final(const double* __restrict__ part, int nblocks,
+                                                              double* __restrict__ out) {
+  if (threadIdx.x != 0) return;
+  Moments m{0, 0, 0, 0, 0, 0, 0, 0, 0};
+  for (int bl = 0; bl < nblocks; ++bl) m = moments_merge(m, moments_load(part + bl * kStatsFields));
+  if (m.n == 0.0) {
+    out[0] = 0.0;
+    out[1] = 0.0;
+    out[2] = 0.0;
+    out[3] = 0.0;
+    out[4] = __builtin_nan("");
+    return;
+  }
+  out[0] = m.n;
+  out[1] = m.mx;
+  out[2] = m.md;
+  out[3] = sqrt(m.m2d / m.n);
+  out[4] = (m.m2a > 0.0 && m.m2b > 0.0) ? m.cab / sqrt(m.m2a * m.m2b) : __builtin_nan("");
+}
+
+hipError_t launch_prob_diff_stats(const float* a, const float* b, const uint8_t* mask, int64_t n, double* out,
+                                  void* ws, hipStream_t s) {
+  double* part = static_cast<double*>(ws);
+  {
+    TimedLaunch tl("k_prob_diff_stats", s);
+    hipLaunchKernelGGL(k_prob_diff_stats_partial, dim3(kStatsBlocks), dim3(256), 0, s, a, b, mask, n, part);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_prob_diff_stats_final, dim3(1), dim3(64), 0, s, static_cast<const double*>(part),
+                     kStatsBlocks, out);
   return hipGetLastError();
 }
 

@@ -173,6 +173,48 @@ lp_status lp_prob_diff(const float* lp_a, const float* lp_b, const uint8_t* mask
                        void* stream);
 
 /*
+ * K targets per row (miles PR #4645, "Scope": the fused log-prob op with K
+ * targets per row that score centering trains on).  Same as the single-target
+ * calls above with targets [T x K] (row-major, K contiguous), 1 <= K <= 64,
+ * and logprob [T x K]: logprob[t][k] = log softmax(z_t / temperature)[targets[t][k]].
+ * The backward's loss is sum over scored rows of
+ *   sum_k grad_logprob[t][k] * logprob[t][k] + grad_entropy[t] * entropy[t],
+ * with grad_logprob [T x K].  Workspace sizes are those of the K = 1 calls.
+ */
+lp_status lp_logprobs_entropy_k(const void* logits, lp_dtype dtype, int64_t T, int64_t V, int64_t ld,
+                                const int64_t* targets, int64_t K, const uint8_t* mask, float temperature,
+                                int64_t chunk_rows, float* logprob, float* entropy, void* stream);
+
+lp_status lp_lm_head_logprobs_entropy_k(const void* hidden, int64_t ld_h, const void* weight, int64_t ld_w,
+                                        int64_t T, int64_t h, int64_t V, const int64_t* targets, int64_t K,
+                                        const uint8_t* mask, float temperature, int64_t tile_rows, float* logprob,
+                                        float* entropy, float* lse, void* workspace, size_t workspace_bytes,
+                                        void* stream);
+
+lp_status lp_lm_head_logprobs_entropy_backward_k(const void* hidden, int64_t ld_h, const void* weight,
+                                                 int64_t ld_w, int64_t T, int64_t h, int64_t V,
+                                                 const int64_t* targets, int64_t K, const uint8_t* mask,
+                                                 float temperature, int64_t tile_rows, const float* lse,
+                                                 const float* entropy, const float* grad_logprob,
+                                                 const float* grad_entropy, float* grad_hidden, float* grad_weight,
+                                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Aggregates of the masked prob diff, the macro statistics the msprobe page
+ * lists next to its per-token diff (§4.1): over positions with mask != 0
+ * (mask NULL = all), with pa = exp(lp_a), pb = exp(lp_b), d = |pa - pb|:
+ *   out[0] = count, out[1] = max d, out[2] = mean d, out[3] = std d
+ *   (population), out[4] = Pearson correlation of pa and pb.
+ * Sums are fp64 and reduced in a fixed order (bitwise reproducible).  With
+ * count 0 every output is 0 except out[4] = NaN, which is also NaN when
+ * either series has zero variance.  out: device double[5], 8-byte aligned.
+ * workspace: >= lp_prob_diff_stats_workspace_bytes() bytes, 256-byte aligned.
+ */
+size_t lp_prob_diff_stats_workspace_bytes(void);
+lp_status lp_prob_diff_stats(const float* lp_a, const float* lp_b, const uint8_t* mask, int64_t n, double* out,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Per-kernel timing (observability; not part of the method).  While enabled,
  * each library launch is bracketed by two HIP events recorded on its own
  * stream.  lp_timing_enable(1) clears earlier records and starts recording,

@@ -327,3 +327,118 @@ def kl_and_prob_diff(student, teacher, targets, diff_mask):
     lpu = target_logprobs(student, targets)
     lpv = target_logprobs(teacher, targets)
     return kl, lpu, lpv, prob_diff(lpu, lpv, diff_mask)
+
+
+# ---------------------------------------------------------------------------
+# aggregates of the prob diff (msprobe page §4.1: max / mean / std of the
+# masked diff and the Pearson correlation of the two probability series)
+# ---------------------------------------------------------------------------
+
+def prob_diff_stats(lp_a, lp_b, mask):
+    """(count, max, mean, std, pearson) over positions with mask != 0.
+
+    diff = |exp(lp_a) - exp(lp_b)|; std is the population std (ddof 0, as
+    numpy's default in the page's offline example); pearson is the
+    correlation of exp(lp_a) and exp(lp_b).  Reading: with no masked
+    position every statistic is 0 except pearson, which is NaN, as it is
+    when either series has zero variance.
+    """
+    a = np.asarray(lp_a, dtype=np.float64).ravel()
+    b = np.asarray(lp_b, dtype=np.float64).ravel()
+    keep = np.ones(a.shape, bool) if mask is None else (np.asarray(mask).ravel() != 0)
+    pa, pb = np.exp(a[keep]), np.exp(b[keep])
+    n = int(keep.sum())
+    if n == 0:
+        return 0, 0.0, 0.0, 0.0, float("nan")
+    d = np.abs(pa - pb)
+    sa, sb = pa.std(), pb.std()
+    if sa == 0.0 or sb == 0.0:
+        r = float("nan")
+    else:
+        r = float(np.mean((pa - pa.mean()) * (pb - pb.mean())) / (sa * sb))
+    return n, float(d.max()), float(d.mean()), float(d.std()), r
+
+
+# ---------------------------------------------------------------------------
+# K targets per row (miles PR #4645, "Scope": the fused log-prob op with K
+# targets per row that score centering trains on)
+# ---------------------------------------------------------------------------
+
+def logprobs_entropy_k(logits, targets_k, mask, temperature: float):
+    """log softmax(z / tau) at each of K targets per row: (logprob[T, K], entropy[T], lse[T])."""
+    z = np.atleast_2d(np.asarray(logits, dtype=np.float64))
+    T = z.shape[0]
+    y = np.asarray(targets_k, dtype=np.int64).reshape(T, -1)
+    K = y.shape[1]
+    keep = _scored(mask, T)
+    lp = np.zeros((T, K))
+    H = np.zeros(T)
+    lse = np.zeros(T)
+    rows = np.nonzero(keep)[0]
+    if rows.size == 0:
+        return lp, H, lse
+    zt = tempered(z[rows], temperature)
+    norm = log_normaliser(zt)
+    logp = zt - norm[:, None]
+    for k in range(K):
+        lp[rows, k] = _gather_targets(logp, y[rows, k])
+    H[rows] = shannon_entropy(logp)
+    lse[rows] = norm
+    return lp, H, lse
+
+
+def lm_head_logprobs_entropy_k(hidden, weight, targets_k, mask, temperature: float):
+    hidden = np.atleast_2d(np.asarray(hidden, dtype=np.float64))
+    T = hidden.shape[0]
+    y = np.asarray(targets_k, dtype=np.int64).reshape(T, -1)
+    keep = _scored(mask, T)
+    rows = np.nonzero(keep)[0]
+    lp = np.zeros((T, y.shape[1]))
+    H = np.zeros(T)
+    lse = np.zeros(T)
+    if rows.size == 0:
+        return lp, H, lse
+    Z = lm_head_logits(hidden[rows], weight)
+    sub = logprobs_entropy_k(Z, y[rows], None, temperature)
+    lp[rows], H[rows], lse[rows] = sub
+    return lp, H, lse
+
+
+def lm_head_loss_k(hidden, weight, targets_k, mask, temperature, grad_logprob_k, grad_entropy) -> float:
+    """sum over scored rows of sum_k g_lp[t, k] lp[t, k] + g_H[t] H[t]."""
+    lp, H, _ = lm_head_logprobs_entropy_k(hidden, weight, targets_k, mask, temperature)
+    T = lp.shape[0]
+    keep = _scored(mask, T)
+    g = np.asarray(grad_logprob_k, dtype=np.float64).reshape(lp.shape)
+    gH = np.zeros(T) if grad_entropy is None else np.asarray(grad_entropy, dtype=np.float64).reshape(T)
+    return float(np.sum(np.where(keep, (g * lp).sum(axis=1) + gH * H, 0.0)))
+
+
+def lm_head_backward_k(hidden, weight, targets_k, mask, temperature, grad_logprob_k, grad_entropy):
+    """(dHidden, dWeight) of `lm_head_loss_k`: with zt = Z / tau and logp = log_softmax(zt),
+      d lp_tk / d zt_tj = [j == y_tk] - p_tj,   d H_t / d zt_tj = -p_tj (logp_tj + H_t),
+    summed with the weights g_lp[t, k] and g_H[t], then dZ = dzt / tau."""
+    hidden = np.atleast_2d(np.asarray(hidden, dtype=np.float64))
+    T, h = hidden.shape
+    W = np.asarray(weight, dtype=np.float64)
+    y = np.asarray(targets_k, dtype=np.int64).reshape(T, -1)
+    g = np.asarray(grad_logprob_k, dtype=np.float64).reshape(y.shape)
+    gH = np.zeros(T) if grad_entropy is None else np.asarray(grad_entropy, dtype=np.float64).reshape(T)
+    rows = np.nonzero(_scored(mask, T))[0]
+    dH = np.zeros((T, h))
+    dW = np.zeros(W.shape)
+    if rows.size == 0:
+        return dH, dW
+    zt = tempered(lm_head_logits(hidden[rows], W), temperature)
+    logp = log_softmax(zt)
+    p = np.exp(logp)
+    Hrow = shannon_entropy(logp)
+    dzt = -g[rows].sum(axis=1)[:, None] * p
+    for k in range(y.shape[1]):
+        np.add.at(dzt, (np.arange(rows.size), y[rows, k]), g[rows, k])
+    with np.errstate(invalid="ignore"):
+        dzt -= gH[rows][:, None] * np.where(p > 0.0, p * (logp + Hrow[:, None]), 0.0)
+    dZ = dzt * ((1.0 / temperature) if temperature_applies(temperature) else 1.0)
+    dH[rows] = dZ @ W
+    dW = dZ.T @ hidden[rows]
+    return dH, dW

@@ -506,3 +506,80 @@ def test_mutation_kl_direction(monkeypatch):
     orig = O.kl_full_vocab
     monkeypatch.setattr(O, "kl_full_vocab", lambda u, v: orig(v, u))
     _must_fail(pin_kl_two_class)
+
+
+# ---------------------------------------------------------------------------
+# pins: prob-diff aggregates and K targets per row
+# ---------------------------------------------------------------------------
+
+def test_prob_diff_stats_hand_values():
+    pa = np.array([0.5, 0.25, 1.0, 0.125, 0.75])
+    pb = np.array([0.25, 0.25, 0.5, 0.5, 0.75])
+    m = np.array([1, 1, 1, 0, 1])
+    n, mx, mean, std, r = O.prob_diff_stats(np.log(pa), np.log(pb), m)
+    d = [0.25, 0.0, 0.5, 0.0]
+    mu = sum(d) / 4
+    assert n == 4 and abs(mx - 0.5) < 1e-15 and abs(mean - mu) < 1e-15
+    assert abs(std - math.sqrt(sum((x - mu) ** 2 for x in d) / 4)) < 1e-15
+    xa, xb = [0.5, 0.25, 1.0, 0.75], [0.25, 0.25, 0.5, 0.75]
+    ma, mb = sum(xa) / 4, sum(xb) / 4
+    cov = sum((u - ma) * (v - mb) for u, v in zip(xa, xb))
+    va = sum((u - ma) ** 2 for u in xa)
+    vb = sum((v - mb) ** 2 for v in xb)
+    assert abs(r - cov / math.sqrt(va * vb)) < 1e-14
+
+
+def test_prob_diff_stats_special_cases():
+    rng = np.random.default_rng(30)
+    p = rng.uniform(0.01, 0.5, size=100)
+    # a linear relation has correlation exactly 1 (up to rounding); identical series give zero diff
+    n, mx, mean, std, r = O.prob_diff_stats(np.log(p), np.log(0.5 * p + 0.1), None)
+    assert n == 100 and abs(r - 1.0) < 1e-12
+    n, mx, mean, std, r = O.prob_diff_stats(np.log(p), np.log(p), None)
+    assert mx == 0 and mean == 0 and std == 0 and abs(r - 1.0) < 1e-12
+    # all-False mask: nothing to aggregate
+    n, mx, mean, std, r = O.prob_diff_stats(np.log(p), np.log(p), np.zeros(100))
+    assert n == 0 and mx == 0 and mean == 0 and std == 0 and math.isnan(r)
+
+
+def test_k_targets_match_single_target_calls():
+    rng = np.random.default_rng(31)
+    z = rng.normal(0, 3, size=(7, 41))
+    yk = rng.integers(0, 41, size=(7, 5))
+    m = np.array([1, 1, 0, 1, 1, 0, 1])
+    lpk, Hk, lsek = O.logprobs_entropy_k(z, yk, m, 0.7)
+    for k in range(5):
+        for t in range(7):
+            if m[t]:
+                lp_ref, H_ref = bf_row(z[t], int(yk[t, k]), 0.7)
+                assert abs(lpk[t, k] - lp_ref) < 1e-12 and abs(Hk[t] - H_ref) < 1e-12
+            else:
+                assert lpk[t, k] == 0 and Hk[t] == 0
+
+
+def test_k_target_backward_finite_differences():
+    rng = np.random.default_rng(32)
+    T, h, V, K = 3, 4, 5, 3
+    Hm = rng.normal(size=(T, h))
+    Wm = rng.normal(0, 0.7, size=(V, h))
+    yk = rng.integers(0, V, size=(T, K))
+    yk[0, 1] = yk[0, 0]  # a repeated target counts twice
+    mask = np.array([1, 0, 1])
+    g = rng.normal(size=(T, K))
+    gH = rng.normal(0, 0.5, size=T)
+    dH, dW = O.lm_head_backward_k(Hm, Wm, yk, mask, 0.7, g, gH)
+    eps = 1e-5
+    for (arr, grad) in ((Hm, dH), (Wm, dW)):
+        for idx in np.ndindex(arr.shape):
+            P, N = arr.copy(), arr.copy()
+            P[idx] += eps
+            N[idx] -= eps
+            args_p = (P, Wm) if arr is Hm else (Hm, P)
+            args_n = (N, Wm) if arr is Hm else (Hm, N)
+            fd = (O.lm_head_loss_k(*args_p, yk, mask, 0.7, g, gH) - O.lm_head_loss_k(*args_n, yk, mask, 0.7, g, gH)) \
+                / (2 * eps)
+            assert abs(fd - grad[idx]) <= 1e-6 * max(1.0, abs(fd)), (idx, fd, grad[idx])
+    # K = 1 reduces to the single-target backward
+    d1 = O.lm_head_backward_k(Hm, Wm, yk[:, :1], mask, 0.7, g[:, :1], gH)
+    d0 = O.lm_head_backward(Hm, Wm, yk[:, 0], mask, 0.7, g[:, 0], gH)
+    assert np.allclose(d1[0], d0[0], atol=1e-14) and np.allclose(d1[1], d0[1], atol=1e-14)
