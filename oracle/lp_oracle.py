@@ -28,7 +28,13 @@ same numbers up to rounding order, so the definition *is* the oracle:
   DeepSeek-V4 book ch.19 "RL / OPD 工程", 名词速通 "不实例化 logits" and
   "TileLang KL Kernel".
 * masked |exp(lp_a) - exp(lp_b)|: msprobe page §3.2
-  (`calculate_token_level_prob_diff`) and its edge-case table.
+  (`calculate_token_level_prob_diff`) and its edge-case table; its
+  aggregates (max / mean / std / Pearson): same page §4.1.
+* K target ids per row: miles PR #4645 "Scope" (the fused op with K targets
+  per row that score centering trains on).
+* KL with each model's logits rebuilt from its cached last hidden state
+  through its own output head: DeepSeek-V4 book ch.19, 名词速通
+  "不实例化 logits" and §2 "Teacher Scheduling".
 
 Readings taken where the pages are silent are listed in the design doc; the main
 ones are repeated next to the code that takes them.
@@ -441,4 +447,72 @@ def lm_head_backward_k(hidden, weight, targets_k, mask, temperature, grad_logpro
     dZ = dzt * ((1.0 / temperature) if temperature_applies(temperature) else 1.0)
     dH[rows] = dZ @ W
     dW = dZ.T @ hidden[rows]
+    return dH, dW
+
+
+# ---------------------------------------------------------------------------
+# KL rebuilt from cached hidden states through each model's output head
+# (DeepSeek-V4 book ch.19 "RL / OPD 工程": 名词速通 "不实例化 logits" and
+# §2 "Teacher Scheduling": only the last hidden state is kept and the logits
+# are rebuilt through the matching prediction head when the KL is computed)
+# ---------------------------------------------------------------------------
+
+def lm_head_kl(hidden_s, weight_s, hidden_t, weight_t, mask, targets, diff_mask):
+    """KL(teacher || student) of the rows' logits hidden @ W^T of each model.
+
+    Returns (kl, lp_student, lp_teacher, diff, lse_student, lse_teacher), each
+    [T]; rows with mask == 0 are 0 everywhere.  No temperature, as for the KL
+    on given logits.  targets None: lp_*, diff are all 0.  diff is
+    |exp(lp_student) - exp(lp_teacher)| on scored rows whose diff_mask is set.
+    """
+    hs = np.atleast_2d(np.asarray(hidden_s, dtype=np.float64))
+    ht = np.atleast_2d(np.asarray(hidden_t, dtype=np.float64))
+    T = hs.shape[0]
+    out = [np.zeros(T) for _ in range(6)]
+    rows = np.nonzero(_scored(mask, T))[0]
+    if rows.size == 0:
+        return tuple(out)
+    u = lm_head_logits(hs[rows], weight_s)
+    v = lm_head_logits(ht[rows], weight_t)
+    out[0][rows] = kl_full_vocab(u, v)
+    out[4][rows] = log_normaliser(u)
+    out[5][rows] = log_normaliser(v)
+    if targets is not None:
+        y = np.asarray(targets, dtype=np.int64).reshape(T)[rows]
+        out[1][rows] = target_logprobs(u, y)
+        out[2][rows] = target_logprobs(v, y)
+        dm = None if diff_mask is None else np.asarray(diff_mask).reshape(T)[rows]
+        out[3][rows] = prob_diff(out[1][rows], out[2][rows], dm)
+    return tuple(out)
+
+
+def lm_head_kl_loss(hidden_s, weight_s, hidden_t, weight_t, mask, grad_kl) -> float:
+    """sum over scored rows of g_t KL_t (the scalar the KL backward differentiates)."""
+    kl = lm_head_kl(hidden_s, weight_s, hidden_t, weight_t, mask, None, None)[0]
+    return float(np.dot(np.asarray(grad_kl, dtype=np.float64).reshape(kl.shape), kl))
+
+
+def lm_head_kl_backward(hidden_s, weight_s, hidden_t, weight_t, mask, grad_kl):
+    """(dHidden_student, dWeight_student) of `lm_head_kl_loss`.
+
+    KL_t = sum_j p_v (log p_v - log p_u) depends on the student logits u only
+    through -sum_j p_v log p_u = lse_u - sum_j p_v u_j, whose derivative in
+    u_j is p_u,j - p_v,j.  The teacher is not trained (its head is only
+    loaded to rebuild logits), so no teacher gradient is formed.
+    """
+    hs = np.atleast_2d(np.asarray(hidden_s, dtype=np.float64))
+    ht = np.atleast_2d(np.asarray(hidden_t, dtype=np.float64))
+    T, h = hs.shape
+    Ws = np.asarray(weight_s, dtype=np.float64)
+    g = np.asarray(grad_kl, dtype=np.float64).reshape(T)
+    dH = np.zeros((T, h))
+    dW = np.zeros(Ws.shape)
+    rows = np.nonzero(_scored(mask, T))[0]
+    if rows.size == 0:
+        return dH, dW
+    pu = np.exp(log_softmax(lm_head_logits(hs[rows], Ws)))
+    pv = np.exp(log_softmax(lm_head_logits(ht[rows], weight_t)))
+    dZ = g[rows][:, None] * (pu - pv)
+    dH[rows] = dZ @ Ws
+    dW = dZ.T @ hs[rows]
     return dH, dW

@@ -583,3 +583,94 @@ def test_k_target_backward_finite_differences():
     d1 = O.lm_head_backward_k(Hm, Wm, yk[:, :1], mask, 0.7, g[:, :1], gH)
     d0 = O.lm_head_backward(Hm, Wm, yk[:, 0], mask, 0.7, g[:, 0], gH)
     assert np.allclose(d1[0], d0[0], atol=1e-14) and np.allclose(d1[1], d0[1], atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# pins: KL rebuilt through each model's output head
+# ---------------------------------------------------------------------------
+
+def _kl_heads(seed, T=4, hs=3, ht=5, V=6):
+    rng = np.random.default_rng(seed)
+    Hs = rng.normal(size=(T, hs))
+    Ws = rng.normal(0, 0.8, size=(V, hs))
+    Ht = rng.normal(size=(T, ht))
+    Wt = rng.normal(0, 0.8, size=(V, ht))
+    return Hs, Ws, Ht, Wt
+
+
+def pin_lm_head_kl_brute_force():
+    Hs, Ws, Ht, Wt = _kl_heads(40)
+    T, V = Hs.shape[0], Ws.shape[0]
+    y = np.array([2, 0, 5, 3])
+    mask = np.array([1, 1, 0, 1])
+    dmask = np.array([1, 0, 1, 1])
+    kl, lpu, lpv, diff, lseu, lsev = O.lm_head_kl(Hs, Ws, Ht, Wt, mask, y, dmask)
+    U = bf_matmul_T(Hs.tolist(), Ws.tolist())
+    Vt = bf_matmul_T(Ht.tolist(), Wt.tolist())
+    for t in range(T):
+        if not mask[t]:
+            assert kl[t] == lpu[t] == lpv[t] == diff[t] == lseu[t] == lsev[t] == 0
+            continue
+        assert abs(kl[t] - bf_kl(U[t], Vt[t])) < 1e-12
+        a, _ = bf_row(U[t], int(y[t]), 1.0)
+        b, _ = bf_row(Vt[t], int(y[t]), 1.0)
+        assert abs(lpu[t] - a) < 1e-12 and abs(lpv[t] - b) < 1e-12
+        want = abs(math.exp(a) - math.exp(b)) if dmask[t] else 0.0
+        assert abs(diff[t] - want) < 1e-12
+        assert abs(lseu[t] - math.log(math.fsum(math.exp(x) for x in U[t]))) < 1e-12
+        assert abs(lsev[t] - math.log(math.fsum(math.exp(x) for x in Vt[t]))) < 1e-12
+
+
+def test_lm_head_kl_brute_force():
+    pin_lm_head_kl_brute_force()
+
+
+def test_lm_head_kl_same_model_is_zero():
+    Hs, Ws, _, _ = _kl_heads(41)
+    kl = O.lm_head_kl(Hs, Ws, Hs, Ws, None, None, None)[0]
+    assert np.all(kl == 0.0)
+    dH, dW = O.lm_head_kl_backward(Hs, Ws, Hs, Ws, None, np.ones(Hs.shape[0]))
+    assert not dH.any() and not dW.any()
+
+
+def pin_lm_head_kl_backward_finite_differences():
+    Hs, Ws, Ht, Wt = _kl_heads(42, T=3, hs=4, ht=2, V=5)
+    mask = np.array([1, 0, 1])
+    g = np.array([0.7, -1.3, 1.9])
+    dH, dW = O.lm_head_kl_backward(Hs, Ws, Ht, Wt, mask, g)
+    eps = 1e-5
+    for arr, grad in ((Hs, dH), (Ws, dW)):
+        for idx in np.ndindex(arr.shape):
+            P, N = arr.copy(), arr.copy()
+            P[idx] += eps
+            N[idx] -= eps
+            ap = (P, Ws) if arr is Hs else (Hs, P)
+            an = (N, Ws) if arr is Hs else (Hs, N)
+            fd = (O.lm_head_kl_loss(*ap, Ht, Wt, mask, g) - O.lm_head_kl_loss(*an, Ht, Wt, mask, g)) / (2 * eps)
+            assert abs(fd - grad[idx]) <= 1e-6 * max(1.0, abs(fd)), (idx, fd, grad[idx])
+
+
+def test_lm_head_kl_backward_finite_differences():
+    pin_lm_head_kl_backward_finite_differences()
+
+
+def test_lm_head_kl_backward_vocab_sum_is_zero():
+    # each row of dL/du sums to 0 (sum p_u - sum p_v), so dW summed over the vocab vanishes
+    Hs, Ws, Ht, Wt = _kl_heads(43, T=6, hs=8, ht=8, V=40)
+    _, dW = O.lm_head_kl_backward(Hs, Ws, Ht, Wt, None, np.linspace(-1, 2, 6))
+    assert np.abs(dW.sum(axis=0)).max() < 1e-13
+
+
+def test_mutation_lm_head_kl_models_swapped(monkeypatch):
+    orig = O.lm_head_kl
+    monkeypatch.setattr(O, "lm_head_kl", lambda hs, ws, ht, wt, m, y, d: orig(ht, wt, hs, ws, m, y, d))
+    _must_fail(pin_lm_head_kl_brute_force)
+
+
+def test_mutation_lm_head_kl_gradient_sign(monkeypatch):
+    orig = O.lm_head_kl_backward
+    def bad(*a):
+        dH, dW = orig(*a)
+        return -dH, -dW
+    monkeypatch.setattr(O, "lm_head_kl_backward", bad)
+    _must_fail(pin_lm_head_kl_backward_finite_differences)
