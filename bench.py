@@ -29,7 +29,7 @@ sys.path.insert(0, ROOT)
 METRIC = "scored tokens/s, fused LM-head logprob+entropy; % of MFMA / HBM peak"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
-ALL_PATHS = ("lm_head_fwd", "logits_input", "kl_prob_diff", "lm_head_fwd_bwd")
+ALL_PATHS = ("lm_head_fwd", "logits_input", "kl_prob_diff", "lm_head_fwd_bwd", "kl_lm_head")
 
 
 def to_dev_bits(bits, dtype):
@@ -300,6 +300,63 @@ def bench_lm_head_fwd_bwd(lp, torch, np, synth, O, steps, warmup):
     return res
 
 
+def bench_kl_lm_head(lp, torch, np, synth, O, steps, warmup):
+    """KL(teacher || student) rebuilt through both heads: forward timed over
+    `steps`, forward + student backward over max(1, steps // 5)."""
+    cfg = synth.KLHeads(grads=True).build()
+    A = cfg.arrays
+    heads = [to_dev_bits(A[k], "bf16") for k in ("student_hidden", "student_weight", "teacher_hidden",
+                                                  "teacher_weight")]
+    y, dm, g = to_dev(A["targets"]), to_dev(A["diff_mask"]), to_dev(A["grad_kl"])
+    wsf = torch.empty(lp.lp_lm_head_kl_workspace_bytes(cfg.T, cfg.h, cfg.V, cfg.tile_rows, False),
+                      dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(lp.lp_lm_head_kl_workspace_bytes(cfg.T, cfg.h, cfg.V, cfg.tile_rows, True),
+                      dtype=torch.uint8, device="cuda")
+    out = {}
+
+    def fwd():
+        out["f"] = lp.lp_lm_head_kl(*heads, None, y, dm, cfg.tile_rows, workspace=wsf)
+
+    def fwd_bwd():
+        fwd()
+        out["g"] = lp.lp_lm_head_kl_backward(*heads, None, cfg.tile_rows, out["f"][4], out["f"][5], g,
+                                             workspace=wsb)
+
+    ms, kt = _timed(lp, torch, fwd, steps, warmup, ["k_kl_tile", "k_kl_merge"])
+    n_launch, kms = kt["k_kl_tile"]
+    flop_fwd = 2.0 * cfg.T * cfg.V * (cfg.h + cfg.h)
+    achieved = flop_fwd * steps / (kms * 1e-3) / 1e12
+    bsteps = max(1, steps // 5)
+    bkernels = ["k_kl_tile", "k_kl_dz", "k_out_gemm_dhidden", "k_out_gemm_dweight", "k_transpose_bf16"]
+    ms_b, kt_b = _timed(lp, torch, fwd_bwd, bsteps, min(1, warmup), bkernels)
+    flop_fb = flop_fwd * 2 + 4.0 * cfg.T * cfg.V * cfg.h
+    mfma_ms = sum(kt_b[k][1] for k in bkernels[:4])
+    achieved_b = flop_fb * bsteps / (mfma_ms * 1e-3) / 1e12
+    kl = out["f"][0].cpu().numpy()
+    rows = np.array([0, cfg.T // 2, cfg.T - 1])
+    kl_o = O.lm_head_kl(O.widen_bf16(A["student_hidden"][rows]), _LazyWeight(O, A["student_weight"]),
+                        O.widen_bf16(A["teacher_hidden"][rows]), _LazyWeight(O, A["teacher_weight"]), None,
+                        None, None)[0]
+    res = dict(
+        workload=f"KL(teacher||student) with logits rebuilt through both heads: T={cfg.T} rows, "
+                 f"h_student=h_teacher={cfg.h}, V={cfg.V}, bf16, tile {cfg.tile_rows}, + target lps and prob diff",
+        ms_per_step=ms / steps, tokens_per_s=cfg.T * steps / (ms * 1e-3),
+        roofline=dict(bound="mfma", kernel="k_kl_tile", achieved=achieved, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                      frac=achieved / BF16_PEAK_TFLOPS, traffic=measured_traffic("k_kl_tile"),
+                      traffic_unit="HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                      launches_per_step=n_launch / steps, algorithmic_flop_per_step=flop_fwd,
+                      algorithmic_flop_per_launch=flop_fwd / (n_launch / steps)),
+        fwd_bwd=dict(ms_per_step=ms_b / bsteps, tokens_per_s=cfg.T * bsteps / (ms_b * 1e-3),
+                     roofline=dict(bound="mfma", kernel="all MFMA GEMMs (2 fwd + 2 recompute + dHidden + dW)",
+                                   achieved=achieved_b, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                                   frac=achieved_b / BF16_PEAK_TFLOPS, algorithmic_flop_per_step=flop_fb),
+                     kernel_ms_per_step={k: v[1] / bsteps for k, v in kt_b.items()}),
+        parity_max_abs_err_sampled=float(np.abs(kl[rows] - kl_o).max()), parity_tol=2e-3)
+    del heads, y, dm, g, wsf, wsb, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -347,6 +404,8 @@ def main():
             results[p] = bench_logits_input(lp, torch, np, synth, O, args.steps, args.warmup)
         elif p == "kl_prob_diff":
             results[p] = bench_kl(lp, torch, np, synth, O, args.steps, args.warmup)
+        elif p == "kl_lm_head":
+            results[p] = bench_kl_lm_head(lp, torch, np, synth, O, args.steps, args.warmup)
         elif p == "lm_head_fwd_bwd":
             results[p] = bench_lm_head_fwd_bwd(lp, torch, np, synth, O, max(1, args.steps // 5),
                                                min(1, args.warmup))

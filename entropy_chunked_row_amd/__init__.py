@@ -18,7 +18,8 @@ __all__ = [
     "lp_logprobs_entropy", "lp_lm_head_logprobs_entropy", "lp_lm_head_logprobs_entropy_backward",
     "lp_lm_head_workspace_bytes", "lp_kl_full_vocab", "lp_prob_diff", "lp_version", "lp_timing_enable",
     "lp_timing_read", "lp_logprobs_entropy_k", "lp_lm_head_logprobs_entropy_k",
-    "lp_lm_head_logprobs_entropy_backward_k", "lp_prob_diff_stats", "LPError", "load",
+    "lp_lm_head_logprobs_entropy_backward_k", "lp_prob_diff_stats", "lp_lm_head_kl_workspace_bytes",
+    "lp_lm_head_kl", "lp_lm_head_kl_backward", "LPError", "load",
 ]
 
 
@@ -319,3 +320,74 @@ def lp_prob_diff_stats(lp_a, lp_b, mask=None, *, stream=None):
                                 _stream(stream))
     check("lp_prob_diff_stats", st)
     return out
+
+
+def lp_lm_head_kl_workspace_bytes(T: int, h_student: int, V: int, tile_rows: int, backward: bool) -> int:
+    return int(load().lp_lm_head_kl_workspace_bytes(T, h_student, V, tile_rows, 1 if backward else 0))
+
+
+def _heads(student_hidden, student_weight, teacher_hidden, teacher_weight):
+    torch = _torch()
+    for t, n in ((student_hidden, "student_hidden"), (student_weight, "student_weight"),
+                 (teacher_hidden, "teacher_hidden"), (teacher_weight, "teacher_weight")):
+        _dev(t, n)
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{n} must be bfloat16")
+    T, hs = student_hidden.shape
+    V, hs2 = student_weight.shape
+    T2, ht = teacher_hidden.shape
+    V2, ht2 = teacher_weight.shape
+    if hs2 != hs or ht2 != ht or T2 != T or V2 != V:
+        raise ValueError("student / teacher hidden and weight shapes disagree")
+    return (T, V, hs, ht,
+            [_ptr(student_hidden), _rows(student_hidden, "student_hidden"), _ptr(student_weight),
+             _rows(student_weight, "student_weight"), hs, _ptr(teacher_hidden), _rows(teacher_hidden, "teacher_hidden"),
+             _ptr(teacher_weight), _rows(teacher_weight, "teacher_weight"), ht])
+
+
+def lp_lm_head_kl(student_hidden, student_weight, teacher_hidden, teacher_weight, mask=None, targets=None,
+                  diff_mask=None, tile_rows: int = 4096, *, want_lse: bool = True, workspace=None, stream=None):
+    """(kl, lp_student, lp_teacher, prob_diff, lse_student, lse_teacher) of the logits hidden @ W^T of each
+    model (bf16 hiddens [T, h_*], weights [V, h_*]); the target outputs are None without targets."""
+    torch = _torch()
+    lib = load()
+    T, V, hs, ht, head_args = _heads(student_hidden, student_weight, teacher_hidden, teacher_weight)
+    mask = _vec(mask, "mask", torch.uint8)
+    targets = _vec(targets, "targets", torch.int64)
+    diff_mask = _vec(diff_mask, "diff_mask", torch.uint8)
+    dev = student_hidden.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    kl = torch.empty(T, **f32)
+    lps = lpt = diff = None
+    if targets is not None:
+        lps, lpt, diff = torch.empty(T, **f32), torch.empty(T, **f32), torch.empty(T, **f32)
+    lseu = torch.empty(T, **f32) if want_lse else None
+    lsev = torch.empty(T, **f32) if want_lse else None
+    ws = _workspace(lp_lm_head_kl_workspace_bytes(T, hs, V, tile_rows, False), dev, workspace)
+    st = lib.lp_lm_head_kl(*head_args, T, V, _ptr(mask), _ptr(targets), _ptr(diff_mask), int(tile_rows), _ptr(kl),
+                           _ptr(lps), _ptr(lpt), _ptr(diff), _ptr(lseu), _ptr(lsev), _ptr(ws), ws.numel(),
+                           _stream(stream))
+    check("lp_lm_head_kl", st)
+    return kl, lps, lpt, diff, lseu, lsev
+
+
+def lp_lm_head_kl_backward(student_hidden, student_weight, teacher_hidden, teacher_weight, mask, tile_rows: int,
+                           lse_student, lse_teacher, grad_kl, *, need_grad_hidden: bool = True,
+                           need_grad_weight: bool = True, workspace=None, stream=None) -> Tuple:
+    """(grad_hidden fp32 [T, h_student] or None, grad_weight fp32 [V, h_student] or None) of sum_t g_t KL_t."""
+    torch = _torch()
+    lib = load()
+    T, V, hs, ht, head_args = _heads(student_hidden, student_weight, teacher_hidden, teacher_weight)
+    mask = _vec(mask, "mask", torch.uint8)
+    lse_student = _vec(lse_student, "lse_student", torch.float32)
+    lse_teacher = _vec(lse_teacher, "lse_teacher", torch.float32)
+    grad_kl = _vec(grad_kl, "grad_kl", torch.float32)
+    dev = student_hidden.device
+    dH = torch.empty((T, hs), dtype=torch.float32, device=dev) if need_grad_hidden else None
+    dW = torch.empty((V, hs), dtype=torch.float32, device=dev) if need_grad_weight else None
+    ws = _workspace(lp_lm_head_kl_workspace_bytes(T, hs, V, tile_rows, True), dev, workspace)
+    st = lib.lp_lm_head_kl_backward(*head_args, T, V, _ptr(mask), int(tile_rows), _ptr(lse_student),
+                                    _ptr(lse_teacher), _ptr(grad_kl), _ptr(dH), _ptr(dW), _ptr(ws), ws.numel(),
+                                    _stream(stream))
+    check("lp_lm_head_kl_backward", st)
+    return dH, dW

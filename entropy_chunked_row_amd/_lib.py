@@ -40,6 +40,13 @@ SIGNATURES = {
                                                        ctypes.c_size_t, c_vp]),
     "lp_prob_diff_stats_workspace_bytes": (ctypes.c_size_t, []),
     "lp_prob_diff_stats": (c_int, [c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, ctypes.c_size_t, c_vp]),
+    "lp_lm_head_kl_workspace_bytes": (ctypes.c_size_t, [c_i64, c_i64, c_i64, c_i64, c_int]),
+    "lp_lm_head_kl": (c_int, [c_vp, c_i64, c_vp, c_i64, c_i64, c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_i64,
+                              c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, ctypes.c_size_t,
+                              c_vp]),
+    "lp_lm_head_kl_backward": (c_int, [c_vp, c_i64, c_vp, c_i64, c_i64, c_vp, c_i64, c_vp, c_i64, c_i64, c_i64,
+                                       c_i64, c_vp, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, ctypes.c_size_t,
+                                       c_vp]),
     "lp_timing_enable": (None, [c_int]),
     "lp_timing_read": (c_int, [ctypes.c_char_p, ctypes.POINTER(c_i64), ctypes.POINTER(ctypes.c_double)]),
 }

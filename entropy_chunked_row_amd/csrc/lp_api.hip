@@ -260,6 +260,105 @@ lp_status lp_lm_head_logprobs_entropy_backward_k(const void* hidden, int64_t ld_
                                grad_weight, workspace, workspace_bytes, stream);
 }
 
+size_t lp_lm_head_kl_workspace_bytes(int64_t T, int64_t h_student, int64_t V, int64_t tile_rows, int backward) {
+  lp::LMHeadWorkspace w;
+  if (!lp::lmhead_workspace_layout(T, h_student, V, tile_rows, backward ? 1 : 2, &w)) return 0;
+  return w.total;
+}
+
+// Checks of one head's operands (T > 0).
+static lp_status check_head(const char* fn, const char* who, const void* hidden, int64_t ld_h, const void* weight,
+                            int64_t ld_w, int64_t h) {
+  if (h <= 0 || h > kMaxV) return fail(LP_ERR_INVALID_ARGUMENT, "%s: %s h must be in 1..2^30", fn, who);
+  if (ld_h < h || ld_w < h) return fail(LP_ERR_INVALID_ARGUMENT, "%s: %s ld_h and ld_w must be >= h", fn, who);
+  if (h % 8 || ld_h % 8 || ld_w % 8)
+    return fail(LP_ERR_UNSUPPORTED, "%s: %s h, ld_h and ld_w must be multiples of 8", fn, who);
+  if (!hidden || !weight) return fail(LP_ERR_INVALID_ARGUMENT, "%s: %s hidden and weight are required", fn, who);
+  if (!aligned(hidden, 16) || !aligned(weight, 16))
+    return fail(LP_ERR_UNSUPPORTED, "%s: %s hidden and weight must be 16-byte aligned", fn, who);
+  return LP_OK;
+}
+
+static lp_status check_kl_heads(const char* fn, const void* hs, int64_t ld_hs, const void* ws_, int64_t ld_ws,
+                                int64_t h_s, const void* ht, int64_t ld_ht, const void* wt, int64_t ld_wt,
+                                int64_t h_t, int64_t T, int64_t V, int64_t tile_rows, void* workspace,
+                                size_t workspace_bytes, int backward, lp::LMHeadWorkspace* w) {
+  if (T < 0) return fail(LP_ERR_INVALID_ARGUMENT, "%s: T < 0", fn);
+  if (V <= 0 || V > kMaxV) return fail(LP_ERR_INVALID_ARGUMENT, "%s: V must be in 1..2^30", fn);
+  if (h_s <= 0 || h_s > kMaxV || h_t <= 0 || h_t > kMaxV)
+    return fail(LP_ERR_INVALID_ARGUMENT, "%s: h_student and h_teacher must be in 1..2^30", fn);
+  if (tile_rows <= 0) return fail(LP_ERR_INVALID_ARGUMENT, "%s: tile_rows must be > 0", fn);
+  if (T == 0) return LP_OK;
+  lp_status st = check_head(fn, "student", hs, ld_hs, ws_, ld_ws, h_s);
+  if (st != LP_OK) return st;
+  if ((st = check_head(fn, "teacher", ht, ld_ht, wt, ld_wt, h_t)) != LP_OK) return st;
+  if (!lp::lmhead_workspace_layout(T, h_s, V, tile_rows, backward ? 1 : 2, w))
+    return fail(LP_ERR_INVALID_ARGUMENT, "%s: sizes overflow the workspace layout", fn);
+  if (!workspace || workspace_bytes < w->total)
+    return fail(LP_ERR_WORKSPACE_TOO_SMALL, "%s: workspace needs %zu bytes, got %zu", fn, w->total,
+                workspace ? workspace_bytes : size_t(0));
+  if (!aligned(workspace, 256)) return fail(LP_ERR_INVALID_ARGUMENT, "%s: workspace must be 256-byte aligned", fn);
+  return LP_OK;
+}
+
+lp_status lp_lm_head_kl(const void* student_hidden, int64_t ld_hs, const void* student_weight, int64_t ld_ws,
+                        int64_t h_student, const void* teacher_hidden, int64_t ld_ht, const void* teacher_weight,
+                        int64_t ld_wt, int64_t h_teacher, int64_t T, int64_t V, const uint8_t* mask,
+                        const int64_t* targets, const uint8_t* diff_mask, int64_t tile_rows, float* kl,
+                        float* lp_student, float* lp_teacher, float* prob_diff, float* lse_student,
+                        float* lse_teacher, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "lp_lm_head_kl";
+  lp::LMHeadWorkspace w;
+  lp_status st = check_kl_heads(fn, student_hidden, ld_hs, student_weight, ld_ws, h_student, teacher_hidden, ld_ht,
+                                teacher_weight, ld_wt, h_teacher, T, V, tile_rows, workspace, workspace_bytes, 0, &w);
+  if (st != LP_OK) return st;
+  if (!targets && (lp_student || lp_teacher || prob_diff))
+    return fail(LP_ERR_INVALID_ARGUMENT, "%s: lp_student/lp_teacher/prob_diff need targets", fn);
+  if (T == 0) return ok();
+  if (!kl) return fail(LP_ERR_INVALID_ARGUMENT, "%s: kl is required", fn);
+  if (targets && !aligned(targets, 8)) return fail(LP_ERR_INVALID_ARGUMENT, "%s: misaligned targets", fn);
+  const lp::LMHeadShape su = make_shape(student_hidden, ld_hs, student_weight, ld_ws, T, h_student, V, targets, 1,
+                                        mask, 1.0f, tile_rows);
+  const lp::LMHeadShape te = make_shape(teacher_hidden, ld_ht, teacher_weight, ld_wt, T, h_teacher, V, targets, 1,
+                                        mask, 1.0f, tile_rows);
+  const lp::KLHeadOutputs out{kl, lp_student, lp_teacher, prob_diff, lse_student, lse_teacher};
+  hipError_t e = lp::launch_lmhead_kl_forward(su, te, targets, diff_mask, out, static_cast<char*>(workspace), w,
+                                              static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return ok();
+}
+
+lp_status lp_lm_head_kl_backward(const void* student_hidden, int64_t ld_hs, const void* student_weight,
+                                 int64_t ld_ws, int64_t h_student, const void* teacher_hidden, int64_t ld_ht,
+                                 const void* teacher_weight, int64_t ld_wt, int64_t h_teacher, int64_t T, int64_t V,
+                                 const uint8_t* mask, int64_t tile_rows, const float* lse_student,
+                                 const float* lse_teacher, const float* grad_kl, float* grad_hidden,
+                                 float* grad_weight, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "lp_lm_head_kl_backward";
+  lp::LMHeadWorkspace w;
+  lp_status st = check_kl_heads(fn, student_hidden, ld_hs, student_weight, ld_ws, h_student, teacher_hidden, ld_ht,
+                                teacher_weight, ld_wt, h_teacher, T, V, tile_rows, workspace, workspace_bytes, 1, &w);
+  if (st != LP_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T == 0) {
+    if (grad_weight) {
+      hipError_t e = lp::launch_zero_f32(grad_weight, V * h_student, s);
+      if (e != hipSuccess) return hip_fail(e, fn);
+    }
+    return ok();
+  }
+  if (!lse_student || !lse_teacher || !grad_kl)
+    return fail(LP_ERR_INVALID_ARGUMENT, "%s: lse_student, lse_teacher and grad_kl are required", fn);
+  const lp::LMHeadShape su = make_shape(student_hidden, ld_hs, student_weight, ld_ws, T, h_student, V, nullptr, 1,
+                                        mask, 1.0f, tile_rows);
+  const lp::LMHeadShape te = make_shape(teacher_hidden, ld_ht, teacher_weight, ld_wt, T, h_teacher, V, nullptr, 1,
+                                        mask, 1.0f, tile_rows);
+  hipError_t e = lp::launch_lmhead_kl_backward(su, te, lse_student, lse_teacher, grad_kl, grad_hidden, grad_weight,
+                                               static_cast<char*>(workspace), w, s);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return ok();
+}
+
 lp_status lp_kl_full_vocab(const void* student, const void* teacher, lp_dtype dtype, int64_t T, int64_t V,
                            int64_t ld_s, int64_t ld_t, float* kl, const int64_t* targets,
                            const uint8_t* diff_mask, float* lp_student, float* lp_teacher, float* prob_diff,

@@ -99,6 +99,7 @@ struct LMHeadWorkspace {
   int64_t vpad;
 };
 
+// backward: 0 log-prob forward, 1 backward (either loss), 2 KL forward.
 bool lmhead_workspace_layout(int64_t T, int64_t h, int64_t V, int64_t tile_rows, int backward,
                              LMHeadWorkspace* w);
 
@@ -111,5 +112,25 @@ hipError_t launch_lmhead_forward(const LMHeadShape& sh, float* logprob, float* e
 hipError_t launch_lmhead_backward(const LMHeadShape& sh, const float* lse, const float* entropy,
                                   const float* grad_logprob, const float* grad_entropy, float* grad_hidden,
                                   float* grad_weight, char* ws, const LMHeadWorkspace& w, hipStream_t s);
+
+// KL(teacher || student) with both models' logits rebuilt through their heads.
+// `student` carries the student's hidden / weight / h plus T, V, mask and
+// tile_rows; `teacher` its hidden / weight / h (other fields unused).
+struct KLHeadOutputs {
+  float* kl;
+  float* lp_student;
+  float* lp_teacher;
+  float* prob_diff;
+  float* lse_student;
+  float* lse_teacher;
+};
+
+hipError_t launch_lmhead_kl_forward(const LMHeadShape& student, const LMHeadShape& teacher, const int64_t* targets,
+                                    const uint8_t* diff_mask, const KLHeadOutputs& out, char* ws,
+                                    const LMHeadWorkspace& w, hipStream_t s);
+
+hipError_t launch_lmhead_kl_backward(const LMHeadShape& student, const LMHeadShape& teacher, const float* lse_student,
+                                     const float* lse_teacher, const float* grad_kl, float* grad_hidden,
+                                     float* grad_weight, char* ws, const LMHeadWorkspace& w, hipStream_t s);
 
 }  // namespace lp

@@ -111,11 +111,15 @@ bool lmhead_workspace_layout(int64_t T, int64_t h, int64_t V, int64_t tile_rows,
   w->count_off = off;
   off += 256;
   w->part_off = w->zy_off = w->dz_off = 0;
-  if (!backward) {
+  if (backward == 0 || backward == 2) {
+    // log-prob forward: 3 floats per partial state, up to kMaxTargets target logits per row;
+    // KL forward: 5 floats per dual state, the student and teacher target logits per row
+    const int fields = backward == 0 ? 3 : 5;
+    const int per_row = backward == 0 ? kMaxTargets : 2;
     w->part_off = off;
-    off = align_up(off + static_cast<size_t>(tr) * w->n_vblocks * 3 * 4, 256);
+    off = align_up(off + static_cast<size_t>(tr) * w->n_vblocks * fields * 4, 256);
     w->zy_off = off;
-    off = align_up(off + static_cast<size_t>(tr) * kMaxTargets * 4, 256);
+    off = align_up(off + static_cast<size_t>(tr) * per_row * 4, 256);
   } else {
     const size_t tpad = align_up(static_cast<size_t>(tr), 64);
     w->dz_off = off;  // dZ [tpad x vpad], dZ^T [vpad x tpad], W^T [h x vpad], H_tile^T [h x tpad]
@@ -133,8 +137,20 @@ bool lmhead_workspace_layout(int64_t T, int64_t h, int64_t V, int64_t tile_rows,
 // scored-row compaction
 // ---------------------------------------------------------------------------
 
+// Per-row outputs that unscored rows get as zeros: up to 6 arrays of
+// width[i] floats per row (null pointers skipped).
+struct ZeroOuts {
+  float* p[6];
+  int width[6];
+};
+
+static ZeroOuts zero_outs(float* a = nullptr, int wa = 1, float* b = nullptr, float* c = nullptr, float* d = nullptr,
+                   float* e = nullptr, float* f = nullptr) {
+  return ZeroOuts{{a, b, c, d, e, f}, {wa, 1, 1, 1, 1, 1}};
+}
+
 __global__ void __launch_bounds__(1024) k_compact(const uint8_t* __restrict__ mask, int64_t T, int* __restrict__ idx,
-                                                  int* __restrict__ count, float* o1, int k1, float* o2, float* o3) {
+                                                  int* __restrict__ count, ZeroOuts z) {
   __shared__ int sums[1024];
   const int tid = threadIdx.x;
   const int64_t per = (T + 1023) / 1024;
@@ -155,10 +171,10 @@ __global__ void __launch_bounds__(1024) k_compact(const uint8_t* __restrict__ ma
     if (mask == nullptr || mask[i] != 0) {
       idx[pos++] = static_cast<int>(i);
     } else {
-      if (o1)
-        for (int k = 0; k < k1; ++k) o1[i * k1 + k] = 0.f;
-      if (o2) o2[i] = 0.f;
-      if (o3) o3[i] = 0.f;
+#pragma unroll
+      for (int q = 0; q < 6; ++q)
+        if (z.p[q])
+          for (int k = 0; k < z.width[q]; ++k) z.p[q][i * z.width[q] + k] = 0.f;
     }
   }
   if (tid == 1023) *count = sums[1023];
@@ -368,7 +384,8 @@ hipError_t launch_lmhead_forward(const LMHeadShape& sh, float* logprob, float* e
   float* zy = reinterpret_cast<float*>(ws + w.zy_off);
   {
     TimedLaunch tl("k_compact", s);
-    hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, s, sh.mask, sh.T, idx, count, logprob, sh.K, entropy, lse);
+    hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, s, sh.mask, sh.T, idx, count,
+                       zero_outs(logprob, sh.K, entropy, lse));
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -516,6 +533,20 @@ struct DzArgs {
   uint16_t* dzt;  // [vpad][tpad] or nullptr
 };
 
+// Four consecutive vocab columns vq..vq+3 of tile row r: one 8-byte store
+// into dZ [row][vocab] and, if requested, four 2-byte stores into dZ^T.
+__device__ __forceinline__ void dz_store4(uint16_t* dz, uint16_t* dzt, int64_t vpad, int64_t tpad, int r, int vq,
+                                          const uint16_t (&outv)[4]) {
+  uint2 pk;
+  pk.x = static_cast<uint32_t>(outv[0]) | (static_cast<uint32_t>(outv[1]) << 16);
+  pk.y = static_cast<uint32_t>(outv[2]) | (static_cast<uint32_t>(outv[3]) << 16);
+  *reinterpret_cast<uint2*>(dz + static_cast<int64_t>(r) * vpad + vq) = pk;
+  if (dzt) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dzt[static_cast<int64_t>(vq + j) * tpad + r] = outv[j];
+  }
+}
+
 // dL/dlogits epilogue: for tile rows r < rowsK (the K span of the
 // weight-gradient GEMM; rows past the tile's valid rows get 0) and vocab
 // columns v < vpad (0 past V), writes bf16 dZ[r][v] and, if requested, dZ^T[v][r].
@@ -566,16 +597,7 @@ __device__ __forceinline__ void dz_epilogue(const DzArgs& a, f32x16_t (&acc)[C::
           }
           outv[j] = f32_to_bf16_rne(d);
         }
-        if (vq < a.vpad) {
-          uint2 pk;
-          pk.x = static_cast<uint32_t>(outv[0]) | (static_cast<uint32_t>(outv[1]) << 16);
-          pk.y = static_cast<uint32_t>(outv[2]) | (static_cast<uint32_t>(outv[3]) << 16);
-          *reinterpret_cast<uint2*>(a.dz + static_cast<int64_t>(r) * a.vpad + vq) = pk;
-          if (a.dzt) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) a.dzt[static_cast<int64_t>(vq + j) * a.tpad + r] = outv[j];
-          }
-        }
+        if (vq < a.vpad) dz_store4(a.dz, a.dzt, a.vpad, a.tpad, r, vq, outv);
       }
   }
 }
@@ -789,9 +811,13 @@ __global__ void __launch_bounds__(C::NT) k_out_gemm(OutGemmArgs g) {
   }
 }
 
-hipError_t launch_lmhead_backward(const LMHeadShape& sh, const float* lse, const float* entropy,
-                                  const float* grad_logprob, const float* grad_entropy, float* grad_hidden,
-                                  float* grad_weight, char* ws, const LMHeadWorkspace& w, hipStream_t s) {
+// Steps shared by both losses' backward: scored-row compaction, W^T, then per
+// tile of rows: dL/dlogits (launched by `launch_dz`, which also zero-pads rows
+// up to a multiple of 64 on the fast path), dHidden and dW.
+template <class LaunchDz>
+hipError_t backward_tiles(const LMHeadShape& sh, bool fast, int bm_fast, int bn_fast, float* grad_hidden,
+                          float* grad_weight,
+                          char* ws, const LMHeadWorkspace& w, hipStream_t s, LaunchDz&& launch_dz) {
   using C = BwdCfg;
   using F = FwdDtlCfg;
   int* idx = reinterpret_cast<int*>(ws + w.idx_off);
@@ -808,12 +834,10 @@ hipError_t launch_lmhead_backward(const LMHeadShape& sh, const float* lse, const
   uint16_t* ht = reinterpret_cast<uint16_t*>(ws + off);
   off = align_up(off + static_cast<size_t>(sh.h) * tpad * 2, 256);
   float* hpart = reinterpret_cast<float*>(ws + off);  // split-K partials of dHidden (fast path)
-  const bool fast = lmhead_fast_path(sh) && (reinterpret_cast<uintptr_t>(grad_hidden) & 15u) == 0;
 
   {
     TimedLaunch tl("k_compact", s);
-    hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, s, sh.mask, sh.T, idx, count, static_cast<float*>(nullptr),
-                       0, static_cast<float*>(nullptr), static_cast<float*>(nullptr));
+    hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, s, sh.mask, sh.T, idx, count, zero_outs());
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -834,45 +858,13 @@ hipError_t launch_lmhead_backward(const LMHeadShape& sh, const float* lse, const
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  const int bm = fast ? F::BM : C::BM;
-  const int bn = fast ? F::BN : C::BN;
+  const int bm = fast ? bm_fast : C::BM;
+  const int bn = fast ? bn_fast : C::BN;
   const int n_vb = (sh.V + bm - 1) / bm;
   const int n_nb = static_cast<int>((tr + bn - 1) / bn);
   for (int64_t base = 0; base < sh.T; base += tr) {
-    DzArgs d;
-    d.weight = sh.weight;
-    d.ld_w = sh.ld_w;
-    d.hidden = sh.hidden;
-    d.ld_h = sh.ld_h;
-    d.h = sh.h;
-    d.V = sh.V;
-    d.vpad = vpad;
-    d.idx = idx;
-    d.count = count;
-    d.targets = sh.targets;
-    d.K = sh.K;
-    d.lse = lse;
-    d.entropy = entropy;
-    d.g_lp = grad_logprob;
-    d.g_H = grad_entropy;
-    d.c = sh.c;
-    d.inv_tau = sh.inv_tau;
-    d.tile_base = base;
-    d.tile_rows = static_cast<int>(tr);
-    d.tpad = tpad;
-    d.n_vb = n_vb;
-    d.n_nb = n_nb;
-    d.dz = dz;
-    d.dzt = grad_weight ? dzt : nullptr;
-    {
-      TimedLaunch tl("k_bwd_dz", s);
-      const dim3 grid(static_cast<unsigned>(n_vb) * n_nb);
-      if (fast)
-        hipLaunchKernelGGL(k_bwd_dz_dtl<F>, grid, dim3(F::NT), 0, s, d);
-      else
-        hipLaunchKernelGGL(k_bwd_dz<C>, grid, dim3(C::NT), 0, s, d);
-    }
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch_dz(base, tr, tpad, vpad, n_vb, n_nb, idx, count, dz, grad_weight ? dzt : nullptr)) != hipSuccess)
+      return e;
 
     if (grad_hidden && fast) {
       // dHidden[idx[r]] = dZ[r] . W : K = vpad split into kSplitK ranges, then a fixed-order sum
@@ -1003,6 +995,514 @@ hipError_t launch_lmhead_backward(const LMHeadShape& sh, const float* lse, const
     }
   }
   return hipSuccess;
+}
+
+
+hipError_t launch_lmhead_backward(const LMHeadShape& sh, const float* lse, const float* entropy,
+                                  const float* grad_logprob, const float* grad_entropy, float* grad_hidden,
+                                  float* grad_weight, char* ws, const LMHeadWorkspace& w, hipStream_t s) {
+  const bool fast = lmhead_fast_path(sh) && (reinterpret_cast<uintptr_t>(grad_hidden) & 15u) == 0;
+  auto launch_dz = [&](int64_t base, int64_t tr, int64_t tpad, int64_t vpad, int n_vb, int n_nb, const int* idx,
+                       const int* count, uint16_t* dz, uint16_t* dzt) -> hipError_t {
+    DzArgs d;
+    d.weight = sh.weight;
+    d.ld_w = sh.ld_w;
+    d.hidden = sh.hidden;
+    d.ld_h = sh.ld_h;
+    d.h = sh.h;
+    d.V = sh.V;
+    d.vpad = vpad;
+    d.idx = idx;
+    d.count = count;
+    d.targets = sh.targets;
+    d.K = sh.K;
+    d.lse = lse;
+    d.entropy = entropy;
+    d.g_lp = grad_logprob;
+    d.g_H = grad_entropy;
+    d.c = sh.c;
+    d.inv_tau = sh.inv_tau;
+    d.tile_base = base;
+    d.tile_rows = static_cast<int>(tr);
+    d.tpad = tpad;
+    d.n_vb = n_vb;
+    d.n_nb = n_nb;
+    d.dz = dz;
+    d.dzt = dzt;
+    TimedLaunch tl("k_bwd_dz", s);
+    const dim3 grid(static_cast<unsigned>(n_vb) * n_nb);
+    if (fast)
+      hipLaunchKernelGGL(k_bwd_dz_dtl<FwdDtlCfg>, grid, dim3(FwdDtlCfg::NT), 0, s, d);
+    else
+      hipLaunchKernelGGL(k_bwd_dz<BwdCfg>, grid, dim3(BwdCfg::NT), 0, s, d);
+    return hipGetLastError();
+  };
+  return backward_tiles(sh, fast, FwdDtlCfg::BM, FwdDtlCfg::BN, grad_hidden, grad_weight, ws, w, s, launch_dz);
+}
+
+
+// ---------------------------------------------------------------------------
+// KL(teacher || student) with both logits rebuilt through each model's head
+// ---------------------------------------------------------------------------
+// DeepSeek-V4 book ch.19 (名词速通 "不实例化 logits", §2 "Teacher
+// Scheduling"): only the last hidden states are kept; the logits of both
+// models are rebuilt through their output heads a tile at a time and reduced
+// to the exact KL directly.  Per (vocab block, row block) the kernel runs two
+// MFMA GEMMs into two accumulator sets (teacher v, then student u), folds
+// them into one dual state per row (the state of the KL on given logits),
+// and a merge kernel combines a row's states in a fixed order.  The backward
+// recomputes both tiles and writes dL/du = g (p_u - p_v) as bf16 for the
+// student's dHidden / dW GEMMs; the teacher is not trained.
+
+// Two accumulator sets must fit next to the mainloop's registers: 128 vocab x
+// 64 rows per wave, 4 waves side by side along the rows (a 128 x 256 block,
+// one wave per SIMD so each wave may hold 2 x 128 accumulator registers).
+// Measured faster than 64 x 64 wave tiles at two waves per SIMD, whose
+// operand traffic per MFMA is a third higher.
+#ifndef LP_KL_DTL_TILE
+#define LP_KL_DTL_TILE 128, 256, 1, 4
+#endif
+using KLDtlCfg = DtlCfg<LP_KL_DTL_TILE>;
+static_assert(KLDtlCfg::BM >= (FwdCfg::BM < FwdDtlCfg::BM ? FwdCfg::BM : FwdDtlCfg::BM),
+              "the workspace holds partial states for vocab blocks of at least the smallest forward block");
+
+struct KLHeadArgs {
+  const uint16_t* ws;  // student weight [V x ld_ws]
+  int64_t ld_ws;
+  const uint16_t* hs;  // student hidden [T x ld_hs]
+  int64_t ld_hs;
+  int h_s;
+  const uint16_t* wt;  // teacher weight
+  int64_t ld_wt;
+  const uint16_t* ht;  // teacher hidden
+  int64_t ld_ht;
+  int h_t;
+  int V;
+  const int* idx;
+  const int* count;
+  const int64_t* targets;  // [T] or nullptr
+  float c;                 // log2 e
+  int64_t tile_base;
+  int tile_rows;
+  int n_vb, n_nb;
+  float* part;  // [tile_rows][n_vb][5]
+  float* zy;    // [tile_rows][2]: student, teacher target logit
+};
+
+template <class C>
+__device__ __forceinline__ void kl_epilogue(const KLHeadArgs& a, f32x16_t (&accu)[C::MI][C::NI],
+                                            f32x16_t (&accv)[C::MI][C::NI], int vb, int n0, int rows, uint16_t* lds) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave % C::WGM, wn = wave / C::WGM;
+  const int vwave = vb * C::BM + wm * C::WTM;
+  const int half = lane >> 5;
+  KLState* sm = reinterpret_cast<KLState*>(lds);  // [WGM][BN], reused after the K loops
+  const float c = a.c;
+  const bool full_block = (vb + 1) * C::BM <= a.V;
+#pragma unroll
+  for (int ni = 0; ni < C::NI; ++ni) {
+    const int nl = wn * C::WTN + ni * 32 + (lane & 31);
+    const int r = n0 + nl;
+    const bool valid_row = r < rows;
+    KLState st{kNegBig, 0.f, kNegBig, 0.f, 0.f};
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi) {
+      float xu[16], xv[16];
+      if (full_block) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          xu[i] = accu[mi][ni][i];
+          xv[i] = accv[mi][ni][i];
+        }
+        kl_push<false, 16, 16>(st, xu, xv, c);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int v = vwave + mi * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+          xu[i] = (v < a.V) ? accu[mi][ni][i] : -INFINITY;
+          xv[i] = (v < a.V) ? accv[mi][ni][i] : -INFINITY;
+        }
+        kl_push<true, 16, 16>(st, xu, xv, c);
+      }
+    }
+    if (a.targets && valid_row) {
+      const int64_t yrel = a.targets[a.idx[a.tile_base + r]] - vwave;
+      if (yrel >= 0 && yrel < C::WTM) {
+        float zu = 0.f, zv = 0.f;
+        bool found = false;
+#pragma unroll
+        for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (yrel == mi * 32 + 8 * (i >> 2) + 4 * half + (i & 3)) {
+              zu = accu[mi][ni][i];
+              zv = accv[mi][ni][i];
+              found = true;
+            }
+        if (found) {
+          a.zy[static_cast<int64_t>(r) * 2] = zu;
+          a.zy[static_cast<int64_t>(r) * 2 + 1] = zv;
+        }
+      }
+    }
+    KLState o;
+    o.mcu = __shfl_xor(st.mcu, 32, 64);
+    o.su = __shfl_xor(st.su, 32, 64);
+    o.mcv = __shfl_xor(st.mcv, 32, 64);
+    o.sv = __shfl_xor(st.sv, 32, 64);
+    o.C = __shfl_xor(st.C, 32, 64);
+    st = kl_merge(st, o);
+    if (lane < 32) sm[wm * C::BN + nl] = st;
+  }
+  __syncthreads();
+  if (wm == 0 && lane < 32) {
+#pragma unroll
+    for (int ni = 0; ni < C::NI; ++ni) {
+      const int nl = wn * C::WTN + ni * 32 + lane;
+      const int r = n0 + nl;
+      if (r < rows) {
+        KLState st = sm[nl];
+#pragma unroll
+        for (int k = 1; k < C::WGM; ++k) st = kl_merge(st, sm[k * C::BN + nl]);
+        float* p = a.part + (static_cast<int64_t>(r) * a.n_vb + vb) * 5;
+        p[0] = st.mcu;
+        p[1] = st.su;
+        p[2] = st.mcv;
+        p[3] = st.sv;
+        p[4] = st.C;
+      }
+    }
+  }
+}
+
+// Block coordinates shared by the KL tiles; false if the block has no rows.
+__device__ __forceinline__ bool kl_block(int n_vb, int n_nb, const int* count_p, int64_t tile_base, int tile_rows,
+                                         int bn, int& vb, int& n0, int& rows) {
+  int nb;
+  tile_coords(xcd_remap(blockIdx.x, n_vb * n_nb), n_vb, n_nb, vb, nb);
+  const int64_t rem = static_cast<int64_t>(*count_p) - tile_base;
+  rows = static_cast<int>(rem < tile_rows ? rem : tile_rows);
+  n0 = nb * bn;
+  return n0 < rows;
+}
+
+// Generic KL tile (any h % 8 == 0).
+template <class C>
+__global__ void __launch_bounds__(C::NT) k_kl_tile(KLHeadArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
+  int vb, n0, rows;
+  if (!kl_block(a.n_vb, a.n_nb, a.count, a.tile_base, a.tile_rows, C::BN, vb, n0, rows)) return;
+  const int v0 = vb * C::BM;
+  GemmOperands op;
+  op.a = a.wt + static_cast<int64_t>(v0) * a.ld_wt;
+  op.lda = a.ld_wt;
+  op.M = a.V - v0;
+  op.b = a.ht;
+  op.ldb = a.ld_ht;
+  op.b_rows = a.idx + a.tile_base + n0;
+  op.N = rows - n0;
+  op.K = a.h_t;
+  f32x16_t accv[C::MI][C::NI], accu[C::MI][C::NI];
+  gemm_tile<C>(op, 0, 0, lds, accv);
+  op.a = a.ws + static_cast<int64_t>(v0) * a.ld_ws;
+  op.lda = a.ld_ws;
+  op.b = a.hs;
+  op.ldb = a.ld_hs;
+  op.K = a.h_s;
+  gemm_tile<C>(op, 0, 0, lds, accu);
+  kl_epilogue<C>(a, accu, accv, vb, n0, rows, lds);
+}
+
+// Fast KL tile (both h % 64 == 0): direct-to-LDS mainloop, 256 x 128 block.
+template <class C>
+__global__ void __launch_bounds__(C::NT) k_kl_tile_dtl(KLHeadArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[C::LDS_ELEMS];
+  int vb, n0, rows;
+  if (!kl_block(a.n_vb, a.n_nb, a.count, a.tile_base, a.tile_rows, C::BN, vb, n0, rows)) return;
+  const int v0 = vb * C::BM;
+  const int* brows = a.idx + a.tile_base + n0;
+  f32x16_t accv[C::MI][C::NI], accu[C::MI][C::NI];
+  gemm_tile_dtl<C>(a.wt + static_cast<int64_t>(v0) * a.ld_wt, a.ld_wt, a.V - v0, a.ht, a.ld_ht, brows, rows - n0,
+                   a.h_t, lds, accv);
+  gemm_tile_dtl<C>(a.ws + static_cast<int64_t>(v0) * a.ld_ws, a.ld_ws, a.V - v0, a.hs, a.ld_hs, brows, rows - n0,
+                   a.h_s, lds, accu);
+  kl_epilogue<C>(a, accu, accv, vb, n0, rows, lds);
+}
+
+struct KLMergeArgs {
+  const float* part;
+  const float* zy;
+  int n_vb;
+  const int* idx;
+  const int* count;
+  const int64_t* targets;
+  const uint8_t* diff_mask;
+  int V;
+  float c;
+  int64_t tile_base;
+  int tile_rows;
+  KLHeadOutputs out;
+};
+
+__global__ void __launch_bounds__(256) k_kl_merge(KLMergeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t rem = static_cast<int64_t>(*a.count) - a.tile_base;
+  const int rows = static_cast<int>(rem < a.tile_rows ? rem : a.tile_rows);
+  if (r >= rows) return;
+  const float* p = a.part + static_cast<int64_t>(r) * a.n_vb * 5;
+  KLState st{kNegBig, 0.f, kNegBig, 0.f, 0.f};
+  for (int vb = lane; vb < a.n_vb; vb += 64)
+    st = kl_merge(st, KLState{p[vb * 5], p[vb * 5 + 1], p[vb * 5 + 2], p[vb * 5 + 3], p[vb * 5 + 4]});
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    KLState o;
+    o.mcu = __shfl_xor(st.mcu, off, 64);
+    o.su = __shfl_xor(st.su, off, 64);
+    o.mcv = __shfl_xor(st.mcv, off, 64);
+    o.sv = __shfl_xor(st.sv, off, 64);
+    o.C = __shfl_xor(st.C, off, 64);
+    st = kl_merge(st, o);
+  }
+  if (lane != 0) return;
+  const int64_t row = a.idx[a.tile_base + r];
+  const float l2u = log2f(st.su), l2v = log2f(st.sv);
+  const float lseu = (st.mcu + l2u) * kLn2, lsev = (st.mcv + l2v) * kLn2;
+  const KLHeadOutputs& o = a.out;
+  o.kl[row] = st.C / st.sv - ((st.mcv - st.mcu) + (l2v - l2u)) * kLn2;
+  if (o.lse_student) o.lse_student[row] = lseu;
+  if (o.lse_teacher) o.lse_teacher[row] = lsev;
+  if (a.targets) {
+    const int64_t y = a.targets[row];
+    float lpu = __builtin_nanf(""), lpv = __builtin_nanf("");
+    if (y >= 0 && y < a.V) {
+      lpu = (fmaf(a.zy[static_cast<int64_t>(r) * 2], a.c, -st.mcu) - l2u) * kLn2;
+      lpv = (fmaf(a.zy[static_cast<int64_t>(r) * 2 + 1], a.c, -st.mcv) - l2v) * kLn2;
+    }
+    if (o.lp_student) o.lp_student[row] = lpu;
+    if (o.lp_teacher) o.lp_teacher[row] = lpv;
+    if (o.prob_diff) {
+      const bool keep = a.diff_mask == nullptr || a.diff_mask[row] != 0;
+      o.prob_diff[row] = keep ? fabsf(expf(lpu) - expf(lpv)) : 0.f;
+    }
+  }
+}
+
+static bool kl_fast_path(const LMHeadShape& st, const LMHeadShape& te) { return lmhead_fast_path(st) && lmhead_fast_path(te); }
+
+static KLHeadArgs kl_args(const LMHeadShape& st, const LMHeadShape& te) {
+  KLHeadArgs a;
+  a.ws = st.weight;
+  a.ld_ws = st.ld_w;
+  a.hs = st.hidden;
+  a.ld_hs = st.ld_h;
+  a.h_s = st.h;
+  a.wt = te.weight;
+  a.ld_wt = te.ld_w;
+  a.ht = te.hidden;
+  a.ld_ht = te.ld_h;
+  a.h_t = te.h;
+  a.V = st.V;
+  a.c = 1.44269504088896340736f;
+  return a;
+}
+
+hipError_t launch_lmhead_kl_forward(const LMHeadShape& sh, const LMHeadShape& te, const int64_t* targets,
+                                    const uint8_t* diff_mask, const KLHeadOutputs& out, char* ws,
+                                    const LMHeadWorkspace& w, hipStream_t s) {
+  int* idx = reinterpret_cast<int*>(ws + w.idx_off);
+  int* count = reinterpret_cast<int*>(ws + w.count_off);
+  float* part = reinterpret_cast<float*>(ws + w.part_off);
+  float* zy = reinterpret_cast<float*>(ws + w.zy_off);
+  {
+    TimedLaunch tl("k_compact", s);
+    hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, s, sh.mask, sh.T, idx, count,
+                       zero_outs(out.kl, 1, out.lp_student, out.lp_teacher, out.prob_diff, out.lse_student,
+                                 out.lse_teacher));
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t tr = sh.tile_rows < sh.T ? sh.tile_rows : sh.T;
+  const bool fast = kl_fast_path(sh, te);
+  const int bm = fast ? KLDtlCfg::BM : FwdCfg::BM;
+  const int bn = fast ? KLDtlCfg::BN : FwdCfg::BN;
+  const int n_vb = (sh.V + bm - 1) / bm;
+  const int n_nb = static_cast<int>((tr + bn - 1) / bn);
+  for (int64_t base = 0; base < sh.T; base += tr) {
+    KLHeadArgs a = kl_args(sh, te);
+    a.idx = idx;
+    a.count = count;
+    a.targets = targets;
+    a.tile_base = base;
+    a.tile_rows = static_cast<int>(tr);
+    a.n_vb = n_vb;
+    a.n_nb = n_nb;
+    a.part = part;
+    a.zy = zy;
+    {
+      TimedLaunch tl("k_kl_tile", s);
+      const dim3 grid(static_cast<unsigned>(n_vb) * n_nb);
+      if (fast)
+        hipLaunchKernelGGL(k_kl_tile_dtl<KLDtlCfg>, grid, dim3(KLDtlCfg::NT), 0, s, a);
+      else
+        hipLaunchKernelGGL(k_kl_tile<FwdCfg>, grid, dim3(FwdCfg::NT), 0, s, a);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    KLMergeArgs m;
+    m.part = part;
+    m.zy = zy;
+    m.n_vb = n_vb;
+    m.idx = idx;
+    m.count = count;
+    m.targets = targets;
+    m.diff_mask = diff_mask;
+    m.V = sh.V;
+    m.c = a.c;
+    m.tile_base = base;
+    m.tile_rows = static_cast<int>(tr);
+    m.out = out;
+    {
+      TimedLaunch tl("k_kl_merge", s);
+      hipLaunchKernelGGL(k_kl_merge, dim3(static_cast<unsigned>((tr + 3) / 4)), dim3(256), 0, s, m);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// ---- KL backward: dL/du = g (p_u - p_v) on the student's logits -----------
+
+struct KLDzArgs {
+  KLHeadArgs h;
+  int64_t vpad;
+  const float* lse_u;
+  const float* lse_v;
+  const float* g;
+  int64_t tpad;
+  uint16_t* dz;
+  uint16_t* dzt;
+};
+
+template <class C>
+__device__ __forceinline__ void kl_dz_epilogue(const KLDzArgs& a, f32x16_t (&accu)[C::MI][C::NI],
+                                               f32x16_t (&accv)[C::MI][C::NI], int v0, int n0, int rows, int rowsK) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave % C::WGM, wn = wave / C::WGM;
+  const int vlane = v0 + wm * C::WTM + 4 * (lane >> 5);
+  const float c = a.h.c;
+#pragma unroll
+  for (int ni = 0; ni < C::NI; ++ni) {
+    const int r = n0 + wn * C::WTN + ni * 32 + (lane & 31);
+    if (r >= rowsK) continue;
+    const bool valid = r < rows;
+    float lu = 0.f, lv = 0.f, g = 0.f;
+    if (valid) {
+      const int64_t row = a.h.idx[a.h.tile_base + r];
+      lu = a.lse_u[row] * c;
+      lv = a.lse_v[row] * c;
+      g = a.g[row];
+    }
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int vq = vlane + mi * 32 + 8 * q;
+        uint16_t outv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float d = 0.f;
+          if (valid && vq + j < a.h.V) {
+            const float pu = fast_exp2(fmaf(accu[mi][ni][q * 4 + j], c, -lu));
+            const float pv = fast_exp2(fmaf(accv[mi][ni][q * 4 + j], c, -lv));
+            d = g * (pu - pv);
+          }
+          outv[j] = f32_to_bf16_rne(d);
+        }
+        if (vq < a.vpad) dz_store4(a.dz, a.dzt, a.vpad, a.tpad, r, vq, outv);
+      }
+  }
+}
+
+template <class C>
+__global__ void __launch_bounds__(C::NT) k_kl_dz(KLDzArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
+  int vb, n0, rows;
+  kl_block(a.h.n_vb, a.h.n_nb, a.h.count, a.h.tile_base, a.h.tile_rows, C::BN, vb, n0, rows);
+  const int rowsK = (rows + 7) & ~7;
+  if (rows <= 0 || n0 >= rowsK) return;
+  const int v0 = vb * C::BM;
+  GemmOperands op;
+  op.a = a.h.wt + static_cast<int64_t>(v0) * a.h.ld_wt;
+  op.lda = a.h.ld_wt;
+  op.M = a.h.V - v0;
+  op.b = a.h.ht;
+  op.ldb = a.h.ld_ht;
+  op.b_rows = a.h.idx + a.h.tile_base + n0;
+  op.N = rows - n0;
+  op.K = a.h.h_t;
+  f32x16_t accv[C::MI][C::NI], accu[C::MI][C::NI];
+  gemm_tile<C>(op, 0, 0, lds, accv);
+  op.a = a.h.ws + static_cast<int64_t>(v0) * a.h.ld_ws;
+  op.lda = a.h.ld_ws;
+  op.b = a.h.hs;
+  op.ldb = a.h.ld_hs;
+  op.K = a.h.h_s;
+  gemm_tile<C>(op, 0, 0, lds, accu);
+  kl_dz_epilogue<C>(a, accu, accv, v0, n0, rows, rowsK);
+}
+
+template <class C>
+__global__ void __launch_bounds__(C::NT) k_kl_dz_dtl(KLDzArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[C::LDS_ELEMS];
+  int vb, n0, rows;
+  kl_block(a.h.n_vb, a.h.n_nb, a.h.count, a.h.tile_base, a.h.tile_rows, C::BN, vb, n0, rows);
+  const int rowsK = (rows + 63) & ~63;
+  if (rows <= 0 || n0 >= rowsK) return;
+  const int v0 = vb * C::BM;
+  const int* brows = a.h.idx + a.h.tile_base + n0;
+  f32x16_t accv[C::MI][C::NI], accu[C::MI][C::NI];
+  gemm_tile_dtl<C>(a.h.wt + static_cast<int64_t>(v0) * a.h.ld_wt, a.h.ld_wt, a.h.V - v0, a.h.ht, a.h.ld_ht, brows,
+                   rows - n0, a.h.h_t, lds, accv);
+  gemm_tile_dtl<C>(a.h.ws + static_cast<int64_t>(v0) * a.h.ld_ws, a.h.ld_ws, a.h.V - v0, a.h.hs, a.h.ld_hs, brows,
+                   rows - n0, a.h.h_s, lds, accu);
+  kl_dz_epilogue<C>(a, accu, accv, v0, n0, rows, rowsK);
+}
+
+hipError_t launch_lmhead_kl_backward(const LMHeadShape& sh, const LMHeadShape& te, const float* lse_student,
+                                     const float* lse_teacher, const float* grad_kl, float* grad_hidden,
+                                     float* grad_weight, char* ws, const LMHeadWorkspace& w, hipStream_t s) {
+  const bool fast = kl_fast_path(sh, te) && (reinterpret_cast<uintptr_t>(grad_hidden) & 15u) == 0;
+  auto launch_dz = [&](int64_t base, int64_t tr, int64_t tpad, int64_t vpad, int n_vb, int n_nb, const int* idx,
+                       const int* count, uint16_t* dz, uint16_t* dzt) -> hipError_t {
+    KLDzArgs d;
+    d.h = kl_args(sh, te);
+    d.h.idx = idx;
+    d.h.count = count;
+    d.h.targets = nullptr;
+    d.h.tile_base = base;
+    d.h.tile_rows = static_cast<int>(tr);
+    d.h.n_vb = n_vb;
+    d.h.n_nb = n_nb;
+    d.h.part = nullptr;
+    d.h.zy = nullptr;
+    d.vpad = vpad;
+    d.lse_u = lse_student;
+    d.lse_v = lse_teacher;
+    d.g = grad_kl;
+    d.tpad = tpad;
+    d.dz = dz;
+    d.dzt = dzt;
+    TimedLaunch tl("k_kl_dz", s);
+    const dim3 grid(static_cast<unsigned>(n_vb) * n_nb);
+    if (fast)
+      hipLaunchKernelGGL(k_kl_dz_dtl<KLDtlCfg>, grid, dim3(KLDtlCfg::NT), 0, s, d);
+    else
+      hipLaunchKernelGGL(k_kl_dz<BwdCfg>, grid, dim3(BwdCfg::NT), 0, s, d);
+    return hipGetLastError();
+  };
+  return backward_tiles(sh, fast, KLDtlCfg::BM, KLDtlCfg::BN, grad_hidden, grad_weight, ws, w, s, launch_dz);
 }
 
 }  // namespace lp

@@ -111,78 +111,8 @@ hipError_t launch_logprobs_entropy(int dtype, const RowArgs& a, hipStream_t s) {
 // ---------------------------------------------------------------------------
 // exact KL(teacher || student) over the full vocabulary
 // ---------------------------------------------------------------------------
-// Student u: (mcu, su).  Teacher v: (mcv, sv) and C = sum_j 2^{tv_j} (v_j - u_j)
-// on the teacher's reference.  Then, with natural-log normalisers
-// lse = ln2 (mc + log2 s):  KL = C / sv - (lse_v - lse_u).
-
-struct KLState {
-  float mcu, su, mcv, sv, C;
-};
-
-template <bool GUARD, int N, int CH>
-__device__ __forceinline__ void kl_push(KLState& st, const float* xu, const float* xv, float c) {
-  float mu = xu[0], mv = xv[0];
-#pragma unroll
-  for (int k = 1; k < N; ++k) {
-    mu = fmaxf(mu, xu[k]);
-    mv = fmaxf(mv, xv[k]);
-  }
-  const float muc = mu * c, mvc = mv * c;
-  if (muc > st.mcu) {
-    if (st.su > 0.f) st.su *= fast_exp2(st.mcu - muc);
-    st.mcu = muc;
-  }
-  if (mvc > st.mcv) {
-    if (st.sv > 0.f) {
-      const float r = fast_exp2(st.mcv - mvc);
-      st.sv *= r;
-      st.C *= r;
-    }
-    st.mcv = mvc;
-  }
-  const float nu = -st.mcu, nv = -st.mcv;
-#pragma unroll
-  for (int g = 0; g < N; g += CH) {
-    float pu = 0.f, pv = 0.f, pc = 0.f;
-#pragma unroll
-    for (int k = 0; k < CH; ++k) {
-      const float eu = fast_exp2(fmaf(xu[g + k], c, nu));
-      const float ev = fast_exp2(fmaf(xv[g + k], c, nv));
-      pu += eu;
-      pv += ev;
-      const float d = xv[g + k] - xu[g + k];
-      if (GUARD)
-        pc += (ev > 0.f) ? ev * d : 0.f;
-      else
-        pc = fmaf(ev, d, pc);
-    }
-    st.su += pu;
-    st.sv += pv;
-    st.C += pc;
-  }
-}
-
-__device__ __forceinline__ KLState kl_merge(KLState x, KLState y) {
-  KLState r;
-  r.mcu = fmaxf(x.mcu, y.mcu);
-  r.su = 0.f;
-  if (x.su > 0.f) r.su += x.su * fast_exp2(x.mcu - r.mcu);
-  if (y.su > 0.f) r.su += y.su * fast_exp2(y.mcu - r.mcu);
-  r.mcv = fmaxf(x.mcv, y.mcv);
-  r.sv = 0.f;
-  r.C = 0.f;
-  if (x.sv > 0.f) {
-    const float f = fast_exp2(x.mcv - r.mcv);
-    r.sv += x.sv * f;
-    r.C += x.C * f;
-  }
-  if (y.sv > 0.f) {
-    const float f = fast_exp2(y.mcv - r.mcv);
-    r.sv += y.sv * f;
-    r.C += y.C * f;
-  }
-  return r;
-}
+// The dual state (KLState, kl_push, kl_merge) is shared with the fused LM-head
+// KL and lives with the other device helpers.
 
 template <int NT>
 __device__ __forceinline__ KLState kl_block_allreduce(KLState st, KLState* sm) {

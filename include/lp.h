@@ -200,6 +200,59 @@ lp_status lp_lm_head_logprobs_entropy_backward_k(const void* hidden, int64_t ld_
                                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * KL(teacher || student) with both models' logits rebuilt from cached last
+ * hidden states through their own output heads, never materialised
+ * (DeepSeek-V4 book ch.19: 名词速通 "不实例化 logits" and §2 "Teacher
+ * Scheduling" -- the teacher's last hidden state is cached and passed
+ * through its prediction head when the KL is computed).
+ *
+ * For each row t with mask[t] != 0 (mask NULL = all rows):
+ *   u = student_hidden[t] . student_weight^T,  v = teacher_hidden[t] . teacher_weight^T
+ *   (bf16 operands, fp32 MFMA accumulation, never rounded), and
+ *   kl[t] = sum_j p_v,j (log p_v,j - log p_u,j) with p = softmax (no temperature),
+ *   lse_student[t] = logsumexp(u), lse_teacher[t] = logsumexp(v),
+ *   lp_student[t] = log p_u(y_t), lp_teacher[t] = log p_v(y_t)  (targets != NULL),
+ *   prob_diff[t] = |exp(lp_student) - exp(lp_teacher)| where diff_mask[t] != 0
+ *   (diff_mask NULL = all), else 0.
+ * Rows with mask 0 get 0 in every output and are never multiplied.
+ *
+ * Layouts: hiddens bf16 [T x ld_h*] with h_student / h_teacher used columns;
+ * weights bf16 [V x ld_w*] (both heads share the vocabulary); every h and ld
+ * a multiple of 8; hiddens and weights 16-byte aligned.  Outputs are fp32
+ * [T]; kl is required, every other output may be NULL (lp_student,
+ * lp_teacher and prob_diff need targets).  A target outside [0, V) gives NaN
+ * in lp_student / lp_teacher / prob_diff of that row only.
+ * Workspace: lp_lm_head_kl_workspace_bytes(T, h_student, V, tile_rows, 0)
+ * bytes, 256-byte aligned, caller-owned; scratch only.  tile_rows bounds it.
+ * Errors as for the other LM-head calls: all checks before any launch.
+ */
+size_t lp_lm_head_kl_workspace_bytes(int64_t T, int64_t h_student, int64_t V, int64_t tile_rows, int backward);
+
+lp_status lp_lm_head_kl(const void* student_hidden, int64_t ld_hs, const void* student_weight, int64_t ld_ws,
+                        int64_t h_student, const void* teacher_hidden, int64_t ld_ht, const void* teacher_weight,
+                        int64_t ld_wt, int64_t h_teacher, int64_t T, int64_t V, const uint8_t* mask,
+                        const int64_t* targets, const uint8_t* diff_mask, int64_t tile_rows, float* kl,
+                        float* lp_student, float* lp_teacher, float* prob_diff, float* lse_student,
+                        float* lse_teacher, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward of sum_t grad_kl[t] * kl[t] with respect to the student only (the
+ * teacher head is frozen: it is only loaded to rebuild logits):
+ *   dL/du_t,j = grad_kl[t] (p_u,j - p_v,j), rows with mask 0 contribute 0,
+ *   grad_hidden = dL/du . student_weight   fp32 [T x h_student] (NULL: skipped),
+ *   grad_weight = dL/du^T . student_hidden fp32 [V x h_student] (NULL: frozen).
+ * Both logit tiles are recomputed; lse_student / lse_teacher are the forward's.
+ * Workspace: lp_lm_head_kl_workspace_bytes(T, h_student, V, tile_rows, 1).
+ * With T == 0, grad_weight (if given) is zero-filled.
+ */
+lp_status lp_lm_head_kl_backward(const void* student_hidden, int64_t ld_hs, const void* student_weight,
+                                 int64_t ld_ws, int64_t h_student, const void* teacher_hidden, int64_t ld_ht,
+                                 const void* teacher_weight, int64_t ld_wt, int64_t h_teacher, int64_t T, int64_t V,
+                                 const uint8_t* mask, int64_t tile_rows, const float* lse_student,
+                                 const float* lse_teacher, const float* grad_kl, float* grad_hidden,
+                                 float* grad_weight, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Aggregates of the masked prob diff, the macro statistics the msprobe page
  * lists next to its per-token diff (§4.1): over positions with mask != 0
  * (mask NULL = all), with pa = exp(lp_a), pb = exp(lp_b), d = |pa - pb|:

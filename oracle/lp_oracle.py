@@ -492,27 +492,38 @@ def lm_head_kl_loss(hidden_s, weight_s, hidden_t, weight_t, mask, grad_kl) -> fl
     return float(np.dot(np.asarray(grad_kl, dtype=np.float64).reshape(kl.shape), kl))
 
 
-def lm_head_kl_backward(hidden_s, weight_s, hidden_t, weight_t, mask, grad_kl):
-    """(dHidden_student, dWeight_student) of `lm_head_kl_loss`.
+def lm_head_kl_logit_grad(hidden_s, weight_s, hidden_t, weight_t, mask, grad_kl):
+    """(scored rows, dL/du [rows, V]) for the loss sum_t g_t KL_t.
 
     KL_t = sum_j p_v (log p_v - log p_u) depends on the student logits u only
     through -sum_j p_v log p_u = lse_u - sum_j p_v u_j, whose derivative in
-    u_j is p_u,j - p_v,j.  The teacher is not trained (its head is only
-    loaded to rebuild logits), so no teacher gradient is formed.
+    u_j is p_u,j - p_v,j.
     """
     hs = np.atleast_2d(np.asarray(hidden_s, dtype=np.float64))
     ht = np.atleast_2d(np.asarray(hidden_t, dtype=np.float64))
-    T, h = hs.shape
-    Ws = np.asarray(weight_s, dtype=np.float64)
+    T = hs.shape[0]
     g = np.asarray(grad_kl, dtype=np.float64).reshape(T)
-    dH = np.zeros((T, h))
-    dW = np.zeros(Ws.shape)
     rows = np.nonzero(_scored(mask, T))[0]
     if rows.size == 0:
-        return dH, dW
-    pu = np.exp(log_softmax(lm_head_logits(hs[rows], Ws)))
+        return rows, np.zeros((0, weight_s.shape[0]))
+    pu = np.exp(log_softmax(lm_head_logits(hs[rows], weight_s)))
     pv = np.exp(log_softmax(lm_head_logits(ht[rows], weight_t)))
-    dZ = g[rows][:, None] * (pu - pv)
+    return rows, g[rows][:, None] * (pu - pv)
+
+
+def lm_head_kl_backward(hidden_s, weight_s, hidden_t, weight_t, mask, grad_kl):
+    """(dHidden_student, dWeight_student) of `lm_head_kl_loss`: dH = dZ . W_s,
+    dW = dZ^T . H_s with dZ from `lm_head_kl_logit_grad`.  The teacher is not
+    trained (its head is only loaded to rebuild logits), so no teacher
+    gradient is formed."""
+    hs = np.atleast_2d(np.asarray(hidden_s, dtype=np.float64))
+    T, h = hs.shape
+    Ws = np.asarray(weight_s, dtype=np.float64)
+    dH = np.zeros((T, h))
+    dW = np.zeros(Ws.shape)
+    rows, dZ = lm_head_kl_logit_grad(hs, Ws, hidden_t, weight_t, mask, grad_kl)
+    if rows.size == 0:
+        return dH, dW
     dH[rows] = dZ @ Ws
     dW = dZ.T @ hs[rows]
     return dH, dW

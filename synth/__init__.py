@@ -21,7 +21,7 @@ import numpy as np
 ROOT_SEED = 20261202
 
 # stream ids
-S_VALUES, S_TARGETS, S_MASK, S_SPIKE, S_WEIGHT, S_NOISE, S_GRAD_LP, S_GRAD_H = range(8)
+S_VALUES, S_TARGETS, S_MASK, S_SPIKE, S_WEIGHT, S_NOISE, S_GRAD_LP, S_GRAD_H, S_NOISE_W, S_GRAD_KL = range(10)
 
 _BLOCK_ELEMS = 1 << 22
 
@@ -117,7 +117,7 @@ def bernoulli_mask(T: int, p: float, workload: int, seed: int = ROOT_SEED) -> np
 # workloads
 # ---------------------------------------------------------------------------
 
-W_TINY_LM_HEAD, W_LOGITS, W_LM_HEAD_FWD, W_KL, W_LM_HEAD_BWD = 1, 2, 3, 4, 5
+W_TINY_LM_HEAD, W_LOGITS, W_LM_HEAD_FWD, W_KL, W_LM_HEAD_BWD, W_KL_HEADS = 1, 2, 3, 4, 5, 6
 
 
 @dataclass
@@ -228,6 +228,66 @@ class KLPair:
         targets = uniform_targets(T, V, wid, self.seed)
         diff_mask = bernoulli_mask(T, self.mask_p, wid, self.seed)
         self.arrays = dict(student=student, teacher=teacher, targets=targets, diff_mask=diff_mask)
+        return self
+
+
+def perturbed_bits(base: np.ndarray, precision: str, sigma: float, workload: int, stream: int,
+                   seed: int = ROOT_SEED) -> np.ndarray:
+    """round(base + N(0, sigma^2)) in `precision`, the noise drawn in fp32 per row block."""
+    rows, cols = base.shape
+    to_f32 = _bits_to_f32_fn(precision)
+    conv = f32_to_bf16_bits if precision == "bf16" else f32_to_fp16_bits
+    out = np.empty_like(base)
+
+    def fill(ib):
+        i, (r0, r1) = ib
+        g = rng(workload, stream, i, seed)
+        n = g.standard_normal((r1 - r0, cols), dtype=np.float32) * np.float32(sigma)
+        out[r0:r1] = conv(to_f32(base[r0:r1]) + n)
+
+    blocks = list(enumerate(_row_blocks(rows, cols)))
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(fill, blocks))
+    return out
+
+
+@dataclass
+class KLHeads:
+    """Student and teacher last hidden states and output heads, bf16:
+    student hidden [T, h] ~ N(0,1), student W [V, h] ~ N(0, w_sigma^2);
+    teacher hidden = bf16(student hidden + N(0, h_noise^2)), teacher W =
+    bf16(student W + N(0, w_noise^2)) (a teacher close to the student, as in
+    distillation); all rows scored unless prompt_frac > 0; uniform targets;
+    Bernoulli(0.6) diff mask; optional g_kl ~ N(0,1)."""
+    T: int = 16384
+    h: int = 7168
+    V: int = 129280
+    w_sigma: float = 0.02
+    h_noise: float = 0.3
+    w_noise: float = 0.005
+    prompt_frac: float = 0.0
+    mask_p: float = 0.6
+    tile_rows: int = 4096
+    grads: bool = False
+    workload: int = W_KL_HEADS
+    seed: int = ROOT_SEED
+    arrays: dict = field(default_factory=dict, repr=False)
+
+    def build(self):
+        wid = self.workload
+        hs = normal_bits((self.T, self.h), 1.0, "bf16", wid, S_VALUES, self.seed)
+        ws = normal_bits((self.V, self.h), self.w_sigma, "bf16", wid, S_WEIGHT, self.seed)
+        ht = perturbed_bits(hs, "bf16", self.h_noise, wid, S_NOISE, self.seed)
+        wt = perturbed_bits(ws, "bf16", self.w_noise, wid, S_NOISE_W, self.seed)
+        if self.prompt_frac > 0:
+            mask = packed_response_mask(self.T, 512, 8192, self.prompt_frac, wid, self.seed)
+        else:
+            mask = np.ones(self.T, dtype=np.uint8)
+        self.arrays = dict(student_hidden=hs, student_weight=ws, teacher_hidden=ht, teacher_weight=wt, mask=mask,
+                           targets=uniform_targets(self.T, self.V, wid, self.seed),
+                           diff_mask=bernoulli_mask(self.T, self.mask_p, wid, self.seed))
+        if self.grads:
+            self.arrays["grad_kl"] = normal_f32(self.T, 1.0, wid, S_GRAD_KL, self.seed)
         return self
 
 

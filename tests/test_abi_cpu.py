@@ -114,6 +114,42 @@ def test_kl_validation(lib):
     assert lib.lp_prob_diff(FAKE, FAKE, None, -1, FAKE, None) == 1
 
 
+@pytest.mark.parametrize("args,code", [
+    (dict(T=-1), 1),
+    (dict(V=0), 1),
+    (dict(tile_rows=0), 1),
+    (dict(h_t=0), 1),
+    (dict(h_s=12, ld_hs=16, ld_ws=16), 2),   # student h % 8
+    (dict(ld_ht=8), 1),                       # teacher ld_h < h
+    (dict(ht=FAKE + 8), 2),                   # teacher hidden not 16-byte aligned
+    (dict(ws=None), 3),
+    (dict(ws_bytes=64), 3),
+    (dict(kl=None), 1),
+    (dict(targets=None, lps=FAKE), 1),        # target outputs need targets
+])
+def test_lm_head_kl_validation(lib, args, code):
+    a = dict(hs=FAKE, ld_hs=64, ws_=FAKE, ld_ws=64, h_s=64, ht=FAKE, ld_ht=32, wt=FAKE, ld_wt=32, h_t=32, T=8, V=100,
+             targets=FAKE, tile_rows=4, kl=FAKE, lps=None, ws=FAKE, ws_bytes=1 << 30)
+    a.update(args)
+    st = lib.lp_lm_head_kl(a["hs"], a["ld_hs"], a["ws_"], a["ld_ws"], a["h_s"], a["ht"], a["ld_ht"], a["wt"],
+                           a["ld_wt"], a["h_t"], a["T"], a["V"], None, a["targets"], None, a["tile_rows"], a["kl"],
+                           a["lps"], None, None, None, None, a["ws"], a["ws_bytes"], None)
+    assert st == code, lib.lp_last_error()
+
+
+def test_lm_head_kl_workspace_and_backward_checks(lib):
+    f = lib.lp_lm_head_kl_workspace_bytes
+    fw, bw = f(16384, 7168, 129280, 4096, 0), f(16384, 7168, 129280, 4096, 1)
+    assert 0 < fw < bw and fw < 16384 * 129280 * 4 / 50
+    assert f(8, 0, 100, 4, 0) == 0 and f(8, 64, 100, 0, 1) == 0
+    # backward without the forward's saved normalisers
+    st = lib.lp_lm_head_kl_backward(FAKE, 64, FAKE, 64, 64, FAKE, 64, FAKE, 64, 64, 8, 100, None, 4, None, FAKE, FAKE,
+                                    FAKE, FAKE, FAKE, 1 << 30, None)
+    assert st == 1 and b"lse_student" in lib.lp_last_error()
+    assert lib.lp_lm_head_kl(None, 64, None, 64, 64, None, 64, None, 64, 64, 0, 100, None, None, None, 4, None,
+                             None, None, None, None, None, None, 0, None) == 0
+
+
 def test_product_path_has_no_fallback(tmp_path):
     """A missing library is an error, not a silent CPU path."""
     from entropy_chunked_row_amd import _lib

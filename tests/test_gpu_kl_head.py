@@ -1,0 +1,141 @@
+"""GPU parity of the KL rebuilt through each model's output head (forward
+and student backward) against the fp64 oracle."""
+import numpy as np
+import pytest
+
+import synth
+from oracle import lp_oracle as O
+from tests.helpers import grad_errors, host, max_abs_err, to_dev, to_dev_bits
+
+pytestmark = pytest.mark.gpu
+
+# Fused class: the logits are fp32 MFMA sums, compared with exact fp64 ones.
+TOL_FWD = 2e-3
+TOL_GRAD = 1e-2
+
+
+def _lp():
+    import entropy_chunked_row_amd as lp
+    return lp
+
+
+def _bf16(rng, shape, sigma):
+    return synth.f32_to_bf16_bits((rng.normal(0, sigma, size=shape)).astype(np.float32))
+
+
+def _case(T, hs, ht, V, seed, scored=0.8):
+    rng = np.random.default_rng(seed)
+    A = dict(student_hidden=_bf16(rng, (T, hs), 1.0), student_weight=_bf16(rng, (V, hs), 0.08),
+             teacher_hidden=_bf16(rng, (T, ht), 1.0), teacher_weight=_bf16(rng, (V, ht), 0.08))
+    A["mask"] = (rng.random(T) < scored).astype(np.uint8)
+    A["targets"] = rng.integers(0, V, size=T).astype(np.int64)
+    A["diff_mask"] = (rng.random(T) < 0.6).astype(np.uint8)
+    A["grad_kl"] = rng.normal(0, 1, size=T).astype(np.float32)
+    return A
+
+
+def _dev_heads(A):
+    return [to_dev_bits(A[k], "bf16") for k in ("student_hidden", "student_weight", "teacher_hidden",
+                                                 "teacher_weight")]
+
+
+def _wide(A):
+    return [O.widen_bf16(A[k]) for k in ("student_hidden", "student_weight", "teacher_hidden", "teacher_weight")]
+
+
+@pytest.mark.parametrize("T,hs,ht,V,tile", [
+    (50, 40, 72, 1031, 16),      # generic path (h % 64 != 0), ragged tiles and vocab block
+    (300, 128, 256, 5000, 128),  # fast path, different widths, partial last vocab block
+    (130, 64, 64, 512, 4096),    # fast path, one tile, vocab a multiple of the block
+])
+def test_kl_head_forward_backward(T, hs, ht, V, tile):
+    A = _case(T, hs, ht, V, seed=T + hs + ht)
+    A["targets"][np.nonzero(A["mask"])[0][0]] = V  # out of range: NaN lps for that row only
+    heads = _dev_heads(A)
+    m, y, dm = to_dev(A["mask"]), to_dev(A["targets"]), to_dev(A["diff_mask"])
+    got = [host(t) for t in _lp().lp_lm_head_kl(*heads, m, y, dm, tile)]
+    want = O.lm_head_kl(*_wide(A), A["mask"], A["targets"], A["diff_mask"])
+    sc = A["mask"] != 0
+    bad = A["targets"] >= V
+    for name, g, w in zip(("kl", "lp_s", "lp_t", "diff", "lse_s", "lse_t"), got, want):
+        assert not g[~sc].any(), name
+        ok = sc & ~bad if name in ("lp_s", "lp_t", "diff") else sc
+        assert max_abs_err(g[ok], w[ok]) <= TOL_FWD, (name, max_abs_err(g[ok], w[ok]))
+    assert np.isnan(got[1][bad]).all() and np.isfinite(got[0][sc]).all()
+    # rows do not depend on the tiling: bitwise equal with another tile size
+    again = _lp().lp_lm_head_kl(*heads, m, y, dm, 7)
+    assert np.array_equal(host(again[0]), got[0]) and np.array_equal(host(again[4]), got[4])
+    # student backward
+    lse_s, lse_t = to_dev(got[4]), to_dev(got[5])
+    dH, dW = _lp().lp_lm_head_kl_backward(*heads, m, tile, lse_s, lse_t, to_dev(A["grad_kl"]))
+    dH_o, dW_o = O.lm_head_kl_backward(*_wide(A), A["mask"], A["grad_kl"])
+    for nm, g, w in (("dH", host(dH), dH_o), ("dW", host(dW), dW_o)):
+        fro, mad = grad_errors(g, w)
+        assert fro <= TOL_GRAD and mad <= TOL_GRAD, (nm, fro, mad)
+    assert not host(dH)[~sc].any()
+
+
+def test_kl_head_same_model_is_exactly_zero():
+    A = _case(96, 128, 128, 777, seed=5, scored=1.0)
+    hs, ws = to_dev_bits(A["student_hidden"], "bf16"), to_dev_bits(A["student_weight"], "bf16")
+    kl, *_ = _lp().lp_lm_head_kl(hs, ws, hs, ws, None, None, None, 32)
+    assert not host(kl).any()
+    _, _, _, _, lse_s, lse_t = _lp().lp_lm_head_kl(hs, ws, hs, ws, None, None, None, 32)
+    dH, dW = _lp().lp_lm_head_kl_backward(hs, ws, hs, ws, None, 32, lse_s, lse_t, to_dev(A["grad_kl"]))
+    assert not host(dH).any() and not host(dW).any()
+
+
+def test_kl_head_no_scored_rows_and_frozen_weight():
+    A = _case(40, 64, 64, 300, seed=9, scored=0.0)
+    heads = _dev_heads(A)
+    m = to_dev(A["mask"])
+    kl, lps, lpt, diff, lse_s, lse_t = _lp().lp_lm_head_kl(*heads, m, to_dev(A["targets"]), None, 16)
+    assert not host(kl).any() and not host(lps).any() and not host(diff).any()
+    dH, dW = _lp().lp_lm_head_kl_backward(*heads, m, 16, lse_s, lse_t, to_dev(A["grad_kl"]), need_grad_weight=False)
+    assert dW is None and not host(dH).any()
+
+
+class _LazyW:
+    def __init__(self, bits):
+        self.bits, self.shape = bits, bits.shape
+
+    def __getitem__(self, sl):
+        return O.widen_bf16(self.bits[sl])
+
+
+@pytest.mark.timeout(900)
+def test_kl_head_full_size_sampled():
+    """T = 16384 rows, h = 7168 for both models, V = 129280, tile 4096 (the
+    distillation workload): sampled rows of every forward output and of the
+    student dHidden against the oracle; dW against the identity
+    sum_v dW[v, :] = 0 (each row of p_u - p_v sums to 0)."""
+    import torch
+    cfg = synth.KLHeads(grads=True).build()
+    A = cfg.arrays
+    heads = _dev_heads(A)
+    y, dm = to_dev(A["targets"]), to_dev(A["diff_mask"])
+    out = _lp().lp_lm_head_kl(*heads, None, y, dm, cfg.tile_rows)
+    got = [host(t) for t in out]
+    rows = np.unique(np.concatenate([[0, 4095, 4096, cfg.T // 2, cfg.T - 1],
+                                     np.random.default_rng(21).choice(cfg.T, 4, replace=False)]))
+    want = O.lm_head_kl(O.widen_bf16(A["student_hidden"][rows]), _LazyW(A["student_weight"]),
+                        O.widen_bf16(A["teacher_hidden"][rows]), _LazyW(A["teacher_weight"]), None,
+                        A["targets"][rows], A["diff_mask"][rows])
+    for name, g, w in zip(("kl", "lp_s", "lp_t", "diff", "lse_s", "lse_t"), got, want):
+        assert max_abs_err(g[rows], w) <= TOL_FWD, (name, max_abs_err(g[rows], w))
+    assert np.isfinite(got[0]).all() and (got[0] > -1e-3).all()
+    g_kl = to_dev(A["grad_kl"])
+    dH, dW = _lp().lp_lm_head_kl_backward(*heads, None, cfg.tile_rows, out[4], out[5], g_kl)
+    Wl = _LazyW(A["student_weight"])
+    _, dZ = O.lm_head_kl_logit_grad(O.widen_bf16(A["student_hidden"][rows]), Wl,
+                                    O.widen_bf16(A["teacher_hidden"][rows]), _LazyW(A["teacher_weight"]), None,
+                                    A["grad_kl"][rows])
+    dH_o = np.zeros((len(rows), cfg.h))
+    for j0 in range(0, cfg.V, 16384):
+        dH_o += dZ[:, j0:j0 + 16384] @ Wl[j0:j0 + 16384]
+    fro, mad = grad_errors(dH[torch.as_tensor(rows)].cpu().numpy(), dH_o)
+    assert fro <= TOL_GRAD and mad <= TOL_GRAD, (fro, mad)
+    colsum = dW.double().sum(0)
+    scale = dW.double().abs().sum(0)
+    assert torch.isfinite(dW).all().item()
+    assert (colsum.abs() <= 1e-2 * scale).all().item()
