@@ -540,6 +540,11 @@ def test_prob_diff_stats_special_cases():
     # all-False mask: nothing to aggregate
     n, mx, mean, std, r = O.prob_diff_stats(np.log(p), np.log(p), np.zeros(100))
     assert n == 0 and mx == 0 and mean == 0 and std == 0 and math.isnan(r)
+    # one position, or a constant series: no spread, so no correlation
+    n, mx, mean, std, r = O.prob_diff_stats(np.log([0.5]), np.log([0.25]), None)
+    assert n == 1 and abs(mx - 0.25) < 1e-15 and abs(mean - 0.25) < 1e-15 and std == 0 and math.isnan(r)
+    n, mx, mean, std, r = O.prob_diff_stats(np.log(np.full(5, 0.3)), np.log(p[:5]), None)
+    assert n == 5 and math.isnan(r)
 
 
 def test_k_targets_match_single_target_calls():
