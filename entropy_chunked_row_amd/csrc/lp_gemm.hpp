@@ -199,13 +199,14 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
 
 // ---------------------------------------------------------------------------
 // Fast NT mainloop for K % BK == 0: global -> LDS with global_load_lds_dwordx4
-// (no register staging), XOR-swizzled LDS rows, two LDS stages, fragment
+// (no register staging), XOR-swizzled LDS rows, NS LDS stages, fragment
 // prefetch one K-substep ahead.
 //
-// LDS row = BK bf16 = 8 chunks of 16 bytes; the chunk holding logical 16-byte
-// column kc of row r sits at position kc ^ swz(r), swz(r) = (r & 7) ^ ((r >> 3) & 1),
-// so the 32 lanes reading one fragment column (rows r..r+31, same kc) spread
-// over all banks.  Each wave-wide load instruction fills 64 consecutive chunk
+// LDS row = BK bf16 = KC chunks of 16 bytes; the chunk holding logical 16-byte
+// column kc of row r sits at position kc ^ swz(r), so the 32 lanes reading one
+// fragment column (rows r..r+31, same kc) spread over all banks:
+//   BK = 64 (128-byte rows): swz(r) = (r & 7) ^ ((r >> 3) & 1);
+//   BK = 32 (64-byte rows, two rows per 128-byte bank line): swz(r) = (r >> 1) & 3.  Each wave-wide load instruction fills 64 consecutive chunk
 // slots (1 KB), so every lane loads the global chunk that belongs in its slot.
 // Rows past the valid range are clamped to the last valid row (their results
 // are discarded by the caller); K must be a multiple of BK.
@@ -218,14 +219,15 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void gbl_void_t;
 
-template <int BM_, int BN_, int WGM_, int WGN_>
+template <int BM_, int BN_, int WGM_, int WGN_, int BK_ = 64, int NS_ = 2>
 struct DtlCfg {
-  static constexpr int BM = BM_, BN = BN_, BK = 64, WGM = WGM_, WGN = WGN_;
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, WGM = WGM_, WGN = WGN_;
+  static constexpr int NS = NS_;                      // LDS stages
   static constexpr int NT = 64 * WGM * WGN;
   static constexpr int NW = WGM * WGN;
   static constexpr int WTM = BM / WGM, WTN = BN / WGN;
   static constexpr int MI = WTM / 32, NI = WTN / 32;
-  static constexpr int KC = BK / 8;                   // 8 chunks per row
+  static constexpr int KC = BK / 8;                   // 16-byte chunks per row
   // Waves that issue the global loads.  With two waves per SIMD, letting only
   // one of them load keeps the other free to feed the matrix unit while the
   // loads queue.
@@ -237,12 +239,22 @@ struct DtlCfg {
   static constexpr int A_INST = BM * KC / 64 / LW;    // load instructions per loading wave per stage (A)
   static constexpr int B_INST = BN * KC / 64 / LW;
   static constexpr int STAGE_ELEMS = (BM + BN) * BK;
-  static constexpr int LDS_ELEMS = 2 * STAGE_ELEMS;
+  static constexpr int LDS_ELEMS = NS * STAGE_ELEMS;
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
   static_assert((BM * KC) % (64 * LW) == 0 && (BN * KC) % (64 * LW) == 0, "tile not divisible among waves");
+  static_assert(BK == 64 || BK == 32, "LDS swizzle defined for 64- and 128-byte rows");
+  static_assert(NS >= 2 && (NS & (NS - 1)) == 0, "stage count must be a power of two >= 2");
 };
 
 __device__ __forceinline__ int lds_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+template <int KC>
+__device__ __forceinline__ int lds_swz_k(int r) {
+  if constexpr (KC == 8)
+    return lds_swz(r);
+  else
+    return (r >> 1) & 3;
+}
 
 // Row sources of one operand for this thread: byte offsets of the global chunk
 // each of its load instructions moves (K offset added per stage).
@@ -259,7 +271,7 @@ __device__ __forceinline__ void dtl_rows_dense(DtlRows<NINST>& rw, int64_t ld, i
   for (int j = 0; j < NINST; ++j) {
     const int slot = (j * C::LW + wave) * 64 + lane;
     const int r = slot / C::KC, pc = slot % C::KC;
-    const int kc = pc ^ lds_swz(r);
+    const int kc = pc ^ lds_swz_k<C::KC>(r);
     const int rr = r < M ? r : M - 1;
     rw.off[j] = static_cast<uint32_t>((static_cast<int64_t>(rr) * ld + kc * 8) * 2);
   }
@@ -273,7 +285,7 @@ __device__ __forceinline__ void dtl_rows_gather(DtlRows<NINST>& rw, int64_t ld, 
   for (int j = 0; j < NINST; ++j) {
     const int slot = (j * C::LW + wave) * 64 + lane;
     const int r = slot / C::KC, pc = slot % C::KC;
-    const int kc = pc ^ lds_swz(r);
+    const int kc = pc ^ lds_swz_k<C::KC>(r);
     const int rr = r < N ? r : N - 1;
     const int64_t src = rows ? static_cast<int64_t>(rows[rr]) : static_cast<int64_t>(rr);
     rw.off[j] = static_cast<uint32_t>((src * ld + kc * 8) * 2);
@@ -298,7 +310,7 @@ __device__ __forceinline__ void dtl_frag_piece(const uint16_t* stage, int kk, in
                                                bf16x8_t (&af)[C::MI], bf16x8_t (&bfr)[C::NI]) {
   const int lane = threadIdx.x & 63;
   const int r32 = lane & 31;
-  const int pc = ((kk >> 3) + (lane >> 5)) ^ lds_swz(r32);
+  const int pc = ((kk >> 3) + (lane >> 5)) ^ lds_swz_k<C::KC>(r32);
   if (q < C::MI) {
     af[q] = *reinterpret_cast<const bf16x8_t*>(stage + (wm * C::WTM + q * 32 + r32) * C::BK + pc * 8);
   } else {
@@ -324,21 +336,38 @@ __device__ __forceinline__ void dtl_issue_one(int j, const char* abase, const Dt
   }
 }
 
-// One K-step on stage X (the other stage is Y).  Instruction order, fixed with
+// Wait until at most `pending` stages' worth of this wave's global loads are
+// still in flight (pending is uniform and at most 3).
+template <class C>
+__device__ __forceinline__ void dtl_wait_vm(int pending) {
+  constexpr int NL = C::A_INST + C::B_INST;
+  static_assert(3 * NL <= 63, "vmcnt field is 6 bits");
+  if (pending <= 0)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if (pending == 1)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NL) : "memory");
+  else if (pending == 2)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NL) : "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * NL) : "memory");
+}
+
+// One K-step on stage X (the next stage is Y).  Instruction order, fixed with
 // scheduling barriers so that an MFMA never waits on a fragment read issued
 // just before it:
 //   substeps 0 .. S-2: MFMAs on X; between them, the fragment reads of the next
 //                      substep (from X).
-//   end of S-2:        wait for this wave's loads of the next stage, barrier
-//                      (next stage complete in Y; every wave is done reading X).
+//   end of S-2:        wait for this wave's loads of the next stage (`pending`
+//                      later stages may stay in flight), barrier (next stage
+//                      complete in Y; every wave is done reading X).
 //   substep S-1:       MFMAs on X (fragments already in registers); between them,
 //                      the first fragments of the next stage (from Y) and the
-//                      global loads of the stage after next (into X).
+//                      global loads of the stage NS steps ahead (into X).
 template <class C, bool NEXT, bool NEXT2>
 __device__ __forceinline__ void dtl_kstep(uint16_t* X, uint16_t* Y, const char* abase2, const DtlRows<C::A_INST>& ra,
                                           const char* bbase2, const DtlRows<C::B_INST>& rb, int wm, int wn,
                                           bf16x8_t (&fa)[2][C::MI], bf16x8_t (&fb)[2][C::NI],
-                                          f32x16_t (&acc)[C::MI][C::NI]) {
+                                          f32x16_t (&acc)[C::MI][C::NI], int pending) {
   constexpr int S = C::BK / 16;
   constexpr int NQ = C::MI * C::NI;
   constexpr int NF = C::MI + C::NI;
@@ -376,7 +405,7 @@ __device__ __forceinline__ void dtl_kstep(uint16_t* X, uint16_t* Y, const char* 
       __builtin_amdgcn_sched_barrier(0);
     }
     if (NEXT && s == S - 2) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      dtl_wait_vm<C>(pending);
       __syncthreads();
     }
   }
@@ -411,37 +440,37 @@ __device__ __forceinline__ void gemm_tile_dtl(const uint16_t* a, int64_t lda, in
   constexpr int KB = C::BK * 2;  // bytes per stage along K
   const int nk = K / C::BK;
   if (nk <= 0) return;  // empty K: D = 0
-  uint16_t* L0 = lds;
-  uint16_t* L1 = lds + C::STAGE_ELEMS;
-
-  // prologue: stages 0 and 1 in flight, wait for stage 0, read its first fragments
+  // prologue: the first min(NS, nk) stages in flight, wait for stage 0, read its first fragments
+  const int npro = nk < C::NS ? nk : C::NS;
   if ((threadIdx.x >> 6) < C::LW) {
 #pragma unroll
-    for (int j = 0; j < NL; ++j) dtl_issue_one<C, C::A_INST, C::B_INST>(j, abase, ra, bbase, rb, L0);
-    if (nk > 1) {
+    for (int st = 0; st < C::NS; ++st) {
+      if (st < npro) {
 #pragma unroll
-      for (int j = 0; j < NL; ++j) dtl_issue_one<C, C::A_INST, C::B_INST>(j, abase + KB, ra, bbase + KB, rb, L1);
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NL) : "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        for (int j = 0; j < NL; ++j)
+          dtl_issue_one<C, C::A_INST, C::B_INST>(j, abase + st * KB, ra, bbase + st * KB, rb,
+                                                 lds + st * C::STAGE_ELEMS);
+      }
     }
+    dtl_wait_vm<C>(npro - 1);
   }
   __syncthreads();
   bf16x8_t fa[2][C::MI], fb[2][C::NI];
 #pragma unroll
-  for (int q = 0; q < NF; ++q) dtl_frag_piece<C>(L0, 0, wm, wn, q, fa[0], fb[0]);
+  for (int q = 0; q < NF; ++q) dtl_frag_piece<C>(lds, 0, wm, wn, q, fa[0], fb[0]);
 
+  auto stage = [&](int k) { return lds + (k & (C::NS - 1)) * C::STAGE_ELEMS; };
   int kt = 0;
-  for (; kt + 2 < nk; ++kt) {
-    const int64_t kb2 = static_cast<int64_t>(kt + 2) * KB;
-    dtl_kstep<C, true, true>((kt & 1) ? L1 : L0, (kt & 1) ? L0 : L1, abase + kb2, ra, bbase + kb2, rb, wm, wn, fa, fb,
-                             acc);
+  // steady state: stage kt + NS is loaded into stage kt's buffer; NS - 2 later stages stay in flight
+  for (; kt + C::NS < nk; ++kt) {
+    const int64_t kbn = static_cast<int64_t>(kt + C::NS) * KB;
+    dtl_kstep<C, true, true>(stage(kt), stage(kt + 1), abase + kbn, ra, bbase + kbn, rb, wm, wn, fa, fb, acc,
+                             C::NS - 2);
   }
-  if (kt + 1 < nk) {
-    dtl_kstep<C, true, false>((kt & 1) ? L1 : L0, (kt & 1) ? L0 : L1, abase, ra, bbase, rb, wm, wn, fa, fb, acc);
-    ++kt;
-  }
-  dtl_kstep<C, false, false>((kt & 1) ? L1 : L0, (kt & 1) ? L0 : L1, abase, ra, bbase, rb, wm, wn, fa, fb, acc);
+  // drain: no more loads; stages kt + 2 .. nk - 1 are still in flight
+  for (; kt + 1 < nk; ++kt)
+    dtl_kstep<C, true, false>(stage(kt), stage(kt + 1), abase, ra, bbase, rb, wm, wn, fa, fb, acc, nk - kt - 2);
+  dtl_kstep<C, false, false>(stage(kt), stage(kt), abase, ra, bbase, rb, wm, wn, fa, fb, acc, 0);
   __syncthreads();
 }
 

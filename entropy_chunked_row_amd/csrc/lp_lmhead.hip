@@ -1289,7 +1289,9 @@ __global__ void __launch_bounds__(256) k_kl_merge(KLMergeArgs a) {
   }
 }
 
-static bool kl_fast_path(const LMHeadShape& st, const LMHeadShape& te) { return lmhead_fast_path(st) && lmhead_fast_path(te); }
+static bool kl_fast_path(const LMHeadShape& st, const LMHeadShape& te) {
+  return lmhead_fast_path(st) && lmhead_fast_path(te) && st.h % KLDtlCfg::BK == 0 && te.h % KLDtlCfg::BK == 0;
+}
 
 static KLHeadArgs kl_args(const LMHeadShape& st, const LMHeadShape& te) {
   KLHeadArgs a;
