@@ -703,6 +703,27 @@ __global__ void __launch_bounds__(C::NT) k_dense_gemm_dtl(DenseGemmArgs g) {
   const int wave = threadIdx.x >> 6;
   const int wm = wave % C::WGM, wn = wave / C::WGM;
   float* out = g.out + static_cast<int64_t>(ks) * g.tile_rows * g.ldo;  // splits > 1: partial ks
+  const int mlane = m0 + wm * C::WTM + 4 * (lane >> 5);
+  if (g.accumulate && m0 + C::BM <= M && n0 + C::BN <= g.N) {
+    // full block, read-modify-write: all reads of a column group are issued
+    // before any is consumed, so the block waits for memory once per group
+#pragma unroll
+    for (int ni = 0; ni < C::NI; ++ni) {
+      float* col = out + (n0 + wn * C::WTN + ni * 32 + (lane & 31));
+      float old[C::MI][16];
+#pragma unroll
+      for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          old[mi][i] = col[static_cast<int64_t>(mlane + mi * 32 + 8 * (i >> 2) + (i & 3)) * g.ldo];
+#pragma unroll
+      for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          col[static_cast<int64_t>(mlane + mi * 32 + 8 * (i >> 2) + (i & 3)) * g.ldo] = old[mi][i] + acc[mi][ni][i];
+    }
+    return;
+  }
 #pragma unroll
   for (int ni = 0; ni < C::NI; ++ni) {
     const int n = n0 + wn * C::WTN + ni * 32 + (lane & 31);
@@ -711,7 +732,7 @@ __global__ void __launch_bounds__(C::NT) k_dense_gemm_dtl(DenseGemmArgs g) {
     for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int m = m0 + wm * C::WTM + mi * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+        const int m = mlane + mi * 32 + 8 * (i >> 2) + (i & 3);
         if (m < M) {
           float* p = out + static_cast<int64_t>(m) * g.ldo + n;
           *p = g.accumulate ? (*p + acc[mi][ni][i]) : acc[mi][ni][i];
