@@ -182,7 +182,18 @@ def _cpu_baseline_lm_head(O, np, A, cfg, scored, seconds):
         n = min(len(scored), int(n * max(2.0, seconds / 3 / max(t, 1e-3))))
     return dict(value=n / t, unit="scored tokens/s", cores=_blas_threads(), kind="oracle",
                 sample=f"{n} scored rows of the same workload through the fp64 oracle (full V={cfg.V}, h={cfg.h})",
-                seconds=t)
+                seconds=t, cpu_model=_cpu_model())
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def bench_logits_input(lp, torch, np, synth, O, steps, warmup):

@@ -364,8 +364,8 @@ lp_status lp_kl_full_vocab(const void* student, const void* teacher, lp_dtype dt
                            const uint8_t* diff_mask, float* lp_student, float* lp_teacher, float* prob_diff,
                            void* stream) {
   const char* fn = "lp_kl_full_vocab";
-  if (dtype != LP_BF16 && dtype != LP_FP16)
-    return fail(LP_ERR_INVALID_ARGUMENT, "%s: dtype must be LP_BF16 or LP_FP16", fn);
+  if (dtype != LP_BF16 && dtype != LP_FP16 && dtype != LP_FP32)
+    return fail(LP_ERR_INVALID_ARGUMENT, "%s: dtype must be LP_BF16, LP_FP16 or LP_FP32", fn);
   if (T < 0) return fail(LP_ERR_INVALID_ARGUMENT, "%s: T < 0", fn);
   if (V <= 0 || V > kMaxV) return fail(LP_ERR_INVALID_ARGUMENT, "%s: V out of range (1..2^30)", fn);
   if (ld_s < V || ld_t < V) return fail(LP_ERR_INVALID_ARGUMENT, "%s: ld_s and ld_t must be >= V", fn);
@@ -374,7 +374,8 @@ lp_status lp_kl_full_vocab(const void* student, const void* teacher, lp_dtype dt
   if (T == 0) return ok();
   if (T > 0x7fffffff) return fail(LP_ERR_UNSUPPORTED, "%s: more than 2^31-1 rows", fn);
   if (!student || !teacher || !kl) return fail(LP_ERR_INVALID_ARGUMENT, "%s: student, teacher, kl required", fn);
-  if (!aligned(student, 2) || !aligned(teacher, 2) || (targets && !aligned(targets, 8)))
+  if (!aligned(student, dtype_bytes(dtype)) || !aligned(teacher, dtype_bytes(dtype)) ||
+      (targets && !aligned(targets, 8)))
     return fail(LP_ERR_INVALID_ARGUMENT, "%s: misaligned pointer", fn);
   lp::KLArgs a;
   a.student = student;

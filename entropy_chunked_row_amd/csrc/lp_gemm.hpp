@@ -374,7 +374,7 @@ __device__ __forceinline__ void dtl_kstep(uint16_t* X, uint16_t* Y, const char* 
   constexpr int NL = C::A_INST + C::B_INST;
   static_assert(S % 2 == 0, "substep 0 of every stage must use fragment buffer 0");
   static_assert(NF <= 2 * NQ, "not enough MFMA slots to interleave fragment reads");
-  const bool loader = (threadIdx.x >> 6) < C::LW;
+  const bool loader = C::LW == C::NW || (threadIdx.x >> 6) < C::LW;  // compile-time true when every wave loads
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     const int cur = s & 1;
@@ -442,7 +442,7 @@ __device__ __forceinline__ void gemm_tile_dtl(const uint16_t* a, int64_t lda, in
   if (nk <= 0) return;  // empty K: D = 0
   // prologue: the first min(NS, nk) stages in flight, wait for stage 0, read its first fragments
   const int npro = nk < C::NS ? nk : C::NS;
-  if ((threadIdx.x >> 6) < C::LW) {
+  if (C::LW == C::NW || (threadIdx.x >> 6) < C::LW) {
 #pragma unroll
     for (int st = 0; st < C::NS; ++st) {
       if (st < npro) {

@@ -74,18 +74,19 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 #define LP_GROUP_V 4
 #endif
 constexpr int kGroupV = LP_GROUP_V;
+template <int G = kGroupV>
 __device__ __forceinline__ void tile_coords(int L, int n_vb, int n_nb, int& vb, int& nb) {
-  const int full = n_vb / kGroupV;
-  const int g = L / (kGroupV * n_nb);
+  const int full = n_vb / G;
+  const int g = L / (G * n_nb);
   if (g < full) {
-    const int w = L - g * kGroupV * n_nb;
-    nb = w / kGroupV;
-    vb = g * kGroupV + w % kGroupV;
+    const int w = L - g * G * n_nb;
+    nb = w / G;
+    vb = g * G + w % G;
   } else {
-    const int w = L - full * kGroupV * n_nb;
-    const int gsz = n_vb - full * kGroupV;
+    const int w = L - full * G * n_nb;
+    const int gsz = n_vb - full * G;
     nb = w / gsz;
-    vb = full * kGroupV + w % gsz;
+    vb = full * G + w % gsz;
   }
 }
 
@@ -1084,6 +1085,11 @@ hipError_t launch_lmhead_backward(const LMHeadShape& sh, const float* lse, const
 #define LP_KL_DTL_TILE 128, 256, 1, 4
 #endif
 using KLDtlCfg = DtlCfg<LP_KL_DTL_TILE>;
+// Vocab blocks per group in the KL tiles' walk (measured: 4 beats 2, 8, 16).
+#ifndef LP_KL_GROUP_V
+#define LP_KL_GROUP_V 4
+#endif
+constexpr int kKLGroupV = LP_KL_GROUP_V;
 static_assert(KLDtlCfg::BM >= (FwdCfg::BM < FwdDtlCfg::BM ? FwdCfg::BM : FwdDtlCfg::BM),
               "the workspace holds partial states for vocab blocks of at least the smallest forward block");
 
@@ -1201,7 +1207,7 @@ __device__ __forceinline__ void kl_epilogue(const KLHeadArgs& a, f32x16_t (&accu
 __device__ __forceinline__ bool kl_block(int n_vb, int n_nb, const int* count_p, int64_t tile_base, int tile_rows,
                                          int bn, int& vb, int& n0, int& rows) {
   int nb;
-  tile_coords(xcd_remap(blockIdx.x, n_vb * n_nb), n_vb, n_nb, vb, nb);
+  tile_coords<kKLGroupV>(xcd_remap(blockIdx.x, n_vb * n_nb), n_vb, n_nb, vb, nb);
   const int64_t rem = static_cast<int64_t>(*count_p) - tile_base;
   rows = static_cast<int>(rem < tile_rows ? rem : tile_rows);
   n0 = nb * bn;

@@ -235,7 +235,11 @@ static hipError_t launch_kl_t(const KLArgs& a, hipStream_t s) {
 
 hipError_t launch_kl_full_vocab(int dtype, const KLArgs& a, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
-  return dtype == 0 ? launch_kl_t<Bf16>(a, s) : launch_kl_t<Fp16>(a, s);
+  switch (dtype) {
+    case 0: return launch_kl_t<Bf16>(a, s);
+    case 1: return launch_kl_t<Fp16>(a, s);
+    default: return launch_kl_t<Fp32>(a, s);
+  }
 }
 
 // ---------------------------------------------------------------------------

@@ -146,7 +146,7 @@ lp_status lp_lm_head_logprobs_entropy_backward(const void* hidden, int64_t ld_h,
  * one pass over both rows.  DeepSeek-V4 book ch.19 "RL / OPD 工程", 名词速通:
  * "不实例化 logits" and "TileLang KL Kernel" (exact student/teacher KL).
  *
- * student, teacher  [T x ld_s], [T x ld_t] of `dtype` (LP_BF16 or LP_FP16).
+ * student, teacher  [T x ld_s], [T x ld_t] of `dtype` (LP_BF16, LP_FP16 or LP_FP32).
  * kl                fp32 [T] (required), every row.
  * targets           int64 [T] or NULL.  When given, lp_student / lp_teacher
  *                   (fp32 [T] or NULL) receive log softmax at the target for

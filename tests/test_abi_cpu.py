@@ -107,7 +107,8 @@ def test_lm_head_validation(lib, args, code):
 
 
 def test_kl_validation(lib):
-    assert lib.lp_kl_full_vocab(FAKE, FAKE, 2, 4, 16, 16, 16, FAKE, None, None, None, None, None, None) == 1
+    assert lib.lp_kl_full_vocab(FAKE, FAKE, 7, 4, 16, 16, 16, FAKE, None, None, None, None, None, None) == 1
+    assert lib.lp_kl_full_vocab(FAKE + 2, FAKE, 2, 4, 16, 16, 16, FAKE, None, None, None, None, None, None) == 1
     assert lib.lp_kl_full_vocab(FAKE, FAKE, 1, 4, 16, 8, 16, FAKE, None, None, None, None, None, None) == 1
     # target outputs without targets
     assert lib.lp_kl_full_vocab(FAKE, FAKE, 1, 4, 16, 16, 16, FAKE, None, None, FAKE, None, None, None) == 1

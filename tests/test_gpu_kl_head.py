@@ -139,3 +139,19 @@ def test_kl_head_full_size_sampled():
     scale = dW.double().abs().sum(0)
     assert torch.isfinite(dW).all().item()
     assert (colsum.abs() <= 1e-2 * scale).all().item()
+
+
+def test_kl_head_matches_kl_on_fp32_logits():
+    """The KL through the heads against the KL on given logits fed each
+    model's hidden @ W^T (fp64 product of the same bf16 values, rounded to
+    fp32): the same fp32 reduction of the same logits."""
+    A = _case(120, 64, 96, 2500, seed=77, scored=1.0)
+    heads = _dev_heads(A)
+    y = to_dev(A["targets"])
+    kl_f, lps_f, lpt_f, _, _, _ = _lp().lp_lm_head_kl(*heads, None, y, None, 64)
+    Hs, Ws, Ht, Wt = _wide(A)
+    U = (Hs @ Ws.T).astype(np.float32)
+    Vt = (Ht @ Wt.T).astype(np.float32)
+    kl_l, lps_l, lpt_l, _ = _lp().lp_kl_full_vocab(to_dev(U), to_dev(Vt), y, None)
+    assert max_abs_err(host(kl_f), host(kl_l)) <= 2e-5
+    assert max_abs_err(host(lps_f), host(lps_l)) <= 2e-5 and max_abs_err(host(lpt_f), host(lpt_l)) <= 2e-5

@@ -265,3 +265,22 @@ def test_backward_full_size_sampled():
     scale = dW.double().abs().sum(0)
     assert torch.isfinite(dW).all().item()
     assert (colsum.abs() <= 1e-2 * scale).all().item()
+
+
+@pytest.mark.parametrize("h,tau", [(256, 0.7), (72, 1.0)])
+def test_fused_matches_logits_path_on_fp32_logits(h, tau):
+    """The fused forward against the logits-input kernel fed hidden @ W^T
+    (fp64 product of the same bf16 values, rounded to fp32): both are fp32
+    reductions of the same logits, so they agree far inside the fused
+    tolerance (miles PR #4645 "Testing": equality against hidden @ W.T)."""
+    T, V, tile = 150, 3001, 64
+    rng = np.random.default_rng(h)
+    hid = synth.f32_to_bf16_bits(rng.normal(0, 1, size=(T, h)).astype(np.float32))
+    W = synth.f32_to_bf16_bits(rng.normal(0, 0.05, size=(V, h)).astype(np.float32))
+    y = rng.integers(0, V, size=T).astype(np.int64)
+    m = (rng.random(T) < 0.7).astype(np.uint8)
+    Z = (O.widen_bf16(hid) @ O.widen_bf16(W).T).astype(np.float32)
+    lp_f, H_f, _ = _lp().lp_lm_head_logprobs_entropy(to_dev_bits(hid, "bf16"), to_dev_bits(W, "bf16"), to_dev(y),
+                                                     to_dev(m), tau, tile)
+    lp_l, H_l = _lp().lp_logprobs_entropy(to_dev(Z), to_dev(y), to_dev(m), tau)
+    assert max_abs_err(host(lp_f), host(lp_l)) <= 2e-5 and max_abs_err(host(H_f), host(H_l)) <= 2e-5

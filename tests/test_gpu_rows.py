@@ -203,6 +203,19 @@ def test_kl_small(dtype, V):
     assert np.all(host(d)[dm == 0] == 0)
 
 
+@pytest.mark.parametrize("V", [3, 1000, 4099])
+def test_kl_fp32_inputs(V):
+    T = 17
+    rng = np.random.default_rng(V + 1)
+    u = rng.normal(0, 4, size=(T, V)).astype(np.float32)
+    v = (u + rng.normal(0, 0.5, size=u.shape)).astype(np.float32)
+    targets = rng.integers(0, V, size=T).astype(np.int64)
+    kl, lpu, lpv, d = _lp().lp_kl_full_vocab(to_dev(u), to_dev(v), to_dev(targets), None)
+    kl_o, lpu_o, lpv_o, d_o = O.kl_and_prob_diff(u.astype(np.float64), v.astype(np.float64), targets, None)
+    assert max_abs_err(host(kl), kl_o) <= TOL
+    assert max_abs_err(host(lpu), lpu_o) <= TOL and max_abs_err(host(d), d_o) <= TOL
+
+
 def test_kl_self_exactly_zero_and_no_targets():
     rng = np.random.default_rng(3)
     ub = synth.f32_to_fp16_bits(rng.normal(0, 4, size=(5, 3333)).astype(np.float32))
