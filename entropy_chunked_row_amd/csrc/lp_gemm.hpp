@@ -256,12 +256,48 @@ __device__ __forceinline__ int lds_swz_k(int r) {
     return (r >> 1) & 3;
 }
 
-// Row sources of one operand for this thread: byte offsets of the global chunk
-// each of its load instructions moves (K offset added per stage).
+// Row sources of one operand for this thread: a buffer resource on the
+// operand base and the byte offset of the global chunk each of its load
+// instructions moves; the stage's K offset goes in the scalar offset, so a
+// load needs no vector address arithmetic.
+// The buffer-resource type exists only in the device pass; the host pass
+// parses device code without generating it.
+#if defined(__HIP_DEVICE_COMPILE__)
+typedef __amdgpu_buffer_rsrc_t dtl_rsrc_t;
+#else
+struct dtl_rsrc_t {
+  unsigned w[4];
+};
+#endif
+
 template <int NINST>
 struct DtlRows {
+  dtl_rsrc_t rsrc;
   uint32_t off[NINST];  // byte offsets from the operand base (the caller checks they fit in 32 bits)
 };
+
+// Raw buffer over [base, base + 4 GiB): offsets are kept in range by the row
+// clamping, the descriptor only removes the 64-bit address arithmetic.
+// Word 3 selects 32-bit data format, as untyped gfx9 buffer loads expect.
+__device__ __forceinline__ dtl_rsrc_t dtl_rsrc(const void* base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(0xffffffffu),
+                                           0x00020000);
+#else
+  (void)base;
+  return dtl_rsrc_t{};
+#endif
+}
+
+// 16-byte chunk at rsrc + voff + soff into this lane's slot of the 1 KB LDS
+// block at dst (direct to LDS, no staging registers).
+__device__ __forceinline__ void dtl_load16(const dtl_rsrc_t& rsrc, uint16_t* dst, uint32_t voff, uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(dst), 16, voff, soff, 0, 0);
+#else
+  (void)rsrc, (void)dst, (void)voff, (void)soff;
+#endif
+}
 
 // A operand: rows m0 + r of a row-major matrix (clamped to M - 1).
 template <class C, int NINST>
@@ -292,18 +328,6 @@ __device__ __forceinline__ void dtl_rows_gather(DtlRows<NINST>& rw, int64_t ld, 
   }
 }
 
-template <class C, int NINST>
-__device__ __forceinline__ void dtl_issue(const char* base, const DtlRows<NINST>& rw, int64_t kbytes,
-                                          uint16_t* lds_region) {
-  const int wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int j = 0; j < NINST; ++j) {
-    uint16_t* dst = lds_region + (j * C::NW + wave) * 64 * 8;
-    // C-style casts: generic -> global / LDS address spaces
-    __builtin_amdgcn_global_load_lds((gbl_void_t*)(base + rw.off[j] + kbytes), (lds_void_t*)(dst), 16, 0, 0);
-  }
-}
-
 // One 16-byte fragment read: piece q < MI reads A fragment q, else B fragment q - MI.
 template <class C>
 __device__ __forceinline__ void dtl_frag_piece(const uint16_t* stage, int kk, int wm, int wn, int q,
@@ -323,16 +347,17 @@ __device__ __forceinline__ void dtl_frag_piece(const uint16_t* stage, int kk, in
 // bases already include the stage's K offset (uniform), the per-lane part is a
 // 32-bit offset.  Only the first LW waves load (see DtlCfg::LW).
 template <class C, int NA, int NB>
-__device__ __forceinline__ void dtl_issue_one(int j, const char* abase, const DtlRows<NA>& ra, const char* bbase,
-                                              const DtlRows<NB>& rb, uint16_t* stage) {
-  const int wave = threadIdx.x >> 6;
+__device__ __forceinline__ void dtl_issue_one(int j, uint32_t kbytes, const DtlRows<NA>& ra, const DtlRows<NB>& rb,
+                                              uint16_t* stage) {
+  // the wave index is uniform: keep the LDS destination (M0) in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (j < NA) {
     uint16_t* dst = stage + (j * C::LW + wave) * 64 * 8;
-    __builtin_amdgcn_global_load_lds((gbl_void_t*)(abase + ra.off[j]), (lds_void_t*)(dst), 16, 0, 0);
+    dtl_load16(ra.rsrc, dst, ra.off[j], kbytes);
   } else {
     const int jb = j - NA;
     uint16_t* dst = stage + C::BM * C::BK + (jb * C::LW + wave) * 64 * 8;
-    __builtin_amdgcn_global_load_lds((gbl_void_t*)(bbase + rb.off[jb]), (lds_void_t*)(dst), 16, 0, 0);
+    dtl_load16(rb.rsrc, dst, rb.off[jb], kbytes);
   }
 }
 
@@ -364,8 +389,8 @@ __device__ __forceinline__ void dtl_wait_vm(int pending) {
 //                      the first fragments of the next stage (from Y) and the
 //                      global loads of the stage NS steps ahead (into X).
 template <class C, bool NEXT, bool NEXT2>
-__device__ __forceinline__ void dtl_kstep(uint16_t* X, uint16_t* Y, const char* abase2, const DtlRows<C::A_INST>& ra,
-                                          const char* bbase2, const DtlRows<C::B_INST>& rb, int wm, int wn,
+__device__ __forceinline__ void dtl_kstep(uint16_t* X, uint16_t* Y, uint32_t kb2, const DtlRows<C::A_INST>& ra,
+                                          const DtlRows<C::B_INST>& rb, int wm, int wn,
                                           bf16x8_t (&fa)[2][C::MI], bf16x8_t (&fb)[2][C::NI],
                                           f32x16_t (&acc)[C::MI][C::NI], int pending) {
   constexpr int S = C::BK / 16;
@@ -397,7 +422,7 @@ __device__ __forceinline__ void dtl_kstep(uint16_t* X, uint16_t* Y, const char* 
 #pragma unroll
         for (int u = 0; u < (NL + NQ - 1) / NQ; ++u) {
           const int j = q * ((NL + NQ - 1) / NQ) + u;
-          if (j < NL) dtl_issue_one<C, C::A_INST, C::B_INST>(j, abase2, ra, bbase2, rb, X);
+          if (j < NL) dtl_issue_one<C, C::A_INST, C::B_INST>(j, kb2, ra, rb, X);
         }
       }
       const int mi = q / C::NI, ni = q % C::NI;
@@ -435,8 +460,8 @@ __device__ __forceinline__ void gemm_tile_dtl(const uint16_t* a, int64_t lda, in
   DtlRows<C::B_INST> rb;
   dtl_rows_dense<C, C::A_INST>(ra, lda, M);
   dtl_rows_gather<C, C::B_INST>(rb, ldb, b_rows, N);
-  const char* abase = reinterpret_cast<const char*>(a);
-  const char* bbase = reinterpret_cast<const char*>(b);
+  ra.rsrc = dtl_rsrc(a);
+  rb.rsrc = dtl_rsrc(b);
   constexpr int KB = C::BK * 2;  // bytes per stage along K
   const int nk = K / C::BK;
   if (nk <= 0) return;  // empty K: D = 0
@@ -448,7 +473,7 @@ __device__ __forceinline__ void gemm_tile_dtl(const uint16_t* a, int64_t lda, in
       if (st < npro) {
 #pragma unroll
         for (int j = 0; j < NL; ++j)
-          dtl_issue_one<C, C::A_INST, C::B_INST>(j, abase + st * KB, ra, bbase + st * KB, rb,
+          dtl_issue_one<C, C::A_INST, C::B_INST>(j, static_cast<uint32_t>(st * KB), ra, rb,
                                                  lds + st * C::STAGE_ELEMS);
       }
     }
@@ -463,14 +488,13 @@ __device__ __forceinline__ void gemm_tile_dtl(const uint16_t* a, int64_t lda, in
   int kt = 0;
   // steady state: stage kt + NS is loaded into stage kt's buffer; NS - 2 later stages stay in flight
   for (; kt + C::NS < nk; ++kt) {
-    const int64_t kbn = static_cast<int64_t>(kt + C::NS) * KB;
-    dtl_kstep<C, true, true>(stage(kt), stage(kt + 1), abase + kbn, ra, bbase + kbn, rb, wm, wn, fa, fb, acc,
-                             C::NS - 2);
+    const uint32_t kbn = static_cast<uint32_t>((kt + C::NS) * KB);
+    dtl_kstep<C, true, true>(stage(kt), stage(kt + 1), kbn, ra, rb, wm, wn, fa, fb, acc, C::NS - 2);
   }
   // drain: no more loads; stages kt + 2 .. nk - 1 are still in flight
   for (; kt + 1 < nk; ++kt)
-    dtl_kstep<C, true, false>(stage(kt), stage(kt + 1), abase, ra, bbase, rb, wm, wn, fa, fb, acc, nk - kt - 2);
-  dtl_kstep<C, false, false>(stage(kt), stage(kt), abase, ra, bbase, rb, wm, wn, fa, fb, acc, 0);
+    dtl_kstep<C, true, false>(stage(kt), stage(kt + 1), 0u, ra, rb, wm, wn, fa, fb, acc, nk - kt - 2);
+  dtl_kstep<C, false, false>(stage(kt), stage(kt), 0u, ra, rb, wm, wn, fa, fb, acc, 0);
   __syncthreads();
 }
 
