@@ -198,20 +198,24 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
 
 
 // ---------------------------------------------------------------------------
-// Fast NT mainloop for K % BK == 0: global -> LDS with global_load_lds_dwordx4
-// (no register staging), XOR-swizzled LDS rows, NS LDS stages, fragment
+// Fast NT mainloop for K % BK == 0: global -> LDS with buffer_load_dwordx4 ...
+// lds (no register staging), XOR-swizzled LDS rows, NS LDS stages, fragment
 // prefetch one K-substep ahead.
 //
 // LDS row = BK bf16 = KC chunks of 16 bytes; the chunk holding logical 16-byte
 // column kc of row r sits at position kc ^ swz(r), so the 32 lanes reading one
 // fragment column (rows r..r+31, same kc) spread over all banks:
 //   BK = 64 (128-byte rows): swz(r) = (r & 7) ^ ((r >> 3) & 1);
-//   BK = 32 (64-byte rows, two rows per 128-byte bank line): swz(r) = (r >> 1) & 3.  Each wave-wide load instruction fills 64 consecutive chunk
-// slots (1 KB), so every lane loads the global chunk that belongs in its slot.
+//   BK = 32 (64-byte rows, two rows per 128-byte bank line): swz(r) = (r >> 1) & 3.
+// Each wave-wide load instruction fills 64 consecutive chunk slots (1 KB), so
+// every lane loads the global chunk that belongs in its slot.
 // Rows past the valid range are clamped to the last valid row (their results
 // are discarded by the caller); K must be a multiple of BK.
 // ---------------------------------------------------------------------------
 
+#ifndef LP_FRAG_PER_SLOT
+#define LP_FRAG_PER_SLOT 2
+#endif
 #ifndef LP_SCHED_HINTS
 #define LP_SCHED_HINTS 0
 #endif
@@ -348,9 +352,8 @@ __device__ __forceinline__ void dtl_frag_piece(const uint16_t* stage, int kk, in
 // 32-bit offset.  Only the first LW waves load (see DtlCfg::LW).
 template <class C, int NA, int NB>
 __device__ __forceinline__ void dtl_issue_one(int j, uint32_t kbytes, const DtlRows<NA>& ra, const DtlRows<NB>& rb,
-                                              uint16_t* stage) {
-  // the wave index is uniform: keep the LDS destination (M0) in scalar registers
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+                                              uint16_t* stage, int wave) {
+  // `wave` is the uniform (scalar) wave index, so the LDS destination (M0) is scalar arithmetic
   if (j < NA) {
     uint16_t* dst = stage + (j * C::LW + wave) * 64 * 8;
     dtl_load16(ra.rsrc, dst, ra.off[j], kbytes);
@@ -392,24 +395,25 @@ template <class C, bool NEXT, bool NEXT2>
 __device__ __forceinline__ void dtl_kstep(uint16_t* X, uint16_t* Y, uint32_t kb2, const DtlRows<C::A_INST>& ra,
                                           const DtlRows<C::B_INST>& rb, int wm, int wn,
                                           bf16x8_t (&fa)[2][C::MI], bf16x8_t (&fb)[2][C::NI],
-                                          f32x16_t (&acc)[C::MI][C::NI], int pending) {
+                                          f32x16_t (&acc)[C::MI][C::NI], int pending, int wave) {
   constexpr int S = C::BK / 16;
   constexpr int NQ = C::MI * C::NI;
   constexpr int NF = C::MI + C::NI;
   constexpr int NL = C::A_INST + C::B_INST;
   static_assert(S % 2 == 0, "substep 0 of every stage must use fragment buffer 0");
-  static_assert(NF <= 2 * NQ, "not enough MFMA slots to interleave fragment reads");
-  const bool loader = C::LW == C::NW || (threadIdx.x >> 6) < C::LW;  // compile-time true when every wave loads
+  constexpr int PER = LP_FRAG_PER_SLOT;  // fragment reads between two MFMAs
+  static_assert(NF <= PER * NQ, "not enough MFMA slots to interleave fragment reads");
+  const bool loader = C::LW == C::NW || wave < C::LW;  // scalar test; compile-time true when every wave loads
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     const int cur = s & 1;
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
-      // fragment reads of the next substep, two per MFMA slot from the start
+      // fragment reads of the next substep, PER per MFMA slot from the start
       // of the substep, so they have most of it to land
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int f = 2 * q + u;
+      for (int u = 0; u < PER; ++u) {
+        const int f = PER * q + u;
         if (f < NF) {
           if (s + 1 < S)
             dtl_frag_piece<C>(X, (s + 1) * 16, wm, wn, f, fa[cur ^ 1], fb[cur ^ 1]);
@@ -422,7 +426,7 @@ __device__ __forceinline__ void dtl_kstep(uint16_t* X, uint16_t* Y, uint32_t kb2
 #pragma unroll
         for (int u = 0; u < (NL + NQ - 1) / NQ; ++u) {
           const int j = q * ((NL + NQ - 1) / NQ) + u;
-          if (j < NL) dtl_issue_one<C, C::A_INST, C::B_INST>(j, kb2, ra, rb, X);
+          if (j < NL) dtl_issue_one<C, C::A_INST, C::B_INST>(j, kb2, ra, rb, X, wave);
         }
       }
       const int mi = q / C::NI, ni = q % C::NI;
@@ -447,7 +451,7 @@ __device__ __forceinline__ void gemm_tile_dtl(const uint16_t* a, int64_t lda, in
                                               f32x16_t (&acc)[C::MI][C::NI]) {
   constexpr int NF = C::MI + C::NI;
   constexpr int NL = C::A_INST + C::B_INST;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar registers
   const int wm = wave % C::WGM, wn = wave / C::WGM;
 #pragma unroll
   for (int mi = 0; mi < C::MI; ++mi)
@@ -467,14 +471,14 @@ __device__ __forceinline__ void gemm_tile_dtl(const uint16_t* a, int64_t lda, in
   if (nk <= 0) return;  // empty K: D = 0
   // prologue: the first min(NS, nk) stages in flight, wait for stage 0, read its first fragments
   const int npro = nk < C::NS ? nk : C::NS;
-  if (C::LW == C::NW || (threadIdx.x >> 6) < C::LW) {
+  if (C::LW == C::NW || wave < C::LW) {
 #pragma unroll
     for (int st = 0; st < C::NS; ++st) {
       if (st < npro) {
 #pragma unroll
         for (int j = 0; j < NL; ++j)
           dtl_issue_one<C, C::A_INST, C::B_INST>(j, static_cast<uint32_t>(st * KB), ra, rb,
-                                                 lds + st * C::STAGE_ELEMS);
+                                                 lds + st * C::STAGE_ELEMS, wave);
       }
     }
     dtl_wait_vm<C>(npro - 1);
@@ -489,12 +493,12 @@ __device__ __forceinline__ void gemm_tile_dtl(const uint16_t* a, int64_t lda, in
   // steady state: stage kt + NS is loaded into stage kt's buffer; NS - 2 later stages stay in flight
   for (; kt + C::NS < nk; ++kt) {
     const uint32_t kbn = static_cast<uint32_t>((kt + C::NS) * KB);
-    dtl_kstep<C, true, true>(stage(kt), stage(kt + 1), kbn, ra, rb, wm, wn, fa, fb, acc, C::NS - 2);
+    dtl_kstep<C, true, true>(stage(kt), stage(kt + 1), kbn, ra, rb, wm, wn, fa, fb, acc, C::NS - 2, wave);
   }
   // drain: no more loads; stages kt + 2 .. nk - 1 are still in flight
   for (; kt + 1 < nk; ++kt)
-    dtl_kstep<C, true, false>(stage(kt), stage(kt + 1), 0u, ra, rb, wm, wn, fa, fb, acc, nk - kt - 2);
-  dtl_kstep<C, false, false>(stage(kt), stage(kt), 0u, ra, rb, wm, wn, fa, fb, acc, 0);
+    dtl_kstep<C, true, false>(stage(kt), stage(kt + 1), 0u, ra, rb, wm, wn, fa, fb, acc, nk - kt - 2, wave);
+  dtl_kstep<C, false, false>(stage(kt), stage(kt), 0u, ra, rb, wm, wn, fa, fb, acc, 0, wave);
   __syncthreads();
 }
 

@@ -47,6 +47,10 @@ using FwdCfg = GemmCfg<LP_FWD_TILE>;
 #ifndef LP_FWD_RS
 #define LP_FWD_RS 0
 #endif
+// Minimum waves per SIMD the forward tile is compiled for (register budget).
+#ifndef LP_FWD_MIN_WAVES
+#define LP_FWD_MIN_WAVES 1
+#endif
 #if LP_FWD_RS
 using FwdDtlCfg = RsCfg<256, 256, 2, 2>;
 #define LP_FWD_MAINLOOP gemm_tile_rs
@@ -319,7 +323,7 @@ __global__ void __launch_bounds__(C::NT) k_fwd_tile(FwdArgs a) {
 
 // Fast forward tile (h % 64 == 0): direct-to-LDS loads, 256 x 256 block.
 template <class C>
-__global__ void __launch_bounds__(C::NT) k_fwd_tile_dtl(FwdArgs a) {
+__global__ void __launch_bounds__(C::NT, LP_FWD_MIN_WAVES) k_fwd_tile_dtl(FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t lds[C::LDS_ELEMS];
   int vb, nb;
   tile_coords(xcd_remap(blockIdx.x, a.n_vb * a.n_nb), a.n_vb, a.n_nb, vb, nb);
