@@ -355,6 +355,8 @@ def bench_kl_lm_head(lp, torch, np, synth, O, steps, warmup):
         roofline=dict(bound="mfma", kernel="k_kl_tile", achieved=achieved, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
                       frac=achieved / BF16_PEAK_TFLOPS, traffic=measured_traffic("k_kl_tile"),
                       traffic_unit="HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                      algorithmic_hbm_bytes_per_launch=(-(-cfg.T // cfg.tile_rows) * cfg.V * 2 * cfg.h * 2
+                                                        + cfg.T * 2 * cfg.h * 2) / (n_launch / steps),
                       launches_per_step=n_launch / steps, algorithmic_flop_per_step=flop_fwd,
                       algorithmic_flop_per_launch=flop_fwd / (n_launch / steps)),
         fwd_bwd=dict(ms_per_step=ms_b / bsteps, tokens_per_s=cfg.T * bsteps / (ms_b * 1e-3),
