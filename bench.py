@@ -177,9 +177,9 @@ def _cpu_baseline_lm_head(O, np, A, cfg, scored, seconds):
         t0 = time.perf_counter()
         O.lm_head_logprobs_entropy(O.widen_bf16(A["hidden"][rows]), W, A["targets"][rows], None, cfg.temperature)
         t = time.perf_counter() - t0
-        if t >= seconds / 3 or n >= len(scored):
+        if t >= 0.6 * seconds or n >= len(scored):
             break
-        n = min(len(scored), int(n * max(2.0, seconds / 3 / max(t, 1e-3))))
+        n = min(len(scored), int(n * min(8.0, max(2.0, seconds / max(t, 1e-3)))))
     return dict(value=n / t, unit="scored tokens/s", cores=_blas_threads(), kind="oracle",
                 sample=f"{n} scored rows of the same workload through the fp64 oracle (full V={cfg.V}, h={cfg.h})",
                 seconds=t, cpu_model=_cpu_model())
