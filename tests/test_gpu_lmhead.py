@@ -284,3 +284,39 @@ def test_fused_matches_logits_path_on_fp32_logits(h, tau):
                                                      to_dev(m), tau, tile)
     lp_l, H_l = _lp().lp_logprobs_entropy(to_dev(Z), to_dev(y), to_dev(m), tau)
     assert max_abs_err(host(lp_f), host(lp_l)) <= 2e-5 and max_abs_err(host(H_f), host(H_l)) <= 2e-5
+
+
+@pytest.mark.timeout(600)
+def test_hidden_past_4_gib_takes_generic_tiles():
+    """Maximum-size case: hidden rows whose byte offsets pass 2^32 (T = 262200,
+    h = 8192, 4.3 GB of bf16) exceed the fast tiles' 32-bit offsets, so forward
+    and backward take the generic tiles; scored rows around the 4 GiB boundary
+    and the last row are checked against the oracle."""
+    torch = _torch()
+    T, h, V, tile, tau = 262200, 8192, 777, 32, 0.7
+    rng = np.random.default_rng(99)
+    rows = np.unique(np.concatenate([[0, 262143, 262144, 262145, T - 1], rng.choice(T, 40, replace=False)]))
+    hid_rows = synth.f32_to_bf16_bits(rng.normal(0, 1, size=(len(rows), h)).astype(np.float32))
+    W = synth.f32_to_bf16_bits(rng.normal(0, 0.02, size=(V, h)).astype(np.float32))
+    y = rng.integers(0, V, size=T).astype(np.int64)
+    mask = np.zeros(T, dtype=np.uint8)
+    mask[rows] = 1
+    g = rng.normal(0, 1, size=T).astype(np.float32)
+    gH = rng.normal(0, 0.1, size=T).astype(np.float32)
+    hd = torch.zeros((T, h), dtype=torch.bfloat16, device="cuda")
+    hd[torch.as_tensor(rows).cuda()] = to_dev_bits(hid_rows, "bf16")
+    Wd = to_dev_bits(W, "bf16")
+    lp, H, lse = _lp().lp_lm_head_logprobs_entropy(hd, Wd, to_dev(y), to_dev(mask), tau, tile)
+    lp_o, H_o, _ = O.lm_head_logprobs_entropy(O.widen_bf16(hid_rows), O.widen_bf16(W), y[rows], None, tau)
+    lph, Hh = host(lp), host(H)
+    assert max_abs_err(lph[rows], lp_o) <= TOL_FWD and max_abs_err(Hh[rows], H_o) <= TOL_FWD
+    assert not lph[mask == 0].any()
+    dH, dW = _lp().lp_lm_head_logprobs_entropy_backward(hd, Wd, to_dev(y), to_dev(mask), tau, tile, lse, H,
+                                                        to_dev(g), to_dev(gH))
+    dH_o, dW_o = O.lm_head_backward(O.widen_bf16(hid_rows), O.widen_bf16(W), y[rows], None, tau, g[rows], gH[rows])
+    got_rows = dH[torch.as_tensor(rows).cuda()].cpu().numpy()
+    for nm, got, want in (("dH", got_rows, dH_o), ("dW", host(dW), dW_o)):
+        fro, mad = grad_errors(got, want)
+        assert fro <= TOL_GRAD and mad <= TOL_GRAD, (nm, fro, mad)
+    nonzero_rows = (dH != 0).any(dim=1).cpu().numpy()
+    assert not nonzero_rows[mask == 0].any()

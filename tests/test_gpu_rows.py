@@ -255,3 +255,24 @@ def test_prob_diff_elementwise():
     got = host(_lp().lp_prob_diff(to_dev(a), to_dev(b), to_dev(m)))
     assert max_abs_err(got, O.prob_diff(a.astype(np.float64), b.astype(np.float64), m)) <= 1e-6
     assert np.all(host(_lp().lp_prob_diff(to_dev(a), to_dev(b), to_dev(np.zeros(n, np.uint8)))) == 0)
+
+
+@pytest.mark.timeout(600)
+def test_logits_past_4_gib():
+    """Maximum-size case for the logits path: bf16 logits [30000, 151936]
+    (9.1 GB), scored rows on both sides of the 4 GiB byte offset, in chunks."""
+    import torch
+    T, V = 30000, 151936
+    rng = np.random.default_rng(98)
+    rows = np.array([0, 14130, 14136, 14137, 20000, T - 1])
+    vals = synth.f32_to_bf16_bits(rng.normal(0, 3, size=(len(rows), V)).astype(np.float32))
+    y = rng.integers(0, V, size=T).astype(np.int64)
+    mask = np.zeros(T, dtype=np.uint8)
+    mask[rows] = 1
+    x = torch.zeros((T, V), dtype=torch.bfloat16, device="cuda")
+    x[torch.as_tensor(rows).cuda()] = to_dev_bits(vals, "bf16")
+    lp, H = _lp().lp_logprobs_entropy(x, to_dev(y), to_dev(mask), 0.7, 8192)
+    lp_o, H_o = O.logprobs_entropy(O.widen_bf16(vals), y[rows], None, 0.7)[:2]
+    lph, Hh = host(lp), host(H)
+    assert max_abs_err(lph[rows], lp_o) <= TOL and max_abs_err(Hh[rows], H_o) <= TOL
+    assert not lph[mask == 0].any() and not Hh[mask == 0].any()
