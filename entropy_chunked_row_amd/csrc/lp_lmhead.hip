@@ -229,14 +229,14 @@ __device__ __forceinline__ void fwd_epilogue(const FwdArgs& a, f32x16_t (&acc)[C
     const int64_t row = valid_row ? a.idx[a.tile_base + r] : 0;
     Stat st = stat_empty();
     if (full_block) {
-      // every vocab row of this block exists: plain fold
+      // every vocab row of this block exists: one fold over all of this
+      // lane's values of the row (one max, no rebase)
+      float x[C::MI * 16];
 #pragma unroll
-      for (int mi = 0; mi < C::MI; ++mi) {
-        float x[16];
+      for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) x[i] = acc[mi][ni][i];
-        stat_push<false, 16, 16>(st, x, c);
-      }
+        for (int i = 0; i < 16; ++i) x[mi * 16 + i] = acc[mi][ni][i];
+      stat_push<false, C::MI * 16, 16>(st, x, c);
     } else {
 #pragma unroll
       for (int mi = 0; mi < C::MI; ++mi) {
