@@ -66,9 +66,15 @@ using BwdCfg = GemmCfg<LP_BWD_TILE>;
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_pk_t __attribute__((ext_vector_type(2)));
+
+// Four fp32 values -> four bf16 (nearest even) packed in 8 bytes, with the
+// hardware pair conversion.
+__device__ __forceinline__ uint2 pack_bf16x4(const float (&d)[4]) {
+  const bf16x2_pk_t lo = __builtin_convertvector(f32x2_t{d[0], d[1]}, bf16x2_pk_t);
+  const bf16x2_pk_t hi = __builtin_convertvector(f32x2_t{d[2], d[3]}, bf16x2_pk_t);
+  return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
 }
 
 // Logical tile -> (vocab block, token block): groups of kGroupV vocab blocks
@@ -540,70 +546,127 @@ struct DzArgs {
 
 // Four consecutive vocab columns vq..vq+3 of tile row r: one 8-byte store
 // into dZ [row][vocab] and, if requested, four 2-byte stores into dZ^T.
+__device__ __forceinline__ void dzt_store4(uint16_t* dzt, int64_t tpad, int r, int vq, uint2 pk) {
+  dzt[static_cast<int64_t>(vq) * tpad + r] = static_cast<uint16_t>(pk.x);
+  dzt[static_cast<int64_t>(vq + 1) * tpad + r] = static_cast<uint16_t>(pk.x >> 16);
+  dzt[static_cast<int64_t>(vq + 2) * tpad + r] = static_cast<uint16_t>(pk.y);
+  dzt[static_cast<int64_t>(vq + 3) * tpad + r] = static_cast<uint16_t>(pk.y >> 16);
+}
+
 __device__ __forceinline__ void dz_store4(uint16_t* dz, uint16_t* dzt, int64_t vpad, int64_t tpad, int r, int vq,
-                                          const uint16_t (&outv)[4]) {
-  uint2 pk;
-  pk.x = static_cast<uint32_t>(outv[0]) | (static_cast<uint32_t>(outv[1]) << 16);
-  pk.y = static_cast<uint32_t>(outv[2]) | (static_cast<uint32_t>(outv[3]) << 16);
+                                          uint2 pk) {
   *reinterpret_cast<uint2*>(dz + static_cast<int64_t>(r) * vpad + vq) = pk;
-  if (dzt) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dzt[static_cast<int64_t>(vq + j) * tpad + r] = outv[j];
+  if (dzt) dzt_store4(dzt, tpad, r, vq, pk);
+}
+
+// Staged dZ rows: the fast kernels first write their tile of dZ [rows][vocab]
+// to LDS with a row pitch of BM + 4 elements (consecutive tile rows then fall
+// in different banks for the 8-byte writes of one MFMA column), then copy
+// whole rows out with 16-byte stores, so every 32 lanes write 512 contiguous
+// bytes instead of 32 scattered 8-byte pieces.
+template <class C>
+struct DzStage {
+  static constexpr int P = C::BM + 4;
+  static constexpr int ELEMS = C::BN * P;
+};
+
+__device__ __forceinline__ void dz_stage4(uint16_t* lds, int pitch, int r_local, int v_local, uint2 pk) {
+  *reinterpret_cast<uint2*>(lds + r_local * pitch + v_local) = pk;
+}
+
+// Copies the staged rows [0, nrow) of the tile (vocab columns v0 + [0, BM),
+// clipped to vpad) to dZ [row][vocab].  Needs a barrier before (all staged
+// writes done); LDS is not reused afterwards.
+template <class C>
+__device__ __forceinline__ void dz_flush_rows(const uint16_t* lds, uint16_t* dz, int64_t vpad, int v0, int n0,
+                                              int nrow) {
+  constexpr int P = DzStage<C>::P;
+  constexpr int NCH = C::BM / 8;  // 16-byte chunks per row
+  for (int idx = threadIdx.x; idx < nrow * NCH; idx += C::NT) {
+    const int r = idx / NCH, ch = idx % NCH;
+    const int v = v0 + ch * 8;
+    if (v >= vpad) continue;
+    const uint2 lo = *reinterpret_cast<const uint2*>(lds + r * P + ch * 8);
+    const uint2 hi = *reinterpret_cast<const uint2*>(lds + r * P + ch * 8 + 4);
+    *reinterpret_cast<uint4*>(dz + static_cast<int64_t>(n0 + r) * vpad + v) = make_uint4(lo.x, lo.y, hi.x, hi.y);
   }
 }
 
 // dL/dlogits epilogue: for tile rows r < rowsK (the K span of the
 // weight-gradient GEMM; rows past the tile's valid rows get 0) and vocab
 // columns v < vpad (0 past V), writes bf16 dZ[r][v] and, if requested, dZ^T[v][r].
-template <class C>
+template <class C, bool STAGED>
 __device__ __forceinline__ void dz_epilogue(const DzArgs& a, f32x16_t (&acc)[C::MI][C::NI], int v0, int n0, int rows,
-                                            int rowsK) {
+                                            int rowsK, uint16_t* lds) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave % C::WGM, wn = wave / C::WGM;
   const int vlane = v0 + wm * C::WTM + 4 * (lane >> 5);
+  const bool full_block = v0 + C::BM <= a.V;  // uniform: every vocab column of the block exists
+  const float it = a.inv_tau;
 #pragma unroll
   for (int ni = 0; ni < C::NI; ++ni) {
     const int r = n0 + wn * C::WTN + ni * 32 + (lane & 31);
     if (r >= rowsK) continue;
     const bool valid = r < rows;
+    // dZ = it * [sum_k g_k onehot_k - p (gsum + gH (z it - mu))] = it * sum_k g_k onehot_k - p (A + B z)
     int64_t row = 0, y0 = -1;
-    float l2 = 0.f, mu = 0.f, g0 = 0.f, gsum = 0.f, gh = 0.f;
+    float l2 = 0.f, A = 0.f, B = 0.f, g0 = 0.f;
     if (valid) {
       row = a.idx[a.tile_base + r];
       const float L = a.lse[row];
       l2 = L * kLog2eF;
-      mu = L - a.entropy[row];
+      const float mu = L - a.entropy[row];
       y0 = a.targets[row * a.K];
       g0 = a.g_lp[row * a.K];
-      gsum = g0;
+      float gsum = g0;
       for (int k = 1; k < a.K; ++k) gsum += a.g_lp[row * a.K + k];
-      gh = a.g_H ? a.g_H[row] : 0.f;
+      const float gh = a.g_H ? a.g_H[row] : 0.f;
+      A = it * fmaf(-gh, mu, gsum);
+      B = it * it * gh;
     }
 #pragma unroll
     for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int vq = vlane + mi * 32 + 8 * q;
-        uint16_t outv[4];
+        float d[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int v = vq + j;
-          float d = 0.f;
-          if (valid && v < a.V) {
-            // sum of g_lp over the row's targets that sit in this column (usually none)
-            float onehot = (v == y0) ? g0 : 0.f;
-            for (int k = 1; k < a.K; ++k)
-              if (a.targets[row * a.K + k] == v) onehot += a.g_lp[row * a.K + k];
-            const float z = acc[mi][ni][q * 4 + j];
-            const float p = fast_exp2(fmaf(z, a.c, -l2));
-            const float zt = z * a.inv_tau;
-            d = a.inv_tau * (onehot - gsum * p - gh * p * (zt - mu));
-          }
-          outv[j] = f32_to_bf16_rne(d);
+          const float z = acc[mi][ni][q * 4 + j];
+          const float p = fast_exp2(fmaf(z, a.c, -l2));
+          d[j] = valid ? -p * fmaf(B, z, A) : 0.f;
+          if (!full_block && vq + j >= a.V) d[j] = 0.f;
         }
-        if (vq < a.vpad) dz_store4(a.dz, a.dzt, a.vpad, a.tpad, r, vq, outv);
+        if (valid) {
+          // the row's targets inside these four columns (usually none)
+          const int64_t y0rel = y0 - vq;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (y0rel == j) d[j] += it * g0;
+          for (int k = 1; k < a.K; ++k) {
+            const int64_t yrel = a.targets[row * a.K + k] - vq;
+            if (yrel >= 0 && yrel < 4) {
+              const float gk = it * a.g_lp[row * a.K + k];
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+                if (yrel == j) d[j] += gk;
+            }
+          }
+        }
+        const uint2 pk = pack_bf16x4(d);
+        if (STAGED) {
+          dz_stage4(lds, DzStage<C>::P, r - n0, vq - v0, pk);
+          if (a.dzt && vq < a.vpad) dzt_store4(a.dzt, a.tpad, r, vq, pk);
+        } else if (vq < a.vpad) {
+          dz_store4(a.dz, a.dzt, a.vpad, a.tpad, r, vq, pk);
+        }
       }
+  }
+  if (STAGED) {
+    __syncthreads();
+    const int nrow = (rowsK - n0) < C::BN ? (rowsK - n0) : C::BN;
+    dz_flush_rows<C>(lds, a.dz, a.vpad, v0, n0, nrow);
   }
 }
 
@@ -631,7 +694,7 @@ __global__ void __launch_bounds__(C::NT) k_bwd_dz(DzArgs a) {
   op.K = a.h;
   f32x16_t acc[C::MI][C::NI];
   gemm_tile<C>(op, 0, 0, lds, acc);
-  dz_epilogue<C>(a, acc, v0, n0, rows, rowsK);
+  dz_epilogue<C, false>(a, acc, v0, n0, rows, rowsK, lds);
 }
 
 // Fast recompute tile (h % 64 == 0): the forward's direct-to-LDS mainloop.
@@ -639,7 +702,8 @@ __global__ void __launch_bounds__(C::NT) k_bwd_dz(DzArgs a) {
 // because the fast weight-gradient GEMM takes K in steps of 64.
 template <class C>
 __global__ void __launch_bounds__(C::NT) k_bwd_dz_dtl(DzArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[C::LDS_ELEMS];
+  constexpr int kLds = C::LDS_ELEMS > DzStage<C>::ELEMS ? C::LDS_ELEMS : DzStage<C>::ELEMS;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[kLds];
   int vb, nb;
   tile_coords(xcd_remap(blockIdx.x, a.n_vb * a.n_nb), a.n_vb, a.n_nb, vb, nb);
   const int count = *a.count;
@@ -652,7 +716,7 @@ __global__ void __launch_bounds__(C::NT) k_bwd_dz_dtl(DzArgs a) {
   f32x16_t acc[C::MI][C::NI];
   LP_FWD_MAINLOOP<C>(a.weight + static_cast<int64_t>(v0) * a.ld_w, a.ld_w, a.V - v0, a.hidden, a.ld_h,
                    a.idx + a.tile_base + n0, rows - n0, a.h, lds, acc);
-  dz_epilogue<C>(a, acc, v0, n0, rows, rowsK);
+  dz_epilogue<C, true>(a, acc, v0, n0, rows, rowsK, lds);
 }
 
 // Fast gradient GEMMs on dense K-contiguous operands (K multiple of 64):
@@ -1417,9 +1481,10 @@ struct KLDzArgs {
   uint16_t* dzt;
 };
 
-template <class C>
+template <class C, bool STAGED>
 __device__ __forceinline__ void kl_dz_epilogue(const KLDzArgs& a, f32x16_t (&accu)[C::MI][C::NI],
-                                               f32x16_t (&accv)[C::MI][C::NI], int v0, int n0, int rows, int rowsK) {
+                                               f32x16_t (&accv)[C::MI][C::NI], int v0, int n0, int rows, int rowsK,
+                                               uint16_t* lds) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave % C::WGM, wn = wave / C::WGM;
@@ -1442,7 +1507,7 @@ __device__ __forceinline__ void kl_dz_epilogue(const KLDzArgs& a, f32x16_t (&acc
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int vq = vlane + mi * 32 + 8 * q;
-        uint16_t outv[4];
+        float dv[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           float d = 0.f;
@@ -1451,10 +1516,21 @@ __device__ __forceinline__ void kl_dz_epilogue(const KLDzArgs& a, f32x16_t (&acc
             const float pv = fast_exp2(fmaf(accv[mi][ni][q * 4 + j], c, -lv));
             d = g * (pu - pv);
           }
-          outv[j] = f32_to_bf16_rne(d);
+          dv[j] = d;
         }
-        if (vq < a.vpad) dz_store4(a.dz, a.dzt, a.vpad, a.tpad, r, vq, outv);
+        const uint2 pk = pack_bf16x4(dv);
+        if (STAGED) {
+          dz_stage4(lds, DzStage<C>::P, r - n0, vq - v0, pk);
+          if (a.dzt && vq < a.vpad) dzt_store4(a.dzt, a.tpad, r, vq, pk);
+        } else if (vq < a.vpad) {
+          dz_store4(a.dz, a.dzt, a.vpad, a.tpad, r, vq, pk);
+        }
       }
+  }
+  if (STAGED) {
+    __syncthreads();
+    const int nrow = (rowsK - n0) < C::BN ? (rowsK - n0) : C::BN;
+    dz_flush_rows<C>(lds, a.dz, a.vpad, v0, n0, nrow);
   }
 }
 
@@ -1483,12 +1559,13 @@ __global__ void __launch_bounds__(C::NT) k_kl_dz(KLDzArgs a) {
   op.ldb = a.h.ld_hs;
   op.K = a.h.h_s;
   gemm_tile<C>(op, 0, 0, lds, accu);
-  kl_dz_epilogue<C>(a, accu, accv, v0, n0, rows, rowsK);
+  kl_dz_epilogue<C, false>(a, accu, accv, v0, n0, rows, rowsK, lds);
 }
 
 template <class C>
 __global__ void __launch_bounds__(C::NT) k_kl_dz_dtl(KLDzArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[C::LDS_ELEMS];
+  constexpr int kLds = C::LDS_ELEMS > DzStage<C>::ELEMS ? C::LDS_ELEMS : DzStage<C>::ELEMS;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[kLds];
   int vb, n0, rows;
   kl_block(a.h.n_vb, a.h.n_nb, a.h.count, a.h.tile_base, a.h.tile_rows, C::BN, vb, n0, rows);
   const int rowsK = (rows + 63) & ~63;
@@ -1500,7 +1577,7 @@ __global__ void __launch_bounds__(C::NT) k_kl_dz_dtl(KLDzArgs a) {
                    rows - n0, a.h.h_t, lds, accv);
   gemm_tile_dtl<C>(a.h.ws + static_cast<int64_t>(v0) * a.h.ld_ws, a.h.ld_ws, a.h.V - v0, a.h.hs, a.h.ld_hs, brows,
                    rows - n0, a.h.h_s, lds, accu);
-  kl_dz_epilogue<C>(a, accu, accv, v0, n0, rows, rowsK);
+  kl_dz_epilogue<C, true>(a, accu, accv, v0, n0, rows, rowsK, lds);
 }
 
 hipError_t launch_lmhead_kl_backward(const LMHeadShape& sh, const LMHeadShape& te, const float* lse_student,
