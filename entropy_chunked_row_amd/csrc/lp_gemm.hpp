@@ -221,7 +221,6 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
 #endif
 
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) const void gbl_void_t;
 
 template <int BM_, int BN_, int WGM_, int WGN_, int BK_ = 64, int NS_ = 2>
 struct DtlCfg {

@@ -544,8 +544,8 @@ struct DzArgs {
   uint16_t* dzt;  // [vpad][tpad] or nullptr
 };
 
-// Four consecutive vocab columns vq..vq+3 of tile row r: one 8-byte store
-// into dZ [row][vocab] and, if requested, four 2-byte stores into dZ^T.
+// Four consecutive vocab columns vq..vq+3 of tile row r, packed bf16 in pk:
+// four 2-byte stores into dZ^T [vocab][row] ...
 __device__ __forceinline__ void dzt_store4(uint16_t* dzt, int64_t tpad, int r, int vq, uint2 pk) {
   dzt[static_cast<int64_t>(vq) * tpad + r] = static_cast<uint16_t>(pk.x);
   dzt[static_cast<int64_t>(vq + 1) * tpad + r] = static_cast<uint16_t>(pk.x >> 16);
@@ -553,6 +553,7 @@ __device__ __forceinline__ void dzt_store4(uint16_t* dzt, int64_t tpad, int r, i
   dzt[static_cast<int64_t>(vq + 3) * tpad + r] = static_cast<uint16_t>(pk.y >> 16);
 }
 
+// ... and one 8-byte store into dZ [row][vocab] (plus dZ^T if requested).
 __device__ __forceinline__ void dz_store4(uint16_t* dz, uint16_t* dzt, int64_t vpad, int64_t tpad, int r, int vq,
                                           uint2 pk) {
   *reinterpret_cast<uint2*>(dz + static_cast<int64_t>(r) * vpad + vq) = pk;
