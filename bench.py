@@ -8,9 +8,12 @@ entropy of softmax(hidden @ W^T / 0.7)) on T = 32768 packed rows (about 70 %
 scored), h = 5120, V = 151936, bf16, tile 4096 rows.  One step is one call of
 lp_lm_head_logprobs_entropy with inputs already resident in HBM.  The same
 JSON line carries the other paths of the hot path measured the same way
-(logits-input rows, exact KL + prob diff, fused forward + backward), the
-roofline of the dominant kernel from live per-launch HIP-event timing, and
-the fp64 oracle timed on the host cores over a bounded sample.
+(logits-input rows, exact KL + prob diff, fused forward + backward, KL through
+both heads), the roofline of the dominant kernel from live per-launch
+HIP-event timing, and the fp64 oracle timed on the host cores over a bounded
+sample.  Each path runs its step untimed for --settle-seconds (steady GPU
+clocks after the host-side input generation), then W warm-up steps, then
+exactly K timed steps.
 
 Inputs are seeded and synthetic (see synth/); the oracle is used only for the
 CPU-baseline leg and a sampled parity check of every path.
@@ -90,7 +93,18 @@ def _events_ms(torch, fn, steps):
     return a.elapsed_time(b)
 
 
+SETTLE_SECONDS = 1.0  # set from --settle-seconds in main()
+
+
 def _timed(lp, torch, fn, steps, warmup, kernels):
+    # Clock settle: the GPU idles while a path's inputs are generated on the
+    # host, and it needs some time under load to reach its steady clocks.  Run
+    # the step untimed for SETTLE_SECONDS first, then the W warm-up steps,
+    # then exactly K timed steps.
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < SETTLE_SECONDS:
+        fn()
+        torch.cuda.synchronize()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -377,6 +391,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--paths", default="all", help="comma list of " + ",".join(ALL_PATHS))
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline (0 = skip)")
+    ap.add_argument("--settle-seconds", type=float, default=1.0,
+                    help="untimed seconds of each path's step before its warm-up steps (steady GPU clocks)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB (reference for HBM counters)")
     args = ap.parse_args()
@@ -385,6 +401,8 @@ def main():
               "(rows shard with no exchange; see DESIGN.md for how the path would shard)", file=sys.stderr)
         sys.exit(2)
     paths = ALL_PATHS if args.paths == "all" else tuple(p.strip() for p in args.paths.split(","))
+    global SETTLE_SECONDS
+    SETTLE_SECONDS = max(0.0, args.settle_seconds)
 
     import numpy as np
     import torch
@@ -436,6 +454,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_seconds": SETTLE_SECONDS,
         "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",

@@ -85,6 +85,15 @@ __global__ void __launch_bounds__(NT) k_logprobs_entropy(RowArgs args) {
   if (threadIdx.x == 0 && args.entropy) args.entropy[row] = (l2s - st.a / st.s) * kLn2;
 }
 
+// Workgroup size and 16-byte loads in flight per lane for rows longer than
+// 16384 (build-time knobs; measured defaults).
+#ifndef LP_ROWS_NT
+#define LP_ROWS_NT 256
+#endif
+#ifndef LP_ROWS_U
+#define LP_ROWS_U 8
+#endif
+
 template <class Tr>
 static hipError_t launch_rows_t(const RowArgs& a, hipStream_t s) {
   const unsigned grid = static_cast<unsigned>(a.rows);
@@ -94,7 +103,7 @@ static hipError_t launch_rows_t(const RowArgs& a, hipStream_t s) {
   } else if (a.V <= 16384) {
     hipLaunchKernelGGL((k_logprobs_entropy<Tr, 128, 4>), dim3(grid), dim3(128), 0, s, a);
   } else {
-    hipLaunchKernelGGL((k_logprobs_entropy<Tr, 256, 4>), dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_logprobs_entropy<Tr, LP_ROWS_NT, LP_ROWS_U>), dim3(grid), dim3(LP_ROWS_NT), 0, s, a);
   }
   return hipGetLastError();
 }
@@ -221,6 +230,12 @@ __global__ void __launch_bounds__(NT) k_kl_full_vocab(KLArgs args) {
   }
 }
 
+// 16-byte loads in flight per lane and per row (student and teacher each)
+// for rows longer than 2048 (build-time knob; measured default).
+#ifndef LP_KL_ROWS_U
+#define LP_KL_ROWS_U 4
+#endif
+
 template <class Tr>
 static hipError_t launch_kl_t(const KLArgs& a, hipStream_t s) {
   const unsigned grid = static_cast<unsigned>(a.T);
@@ -228,7 +243,7 @@ static hipError_t launch_kl_t(const KLArgs& a, hipStream_t s) {
   if (a.V <= 2048) {
     hipLaunchKernelGGL((k_kl_full_vocab<Tr, 64, 2>), dim3(grid), dim3(64), 0, s, a);
   } else {
-    hipLaunchKernelGGL((k_kl_full_vocab<Tr, 256, 2>), dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_kl_full_vocab<Tr, 256, LP_KL_ROWS_U>), dim3(grid), dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }
