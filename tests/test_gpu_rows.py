@@ -276,3 +276,34 @@ def test_logits_past_4_gib():
     lph, Hh = host(lp), host(H)
     assert max_abs_err(lph[rows], lp_o) <= TOL and max_abs_err(Hh[rows], H_o) <= TOL
     assert not lph[mask == 0].any() and not Hh[mask == 0].any()
+
+
+@pytest.mark.parametrize("V", [1, 2, 5, 16])
+@pytest.mark.parametrize("tau", [1.0, 0.7])
+def test_brute_force_adversarial_small_vocab(V, tau):
+    """GPU against the pure-Python brute force (math.fsum softmax, no max
+    shift) on adversarial rows: all equal, two equal maxima, a -inf entry,
+    large magnitudes, and random rows; every target id of every row."""
+    from tests.test_oracle_pins import bf_row
+    rng = np.random.default_rng(V * 10 + int(tau * 10))
+    rows = [np.zeros(V), rng.normal(0, 3, V), np.full(V, 7.5)]
+    if V >= 2:
+        r = rng.normal(0, 1, V)
+        r[0] = r[V - 1] = r.max() + 2.0  # two equal maxima
+        rows.append(r)
+        r = rng.normal(0, 2, V)
+        r[V // 2] = -np.inf
+        rows.append(r)
+        rows.append(rng.uniform(-40, 40, V))
+    Z = np.array(rows, dtype=np.float32)
+    n = Z.shape[0]
+    for y_col in range(V):
+        y = np.full(n, y_col, dtype=np.int64)
+        lp, H = _lp().lp_logprobs_entropy(to_dev(Z), to_dev(y), None, tau)
+        lp, H = host(lp), host(H)
+        for t in range(n):
+            if not np.isfinite(Z[t, y_col]):
+                continue
+            want_lp, want_H = bf_row([float(v) for v in Z[t]], y_col, tau)
+            assert abs(lp[t] - want_lp) <= TOL * max(1.0, abs(want_lp)), (t, y_col, lp[t], want_lp)
+            assert abs(H[t] - want_H) <= TOL, (t, H[t], want_H)
