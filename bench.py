@@ -347,15 +347,23 @@ def bench_kl_lm_head(lp, torch, np, synth, O, steps, warmup):
         out["g"] = lp.lp_lm_head_kl_backward(*heads, None, cfg.tile_rows, out["f"][4], out["f"][5], g,
                                              workspace=wsb)
 
-    ms, kt = _timed(lp, torch, fwd, steps, warmup, ["k_kl_tile", "k_kl_merge"])
-    n_launch, kms = kt["k_kl_tile"]
+    ms, kt = _timed(lp, torch, fwd, steps, warmup, ["k_kl_teacher", "k_kl_student", "k_kl_merge"])
+    n_launch, t_ms = kt["k_kl_teacher"]
+    s_ms = kt["k_kl_student"][1]
+    kms = t_ms + s_ms
     flop_fwd = 2.0 * cfg.T * cfg.V * (cfg.h + cfg.h)
     achieved = flop_fwd * steps / (kms * 1e-3) / 1e12
+    chunks = n_launch / steps  # row chunks per forward: one teacher and one student launch each
+    chunk_rows = cfg.T / chunks
+    # per chunk and pass: one model's weight once, the chunk's hidden rows, the chunk's fp32 teacher logits
+    # (written by the teacher pass, read by the student pass)
+    pass_bytes = cfg.V * cfg.h * 2 + chunk_rows * cfg.h * 2 + chunk_rows * cfg.V * 4
     bsteps = max(1, steps // 5)
-    bkernels = ["k_kl_tile", "k_kl_dz", "k_out_gemm_dhidden", "k_out_gemm_dweight", "k_transpose_bf16"]
+    bkernels = ["k_kl_teacher", "k_kl_student", "k_kl_dz", "k_out_gemm_dhidden", "k_out_gemm_dweight",
+                "k_transpose_bf16"]
     ms_b, kt_b = _timed(lp, torch, fwd_bwd, bsteps, min(1, warmup), bkernels)
     flop_fb = flop_fwd * 2 + 4.0 * cfg.T * cfg.V * cfg.h
-    mfma_ms = sum(kt_b[k][1] for k in bkernels[:4])
+    mfma_ms = sum(kt_b[k][1] for k in bkernels[:5])
     achieved_b = flop_fb * bsteps / (mfma_ms * 1e-3) / 1e12
     kl = out["f"][0].cpu().numpy()
     rows = np.array([0, cfg.T // 2, cfg.T - 1])
@@ -366,13 +374,16 @@ def bench_kl_lm_head(lp, torch, np, synth, O, steps, warmup):
         workload=f"KL(teacher||student) with logits rebuilt through both heads: T={cfg.T} rows, "
                  f"h_student=h_teacher={cfg.h}, V={cfg.V}, bf16, tile {cfg.tile_rows}, + target lps and prob diff",
         ms_per_step=ms / steps, tokens_per_s=cfg.T * steps / (ms * 1e-3),
-        roofline=dict(bound="mfma", kernel="k_kl_tile", achieved=achieved, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                      frac=achieved / BF16_PEAK_TFLOPS, traffic=measured_traffic("k_kl_tile"),
+        roofline=dict(bound="mfma", kernel="k_kl_teacher + k_kl_student", achieved=achieved,
+                      peak=BF16_PEAK_TFLOPS, unit="TFLOP/s", frac=achieved / BF16_PEAK_TFLOPS,
+                      traffic=measured_traffic("k_kl_student"),
+                      traffic_kernel="k_kl_student",
                       traffic_unit="HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-                      algorithmic_hbm_bytes_per_launch=(-(-cfg.T // cfg.tile_rows) * cfg.V * 2 * cfg.h * 2
-                                                        + cfg.T * 2 * cfg.h * 2) / (n_launch / steps),
+                      traffic_teacher=measured_traffic("k_kl_teacher"),
+                      algorithmic_hbm_bytes_per_launch=pass_bytes,
                       launches_per_step=n_launch / steps, algorithmic_flop_per_step=flop_fwd,
-                      algorithmic_flop_per_launch=flop_fwd / (n_launch / steps)),
+                      algorithmic_flop_per_launch=flop_fwd / 2 / chunks,
+                      teacher_ms_per_launch=t_ms / n_launch, student_ms_per_launch=s_ms / n_launch),
         fwd_bwd=dict(ms_per_step=ms_b / bsteps, tokens_per_s=cfg.T * bsteps / (ms_b * 1e-3),
                      roofline=dict(bound="mfma", kernel="all MFMA GEMMs (2 fwd + 2 recompute + dHidden + dW)",
                                    achieved=achieved_b, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",

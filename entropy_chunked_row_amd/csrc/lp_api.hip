@@ -262,7 +262,7 @@ lp_status lp_lm_head_logprobs_entropy_backward_k(const void* hidden, int64_t ld_
 
 size_t lp_lm_head_kl_workspace_bytes(int64_t T, int64_t h_student, int64_t V, int64_t tile_rows, int backward) {
   lp::LMHeadWorkspace w;
-  if (!lp::lmhead_workspace_layout(T, h_student, V, tile_rows, backward ? 1 : 2, &w)) return 0;
+  if (!lp::lmhead_workspace_layout(T, h_student, V, tile_rows, backward ? 3 : 2, &w)) return 0;
   return w.total;
 }
 
@@ -292,7 +292,7 @@ static lp_status check_kl_heads(const char* fn, const void* hs, int64_t ld_hs, c
   lp_status st = check_head(fn, "student", hs, ld_hs, ws_, ld_ws, h_s);
   if (st != LP_OK) return st;
   if ((st = check_head(fn, "teacher", ht, ld_ht, wt, ld_wt, h_t)) != LP_OK) return st;
-  if (!lp::lmhead_workspace_layout(T, h_s, V, tile_rows, backward ? 1 : 2, w))
+  if (!lp::lmhead_workspace_layout(T, h_s, V, tile_rows, backward ? 3 : 2, w))
     return fail(LP_ERR_INVALID_ARGUMENT, "%s: sizes overflow the workspace layout", fn);
   if (!workspace || workspace_bytes < w->total)
     return fail(LP_ERR_WORKSPACE_TOO_SMALL, "%s: workspace needs %zu bytes, got %zu", fn, w->total,

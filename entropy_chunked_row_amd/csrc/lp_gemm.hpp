@@ -20,6 +20,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace lp {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -243,6 +245,15 @@ struct DtlCfg {
   static constexpr int B_INST = BN * KC / 64 / LW;
   static constexpr int STAGE_ELEMS = (BM + BN) * BK;
   static constexpr int LDS_ELEMS = NS * STAGE_ELEMS;
+  // B fragments reloaded in place after their last use (one register set
+  // instead of two) when the accumulators plus two fragment sets would not
+  // fit two waves per SIMD.
+#ifdef LP_FRAG_B_INPLACE
+  static constexpr bool B_INPLACE = LP_FRAG_B_INPLACE != 0;
+#else
+  static constexpr bool B_INPLACE = MI * NI * 16 + 8 * (MI + NI) > 224;
+#endif
+  static constexpr int FB_SETS = B_INPLACE ? 1 : 2;
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
   static_assert((BM * KC) % (64 * LW) == 0 && (BN * KC) % (64 * LW) == 0, "tile not divisible among waves");
   static_assert(BK == 64 || BK == 32, "LDS swizzle defined for 64- and 128-byte rows");
@@ -439,6 +450,53 @@ __device__ __forceinline__ void dtl_kstep(uint16_t* X, uint16_t* Y, uint32_t kb2
   }
 }
 
+// The same K-step with one B fragment set.  MFMAs run column by column
+// (q = ni * MI + mi), so B fragment ni is free once column ni is done and its
+// next-substep copy is read right then, into the same registers; the A
+// fragments of the next substep go to the other A set in the first MI slots.
+// The last column's B fragment is read after the substep's last MFMA, before
+// the stage barrier, so no wave reads a stage that others may overwrite.
+template <class C, bool NEXT, bool NEXT2>
+__device__ __forceinline__ void dtl_kstep_bi(uint16_t* X, uint16_t* Y, uint32_t kb2, const DtlRows<C::A_INST>& ra,
+                                             const DtlRows<C::B_INST>& rb, int wm, int wn,
+                                             bf16x8_t (&fa)[2][C::MI], bf16x8_t (&fb)[C::NI],
+                                             f32x16_t (&acc)[C::MI][C::NI], int pending, int wave) {
+  constexpr int S = C::BK / 16;
+  constexpr int NQ = C::MI * C::NI;
+  constexpr int NL = C::A_INST + C::B_INST;
+  static_assert(S % 2 == 0, "substep 0 of every stage must use A fragment set 0");
+  const bool loader = C::LW == C::NW || wave < C::LW;
+  bf16x8_t dummy[C::MI];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int cur = s & 1;
+    const bool rd = s + 1 < S || NEXT;  // fragments of a next substep exist
+    uint16_t* src = s + 1 < S ? X : Y;
+    const int kk = s + 1 < S ? (s + 1) * 16 : 0;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      if (rd && q < C::MI) dtl_frag_piece<C>(src, kk, wm, wn, q, fa[cur ^ 1], fb);
+      if (rd && q >= C::MI && q % C::MI == 0)
+        dtl_frag_piece<C>(src, kk, wm, wn, C::MI + q / C::MI - 1, dummy, fb);
+      if (s + 1 == S && NEXT2 && loader) {
+#pragma unroll
+        for (int u = 0; u < (NL + NQ - 1) / NQ; ++u) {
+          const int j = q * ((NL + NQ - 1) / NQ) + u;
+          if (j < NL) dtl_issue_one<C, C::A_INST, C::B_INST>(j, kb2, ra, rb, X, wave);
+        }
+      }
+      const int ni = q / C::MI, mi = q % C::MI;
+      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][mi], fb[ni], acc[mi][ni], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (rd) dtl_frag_piece<C>(src, kk, wm, wn, C::MI + C::NI - 1, dummy, fb);
+    if (NEXT && s == S - 2) {
+      dtl_wait_vm<C>(pending);
+      __syncthreads();
+    }
+  }
+}
+
 // D[m][n] = sum_k A[m][k] * B[rows[n]][k] over K (multiple of 64, may be 0).
 // a: bf16 rows of the block (row 0 = the block's first row, column 0 = the
 // first K column used), M valid rows; b: bf16 base of the gathered matrix,
@@ -483,21 +541,27 @@ __device__ __forceinline__ void gemm_tile_dtl(const uint16_t* a, int64_t lda, in
     dtl_wait_vm<C>(npro - 1);
   }
   __syncthreads();
-  bf16x8_t fa[2][C::MI], fb[2][C::NI];
+  bf16x8_t fa[2][C::MI], fb[C::FB_SETS][C::NI];
 #pragma unroll
   for (int q = 0; q < NF; ++q) dtl_frag_piece<C>(lds, 0, wm, wn, q, fa[0], fb[0]);
 
   auto stage = [&](int k) { return lds + (k & (C::NS - 1)) * C::STAGE_ELEMS; };
+  auto kstep = [&](auto next, auto next2, int kt, uint32_t kbn, int pending) {
+    if constexpr (C::B_INPLACE)
+      dtl_kstep_bi<C, decltype(next)::value, decltype(next2)::value>(stage(kt), stage(kt + 1), kbn, ra, rb, wm, wn,
+                                                                     fa, fb[0], acc, pending, wave);
+    else
+      dtl_kstep<C, decltype(next)::value, decltype(next2)::value>(stage(kt), stage(kt + 1), kbn, ra, rb, wm, wn, fa,
+                                                                  fb, acc, pending, wave);
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
   int kt = 0;
   // steady state: stage kt + NS is loaded into stage kt's buffer; NS - 2 later stages stay in flight
-  for (; kt + C::NS < nk; ++kt) {
-    const uint32_t kbn = static_cast<uint32_t>((kt + C::NS) * KB);
-    dtl_kstep<C, true, true>(stage(kt), stage(kt + 1), kbn, ra, rb, wm, wn, fa, fb, acc, C::NS - 2, wave);
-  }
+  for (; kt + C::NS < nk; ++kt) kstep(T_{}, T_{}, kt, static_cast<uint32_t>((kt + C::NS) * KB), C::NS - 2);
   // drain: no more loads; stages kt + 2 .. nk - 1 are still in flight
-  for (; kt + 1 < nk; ++kt)
-    dtl_kstep<C, true, false>(stage(kt), stage(kt + 1), 0u, ra, rb, wm, wn, fa, fb, acc, nk - kt - 2, wave);
-  dtl_kstep<C, false, false>(stage(kt), stage(kt), 0u, ra, rb, wm, wn, fa, fb, acc, 0, wave);
+  for (; kt + 1 < nk; ++kt) kstep(T_{}, F_{}, kt, 0u, nk - kt - 2);
+  kstep(F_{}, F_{}, kt, 0u, 0);
   __syncthreads();
 }
 

@@ -94,12 +94,13 @@ struct LMHeadWorkspace {
   size_t part_off;    // float [tile_rows x n_vblocks x 3]   (forward)
   size_t zy_off;      // float [tile_rows]                   (forward)
   size_t dz_off;      // bf16 [tile_rows x Vpad]             (backward)
+  size_t tbuf_off;    // float teacher logits of one row chunk (KL, direct-to-LDS tiles)
   size_t total;
   int n_vblocks;
   int64_t vpad;
 };
 
-// backward: 0 log-prob forward, 1 backward (either loss), 2 KL forward.
+// backward: 0 log-prob forward, 1 log-prob backward, 2 KL forward, 3 KL backward.
 bool lmhead_workspace_layout(int64_t T, int64_t h, int64_t V, int64_t tile_rows, int backward,
                              LMHeadWorkspace* w);
 

@@ -58,6 +58,26 @@ using FwdDtlCfg = RsCfg<256, 256, 2, 2>;
 using FwdDtlCfg = DtlCfg<LP_FWD_DTL_TILE>;
 #define LP_FWD_MAINLOOP gemm_tile_dtl
 #endif
+// Backward GEMMs on the fast path (dL/dlogits recompute, dHidden, dW).
+#ifndef LP_BWD_DTL_TILE
+#define LP_BWD_DTL_TILE 256, 256, 4, 2
+#endif
+using BwdDtlCfg = DtlCfg<LP_BWD_DTL_TILE>;
+// KL through both heads on the fast path: two passes per chunk of at most
+// kKLChunk scored rows on this tile.  The teacher pass stores its fp32 logits
+// for the chunk; the student pass's epilogue reads them back.  Measured on
+// the 16384 x 7168 x 129280 distillation shape: 4096-row chunks beat 2048 and
+// 1024 (each chunk re-reads both weights) and the one-kernel form with both
+// accumulator sets, which caps the wave tile at 128 x 64.
+#ifndef LP_KL_TILE
+#define LP_KL_TILE 256, 256, 4, 2
+#endif
+using KLCfg = DtlCfg<LP_KL_TILE>;
+#ifndef LP_KL_CHUNK_ROWS
+#define LP_KL_CHUNK_ROWS 4096
+#endif
+constexpr int kKLChunk = LP_KL_CHUNK_ROWS;
+static_assert(kKLChunk % KLCfg::BN == 0 && kKLChunk % 64 == 0, "chunk must hold whole row blocks");
 
 // K splits of the dHidden GEMM (its output is only tile_rows x h, too few
 // blocks to fill the chip without splitting K = V).
@@ -122,16 +142,19 @@ bool lmhead_workspace_layout(int64_t T, int64_t h, int64_t V, int64_t tile_rows,
   w->count_off = off;
   off += 256;
   w->part_off = w->zy_off = w->dz_off = 0;
+  w->tbuf_off = 0;
   if (backward == 0 || backward == 2) {
     // log-prob forward: 3 floats per partial state, up to kMaxTargets target logits per row;
     // KL forward: 5 floats per dual state, the student and teacher target logits per row
+    // (the KL forward runs chunks of at most kKLChunk rows)
     const int fields = backward == 0 ? 3 : 5;
     const int per_row = backward == 0 ? kMaxTargets : 2;
+    const int64_t prow = backward == 2 && tr > kKLChunk ? kKLChunk : tr;
     w->part_off = off;
-    off = align_up(off + static_cast<size_t>(tr) * w->n_vblocks * fields * 4, 256);
+    off = align_up(off + static_cast<size_t>(prow) * w->n_vblocks * fields * 4, 256);
     w->zy_off = off;
-    off = align_up(off + static_cast<size_t>(tr) * per_row * 4, 256);
-  } else {
+    off = align_up(off + static_cast<size_t>(prow) * per_row * 4, 256);
+  } else {  // backward == 1 or 3
     const size_t tpad = align_up(static_cast<size_t>(tr), 64);
     w->dz_off = off;  // dZ [tpad x vpad], dZ^T [vpad x tpad], W^T [h x vpad], H_tile^T [h x tpad]
     off = align_up(off + tpad * static_cast<size_t>(w->vpad) * 2, 256);
@@ -139,6 +162,13 @@ bool lmhead_workspace_layout(int64_t T, int64_t h, int64_t V, int64_t tile_rows,
     off = align_up(off + static_cast<size_t>(h) * static_cast<size_t>(w->vpad) * 2, 256);
     off = align_up(off + static_cast<size_t>(h) * tpad * 2, 256);
     off = align_up(off + static_cast<size_t>(kSplitK) * tr * static_cast<size_t>(h) * 4, 256);  // dHidden partials
+  }
+  if (backward >= 2) {
+    // teacher logits of one chunk: [vocab block][row block][BM x BN] floats
+    const int64_t chunk = tr < kKLChunk ? tr : kKLChunk;
+    const int64_t nvb = (V + KLCfg::BM - 1) / KLCfg::BM, nnb = (chunk + KLCfg::BN - 1) / KLCfg::BN;
+    w->tbuf_off = off;
+    off = align_up(off + static_cast<size_t>(nvb * nnb) * KLCfg::BM * KLCfg::BN * 4, 256);
   }
   w->total = off;
   return true;
@@ -281,6 +311,7 @@ __device__ __forceinline__ void fwd_epilogue(const FwdArgs& a, f32x16_t (&acc)[C
     o.a = __shfl_xor(st.a, 32, 64);
     st = stat_merge(st, o);
     if (lane < 32) sm[wm * C::BN + nl] = st;
+    __builtin_amdgcn_sched_barrier(0);  // one token column at a time: bounds the live registers
   }
   __syncthreads();
   if (wm == 0 && lane < 32) {
@@ -910,7 +941,7 @@ hipError_t backward_tiles(const LMHeadShape& sh, bool fast, int bm_fast, int bn_
                           float* grad_weight,
                           char* ws, const LMHeadWorkspace& w, hipStream_t s, LaunchDz&& launch_dz) {
   using C = BwdCfg;
-  using F = FwdDtlCfg;
+  using F = BwdDtlCfg;
   int* idx = reinterpret_cast<int*>(ws + w.idx_off);
   int* count = reinterpret_cast<int*>(ws + w.count_off);
   const int64_t tr = sh.tile_rows < sh.T ? sh.tile_rows : sh.T;
@@ -1123,12 +1154,12 @@ hipError_t launch_lmhead_backward(const LMHeadShape& sh, const float* lse, const
     TimedLaunch tl("k_bwd_dz", s);
     const dim3 grid(static_cast<unsigned>(n_vb) * n_nb);
     if (fast)
-      hipLaunchKernelGGL(k_bwd_dz_dtl<FwdDtlCfg>, grid, dim3(FwdDtlCfg::NT), 0, s, d);
+      hipLaunchKernelGGL(k_bwd_dz_dtl<BwdDtlCfg>, grid, dim3(BwdDtlCfg::NT), 0, s, d);
     else
       hipLaunchKernelGGL(k_bwd_dz<BwdCfg>, grid, dim3(BwdCfg::NT), 0, s, d);
     return hipGetLastError();
   };
-  return backward_tiles(sh, fast, FwdDtlCfg::BM, FwdDtlCfg::BN, grad_hidden, grad_weight, ws, w, s, launch_dz);
+  return backward_tiles(sh, fast, BwdDtlCfg::BM, BwdDtlCfg::BN, grad_hidden, grad_weight, ws, w, s, launch_dz);
 }
 
 
@@ -1146,20 +1177,12 @@ hipError_t launch_lmhead_backward(const LMHeadShape& sh, const float* lse, const
 // student's dHidden / dW GEMMs; the teacher is not trained.
 
 // Two accumulator sets must fit next to the mainloop's registers: 128 vocab x
-// 64 rows per wave, 4 waves side by side along the rows (a 128 x 256 block,
-// one wave per SIMD so each wave may hold 2 x 128 accumulator registers).
-// Measured faster than 64 x 64 wave tiles at two waves per SIMD, whose
-// operand traffic per MFMA is a third higher.
-#ifndef LP_KL_DTL_TILE
-#define LP_KL_DTL_TILE 128, 256, 1, 4
-#endif
-using KLDtlCfg = DtlCfg<LP_KL_DTL_TILE>;
-// Vocab blocks per group in the KL tiles' walk (measured: 4 beats 2, 8, 16).
+// Vocab blocks per group in the KL tiles' walk.
 #ifndef LP_KL_GROUP_V
 #define LP_KL_GROUP_V 4
 #endif
 constexpr int kKLGroupV = LP_KL_GROUP_V;
-static_assert(KLDtlCfg::BM >= (FwdCfg::BM < FwdDtlCfg::BM ? FwdCfg::BM : FwdDtlCfg::BM),
+static_assert(KLCfg::BM >= (FwdCfg::BM < FwdDtlCfg::BM ? FwdCfg::BM : FwdDtlCfg::BM),
               "the workspace holds partial states for vocab blocks of at least the smallest forward block");
 
 struct KLHeadArgs {
@@ -1183,11 +1206,94 @@ struct KLHeadArgs {
   int n_vb, n_nb;
   float* part;  // [tile_rows][n_vb][5]
   float* zy;    // [tile_rows][2]: student, teacher target logit
+  float* tbuf;  // teacher logits of the chunk (two-pass tiles)
 };
 
+// Where the student epilogues find the teacher's logits of their block: in
+// registers (both GEMMs in one kernel), or in the chunk buffer the teacher
+// pass wrote in accumulator order.  column(ni, x) yields x[mi][i] =
+// teacher logit at accumulator (mi, ni, i) of this lane.
 template <class C>
-__device__ __forceinline__ void kl_epilogue(const KLHeadArgs& a, f32x16_t (&accu)[C::MI][C::NI],
-                                            f32x16_t (&accv)[C::MI][C::NI], int vb, int n0, int rows, uint16_t* lds) {
+struct TeacherRegs {
+  f32x16_t (&acc)[C::MI][C::NI];
+  __device__ __forceinline__ void column(int ni, float (&x)[C::MI][16]) {
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[mi][i] = acc[mi][ni][i];
+  }
+};
+
+// Accumulator-order buffer of one BM x BN block: wave w's sub-tile at
+// w * WTM * WTN floats, inside it [mi][ni][quad][lane][4], so each 16-byte
+// store or load of a wave covers 1 KB contiguously.
+template <class C>
+__device__ __forceinline__ int64_t tbuf_block(int vb, int nb, int n_nb) {
+  return (static_cast<int64_t>(vb) * n_nb + nb) * (C::BM * C::BN);
+}
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+// The chunk buffer is written once and read once, far apart: non-temporal
+// accesses keep it from evicting the weight and hidden strips the tiles share
+// in L2 (measured 2 % faster).
+#ifndef LP_KL_TBUF_NT
+#define LP_KL_TBUF_NT 1
+#endif
+
+template <class C>
+__device__ __forceinline__ void tbuf_store(float* blk, const f32x16_t (&acc)[C::MI][C::NI]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float* p = blk + wave * (C::WTM * C::WTN) + 4 * lane;
+#pragma unroll
+  for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < C::NI; ++ni)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4_t v{acc[mi][ni][4 * q], acc[mi][ni][4 * q + 1], acc[mi][ni][4 * q + 2], acc[mi][ni][4 * q + 3]};
+        f32x4_t* d = reinterpret_cast<f32x4_t*>(p + ((mi * C::NI + ni) * 4 + q) * 256);
+        if (LP_KL_TBUF_NT)
+          __builtin_nontemporal_store(v, d);
+        else
+          *d = v;
+      }
+}
+
+// Column ni + 1 is loaded while column ni is folded.
+template <class C>
+struct TeacherMem {
+  const float* p;  // block base + this wave's sub-tile + 4 * lane
+  f32x4_t nxt[C::MI][4];
+  __device__ __forceinline__ TeacherMem(const float* blk) {
+    p = blk + (threadIdx.x >> 6) * (C::WTM * C::WTN) + 4 * (threadIdx.x & 63);
+    load(0);
+  }
+  __device__ __forceinline__ void load(int ni) {
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4_t* src = reinterpret_cast<const f32x4_t*>(p + ((mi * C::NI + ni) * 4 + q) * 256);
+        nxt[mi][q] = LP_KL_TBUF_NT ? __builtin_nontemporal_load(src) : *src;
+      }
+  }
+  __device__ __forceinline__ void column(int ni, float (&x)[C::MI][16]) {
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        x[mi][4 * q] = nxt[mi][q][0];
+        x[mi][4 * q + 1] = nxt[mi][q][1];
+        x[mi][4 * q + 2] = nxt[mi][q][2];
+        x[mi][4 * q + 3] = nxt[mi][q][3];
+      }
+    if (ni + 1 < C::NI) load(ni + 1);
+  }
+};
+
+template <class C, class TSrc>
+__device__ __forceinline__ void kl_epilogue(const KLHeadArgs& a, f32x16_t (&accu)[C::MI][C::NI], TSrc& tv, int vb,
+                                            int n0, int rows, uint16_t* lds) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave % C::WGM, wn = wave / C::WGM;
@@ -1202,6 +1308,8 @@ __device__ __forceinline__ void kl_epilogue(const KLHeadArgs& a, f32x16_t (&accu
     const int r = n0 + nl;
     const bool valid_row = r < rows;
     KLState st{kNegBig, 0.f, kNegBig, 0.f, 0.f};
+    float tcol[C::MI][16];
+    tv.column(ni, tcol);
 #pragma unroll
     for (int mi = 0; mi < C::MI; ++mi) {
       float xu[16], xv[16];
@@ -1209,7 +1317,7 @@ __device__ __forceinline__ void kl_epilogue(const KLHeadArgs& a, f32x16_t (&accu
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           xu[i] = accu[mi][ni][i];
-          xv[i] = accv[mi][ni][i];
+          xv[i] = tcol[mi][i];
         }
         kl_push<false, 16, 16>(st, xu, xv, c);
       } else {
@@ -1217,7 +1325,7 @@ __device__ __forceinline__ void kl_epilogue(const KLHeadArgs& a, f32x16_t (&accu
         for (int i = 0; i < 16; ++i) {
           const int v = vwave + mi * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
           xu[i] = (v < a.V) ? accu[mi][ni][i] : -INFINITY;
-          xv[i] = (v < a.V) ? accv[mi][ni][i] : -INFINITY;
+          xv[i] = (v < a.V) ? tcol[mi][i] : -INFINITY;
         }
         kl_push<true, 16, 16>(st, xu, xv, c);
       }
@@ -1233,7 +1341,7 @@ __device__ __forceinline__ void kl_epilogue(const KLHeadArgs& a, f32x16_t (&accu
           for (int i = 0; i < 16; ++i)
             if (yrel == mi * 32 + 8 * (i >> 2) + 4 * half + (i & 3)) {
               zu = accu[mi][ni][i];
-              zv = accv[mi][ni][i];
+              zv = tcol[mi][i];
               found = true;
             }
         if (found) {
@@ -1307,23 +1415,37 @@ __global__ void __launch_bounds__(C::NT) k_kl_tile(KLHeadArgs a) {
   op.ldb = a.ld_hs;
   op.K = a.h_s;
   gemm_tile<C>(op, 0, 0, lds, accu);
-  kl_epilogue<C>(a, accu, accv, vb, n0, rows, lds);
+  TeacherRegs<C> tv{accv};
+  kl_epilogue<C>(a, accu, tv, vb, n0, rows, lds);
 }
 
-// Fast KL tile (both h % 64 == 0): direct-to-LDS mainloop, 256 x 128 block.
+// Fast path, pass 1 (both h % 64 == 0): the teacher's logits of the chunk,
+// stored in accumulator order.
 template <class C>
-__global__ void __launch_bounds__(C::NT) k_kl_tile_dtl(KLHeadArgs a) {
+__global__ void __launch_bounds__(C::NT) k_kl_teacher_dtl(KLHeadArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t lds[C::LDS_ELEMS];
   int vb, n0, rows;
   if (!kl_block(a.n_vb, a.n_nb, a.count, a.tile_base, a.tile_rows, C::BN, vb, n0, rows)) return;
   const int v0 = vb * C::BM;
-  const int* brows = a.idx + a.tile_base + n0;
-  f32x16_t accv[C::MI][C::NI], accu[C::MI][C::NI];
-  gemm_tile_dtl<C>(a.wt + static_cast<int64_t>(v0) * a.ld_wt, a.ld_wt, a.V - v0, a.ht, a.ld_ht, brows, rows - n0,
-                   a.h_t, lds, accv);
-  gemm_tile_dtl<C>(a.ws + static_cast<int64_t>(v0) * a.ld_ws, a.ld_ws, a.V - v0, a.hs, a.ld_hs, brows, rows - n0,
-                   a.h_s, lds, accu);
-  kl_epilogue<C>(a, accu, accv, vb, n0, rows, lds);
+  f32x16_t acc[C::MI][C::NI];
+  gemm_tile_dtl<C>(a.wt + static_cast<int64_t>(v0) * a.ld_wt, a.ld_wt, a.V - v0, a.ht, a.ld_ht,
+                   a.idx + a.tile_base + n0, rows - n0, a.h_t, lds, acc);
+  tbuf_store<C>(a.tbuf + tbuf_block<C>(vb, n0 / C::BN, a.n_nb), acc);
+}
+
+// Fast path, pass 2: the student's logits, folded with the stored teacher
+// logits into one dual state per (row, vocab block).
+template <class C>
+__global__ void __launch_bounds__(C::NT) k_kl_student_dtl(KLHeadArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[C::LDS_ELEMS];
+  int vb, n0, rows;
+  if (!kl_block(a.n_vb, a.n_nb, a.count, a.tile_base, a.tile_rows, C::BN, vb, n0, rows)) return;
+  const int v0 = vb * C::BM;
+  f32x16_t accu[C::MI][C::NI];
+  gemm_tile_dtl<C>(a.ws + static_cast<int64_t>(v0) * a.ld_ws, a.ld_ws, a.V - v0, a.hs, a.ld_hs,
+                   a.idx + a.tile_base + n0, rows - n0, a.h_s, lds, accu);
+  TeacherMem<C> tv(a.tbuf + tbuf_block<C>(vb, n0 / C::BN, a.n_nb));
+  kl_epilogue<C>(a, accu, tv, vb, n0, rows, lds);
 }
 
 struct KLMergeArgs {
@@ -1386,7 +1508,7 @@ __global__ void __launch_bounds__(256) k_kl_merge(KLMergeArgs a) {
 }
 
 static bool kl_fast_path(const LMHeadShape& st, const LMHeadShape& te) {
-  return lmhead_fast_path(st) && lmhead_fast_path(te) && st.h % KLDtlCfg::BK == 0 && te.h % KLDtlCfg::BK == 0;
+  return lmhead_fast_path(st) && lmhead_fast_path(te) && st.h % KLCfg::BK == 0 && te.h % KLCfg::BK == 0;
 }
 
 static KLHeadArgs kl_args(const LMHeadShape& st, const LMHeadShape& te) {
@@ -1421,10 +1543,12 @@ hipError_t launch_lmhead_kl_forward(const LMHeadShape& sh, const LMHeadShape& te
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t tr = sh.tile_rows < sh.T ? sh.tile_rows : sh.T;
   const bool fast = kl_fast_path(sh, te);
-  const int bm = fast ? KLDtlCfg::BM : FwdCfg::BM;
-  const int bn = fast ? KLDtlCfg::BN : FwdCfg::BN;
+  // chunks of at most kKLChunk rows (the fast path's teacher buffer holds one)
+  const int64_t tr0 = sh.tile_rows < sh.T ? sh.tile_rows : sh.T;
+  const int64_t tr = tr0 > kKLChunk ? kKLChunk : tr0;
+  const int bm = fast ? KLCfg::BM : FwdCfg::BM;
+  const int bn = fast ? KLCfg::BN : FwdCfg::BN;
   const int n_vb = (sh.V + bm - 1) / bm;
   const int n_nb = static_cast<int>((tr + bn - 1) / bn);
   for (int64_t base = 0; base < sh.T; base += tr) {
@@ -1438,13 +1562,19 @@ hipError_t launch_lmhead_kl_forward(const LMHeadShape& sh, const LMHeadShape& te
     a.n_nb = n_nb;
     a.part = part;
     a.zy = zy;
-    {
+    a.tbuf = reinterpret_cast<float*>(ws + w.tbuf_off);
+    const dim3 grid(static_cast<unsigned>(n_vb) * n_nb);
+    if (fast) {
+      {
+        TimedLaunch tl("k_kl_teacher", s);
+        hipLaunchKernelGGL(k_kl_teacher_dtl<KLCfg>, grid, dim3(KLCfg::NT), 0, s, a);
+      }
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      TimedLaunch tl("k_kl_student", s);
+      hipLaunchKernelGGL(k_kl_student_dtl<KLCfg>, grid, dim3(KLCfg::NT), 0, s, a);
+    } else {
       TimedLaunch tl("k_kl_tile", s);
-      const dim3 grid(static_cast<unsigned>(n_vb) * n_nb);
-      if (fast)
-        hipLaunchKernelGGL(k_kl_tile_dtl<KLDtlCfg>, grid, dim3(KLDtlCfg::NT), 0, s, a);
-      else
-        hipLaunchKernelGGL(k_kl_tile<FwdCfg>, grid, dim3(FwdCfg::NT), 0, s, a);
+      hipLaunchKernelGGL(k_kl_tile<FwdCfg>, grid, dim3(FwdCfg::NT), 0, s, a);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     KLMergeArgs m;
@@ -1482,10 +1612,9 @@ struct KLDzArgs {
   uint16_t* dzt;
 };
 
-template <class C, bool STAGED>
-__device__ __forceinline__ void kl_dz_epilogue(const KLDzArgs& a, f32x16_t (&accu)[C::MI][C::NI],
-                                               f32x16_t (&accv)[C::MI][C::NI], int v0, int n0, int rows, int rowsK,
-                                               uint16_t* lds) {
+template <class C, bool STAGED, class TSrc>
+__device__ __forceinline__ void kl_dz_epilogue(const KLDzArgs& a, f32x16_t (&accu)[C::MI][C::NI], TSrc& tv, int v0,
+                                               int n0, int rows, int rowsK, uint16_t* lds) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave % C::WGM, wn = wave / C::WGM;
@@ -1494,6 +1623,8 @@ __device__ __forceinline__ void kl_dz_epilogue(const KLDzArgs& a, f32x16_t (&acc
 #pragma unroll
   for (int ni = 0; ni < C::NI; ++ni) {
     const int r = n0 + wn * C::WTN + ni * 32 + (lane & 31);
+    float tcol[C::MI][16];
+    tv.column(ni, tcol);  // before the row test: keeps the column prefetch uniform
     if (r >= rowsK) continue;
     const bool valid = r < rows;
     float lu = 0.f, lv = 0.f, g = 0.f;
@@ -1514,7 +1645,7 @@ __device__ __forceinline__ void kl_dz_epilogue(const KLDzArgs& a, f32x16_t (&acc
           float d = 0.f;
           if (valid && vq + j < a.h.V) {
             const float pu = fast_exp2(fmaf(accu[mi][ni][q * 4 + j], c, -lu));
-            const float pv = fast_exp2(fmaf(accv[mi][ni][q * 4 + j], c, -lv));
+            const float pv = fast_exp2(fmaf(tcol[mi][q * 4 + j], c, -lv));
             d = g * (pu - pv);
           }
           dv[j] = d;
@@ -1560,31 +1691,34 @@ __global__ void __launch_bounds__(C::NT) k_kl_dz(KLDzArgs a) {
   op.ldb = a.h.ld_hs;
   op.K = a.h.h_s;
   gemm_tile<C>(op, 0, 0, lds, accu);
-  kl_dz_epilogue<C, false>(a, accu, accv, v0, n0, rows, rowsK, lds);
+  TeacherRegs<C> tv{accv};
+  kl_dz_epilogue<C, false>(a, accu, tv, v0, n0, rows, rowsK, lds);
 }
 
+// Fast path, pass 2 of the backward (pass 1 is k_kl_teacher_dtl): the
+// student's logits against the stored teacher logits; the chunk's rows are
+// zero-padded up to a multiple of 64.
 template <class C>
-__global__ void __launch_bounds__(C::NT) k_kl_dz_dtl(KLDzArgs a) {
+__global__ void __launch_bounds__(C::NT) k_kl_dz_student_dtl(KLDzArgs a) {
   constexpr int kLds = C::LDS_ELEMS > DzStage<C>::ELEMS ? C::LDS_ELEMS : DzStage<C>::ELEMS;
   __shared__ __attribute__((aligned(1024))) uint16_t lds[kLds];
   int vb, n0, rows;
   kl_block(a.h.n_vb, a.h.n_nb, a.h.count, a.h.tile_base, a.h.tile_rows, C::BN, vb, n0, rows);
   const int rowsK = (rows + 63) & ~63;
-  if (rows <= 0 || n0 >= rowsK) return;
+  if (rows <= 0 || n0 >= rowsK) return;  // n0 < rowsK implies n0 < rows: the teacher pass ran this block
   const int v0 = vb * C::BM;
-  const int* brows = a.h.idx + a.h.tile_base + n0;
-  f32x16_t accv[C::MI][C::NI], accu[C::MI][C::NI];
-  gemm_tile_dtl<C>(a.h.wt + static_cast<int64_t>(v0) * a.h.ld_wt, a.h.ld_wt, a.h.V - v0, a.h.ht, a.h.ld_ht, brows,
-                   rows - n0, a.h.h_t, lds, accv);
-  gemm_tile_dtl<C>(a.h.ws + static_cast<int64_t>(v0) * a.h.ld_ws, a.h.ld_ws, a.h.V - v0, a.h.hs, a.h.ld_hs, brows,
-                   rows - n0, a.h.h_s, lds, accu);
-  kl_dz_epilogue<C, true>(a, accu, accv, v0, n0, rows, rowsK, lds);
+  f32x16_t accu[C::MI][C::NI];
+  gemm_tile_dtl<C>(a.h.ws + static_cast<int64_t>(v0) * a.h.ld_ws, a.h.ld_ws, a.h.V - v0, a.h.hs, a.h.ld_hs,
+                   a.h.idx + a.h.tile_base + n0, rows - n0, a.h.h_s, lds, accu);
+  TeacherMem<C> tv(a.h.tbuf + tbuf_block<C>(vb, n0 / C::BN, a.h.n_nb));
+  kl_dz_epilogue<C, true>(a, accu, tv, v0, n0, rows, rowsK, lds);
 }
 
 hipError_t launch_lmhead_kl_backward(const LMHeadShape& sh, const LMHeadShape& te, const float* lse_student,
                                      const float* lse_teacher, const float* grad_kl, float* grad_hidden,
                                      float* grad_weight, char* ws, const LMHeadWorkspace& w, hipStream_t s) {
   const bool fast = kl_fast_path(sh, te) && (reinterpret_cast<uintptr_t>(grad_hidden) & 15u) == 0;
+  float* tbuf = reinterpret_cast<float*>(ws + w.tbuf_off);
   auto launch_dz = [&](int64_t base, int64_t tr, int64_t tpad, int64_t vpad, int n_vb, int n_nb, const int* idx,
                        const int* count, uint16_t* dz, uint16_t* dzt) -> hipError_t {
     KLDzArgs d;
@@ -1592,28 +1726,49 @@ hipError_t launch_lmhead_kl_backward(const LMHeadShape& sh, const LMHeadShape& t
     d.h.idx = idx;
     d.h.count = count;
     d.h.targets = nullptr;
-    d.h.tile_base = base;
-    d.h.tile_rows = static_cast<int>(tr);
     d.h.n_vb = n_vb;
-    d.h.n_nb = n_nb;
     d.h.part = nullptr;
     d.h.zy = nullptr;
+    d.h.tbuf = tbuf;
     d.vpad = vpad;
     d.lse_u = lse_student;
     d.lse_v = lse_teacher;
     d.g = grad_kl;
     d.tpad = tpad;
-    d.dz = dz;
-    d.dzt = dzt;
-    TimedLaunch tl("k_kl_dz", s);
-    const dim3 grid(static_cast<unsigned>(n_vb) * n_nb);
-    if (fast)
-      hipLaunchKernelGGL(k_kl_dz_dtl<KLDtlCfg>, grid, dim3(KLDtlCfg::NT), 0, s, d);
-    else
-      hipLaunchKernelGGL(k_kl_dz<BwdCfg>, grid, dim3(BwdCfg::NT), 0, s, d);
-    return hipGetLastError();
+    if (!fast) {
+      d.h.tile_base = base;
+      d.h.tile_rows = static_cast<int>(tr);
+      d.h.n_nb = n_nb;
+      d.dz = dz;
+      d.dzt = dzt;
+      TimedLaunch tl("k_kl_dz", s);
+      hipLaunchKernelGGL(k_kl_dz<BwdCfg>, dim3(static_cast<unsigned>(n_vb) * n_nb), dim3(BwdCfg::NT), 0, s, d);
+      return hipGetLastError();
+    }
+    // chunks of the tile that fit the teacher buffer; each fills its rows of dZ (and dZ^T)
+    for (int64_t c0 = 0; c0 < tr; c0 += kKLChunk) {
+      const int64_t cr = tr - c0 < kKLChunk ? tr - c0 : kKLChunk;
+      d.h.tile_base = base + c0;
+      d.h.tile_rows = static_cast<int>(cr);
+      d.h.n_nb = static_cast<int>((cr + KLCfg::BN - 1) / KLCfg::BN);
+      d.dz = dz + c0 * vpad;
+      d.dzt = dzt ? dzt + c0 : nullptr;
+      const dim3 grid(static_cast<unsigned>(n_vb) * d.h.n_nb);
+      {
+        TimedLaunch tl("k_kl_teacher", s);
+        hipLaunchKernelGGL(k_kl_teacher_dtl<KLCfg>, grid, dim3(KLCfg::NT), 0, s, d.h);
+      }
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      {
+        TimedLaunch tl("k_kl_dz", s);
+        hipLaunchKernelGGL(k_kl_dz_student_dtl<KLCfg>, grid, dim3(KLCfg::NT), 0, s, d);
+      }
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
   };
-  return backward_tiles(sh, fast, KLDtlCfg::BM, KLDtlCfg::BN, grad_hidden, grad_weight, ws, w, s, launch_dz);
+  return backward_tiles(sh, fast, KLCfg::BM, KLCfg::BN, grad_hidden, grad_weight, ws, w, s, launch_dz);
 }
 
 }  // namespace lp

@@ -223,7 +223,10 @@ lp_status lp_lm_head_logprobs_entropy_backward_k(const void* hidden, int64_t ld_
  * lp_teacher and prob_diff need targets).  A target outside [0, V) gives NaN
  * in lp_student / lp_teacher / prob_diff of that row only.
  * Workspace: lp_lm_head_kl_workspace_bytes(T, h_student, V, tile_rows, 0)
- * bytes, 256-byte aligned, caller-owned; scratch only.  tile_rows bounds it.
+ * bytes, 256-byte aligned, caller-owned; scratch only.  Besides per-row
+ * partial states it holds the teacher's fp32 logits of one chunk of rows
+ * (min(tile_rows, 4096) x V x 4 bytes, rounded up to whole 256 x 256 blocks);
+ * only the row index list grows with T, and tile_rows trades it for speed.
  * Errors as for the other LM-head calls: all checks before any launch.
  */
 size_t lp_lm_head_kl_workspace_bytes(int64_t T, int64_t h_student, int64_t V, int64_t tile_rows, int backward);
@@ -242,7 +245,8 @@ lp_status lp_lm_head_kl(const void* student_hidden, int64_t ld_hs, const void* s
  *   grad_hidden = dL/du . student_weight   fp32 [T x h_student] (NULL: skipped),
  *   grad_weight = dL/du^T . student_hidden fp32 [V x h_student] (NULL: frozen).
  * Both logit tiles are recomputed; lse_student / lse_teacher are the forward's.
- * Workspace: lp_lm_head_kl_workspace_bytes(T, h_student, V, tile_rows, 1).
+ * Workspace: lp_lm_head_kl_workspace_bytes(T, h_student, V, tile_rows, 1)
+ * (the log-prob backward's buffers plus the same teacher-logit chunk).
  * With T == 0, grad_weight (if given) is zero-filled.
  */
 lp_status lp_lm_head_kl_backward(const void* student_hidden, int64_t ld_hs, const void* student_weight,

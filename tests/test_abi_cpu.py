@@ -141,7 +141,13 @@ def test_lm_head_kl_validation(lib, args, code):
 def test_lm_head_kl_workspace_and_backward_checks(lib):
     f = lib.lp_lm_head_kl_workspace_bytes
     fw, bw = f(16384, 7168, 129280, 4096, 0), f(16384, 7168, 129280, 4096, 1)
-    assert 0 < fw < bw and fw < 16384 * 129280 * 4 / 50
+    # the forward holds the teacher's fp32 logits of one chunk of min(tile_rows, 4096) rows, never [T x V]
+    assert 0 < fw < bw and fw < 4096 * 129536 * 4 * 1.1
+    assert f(16384, 7168, 129280, 1024, 0) < 1024 * 129536 * 4 * 1.1
+    assert f(16384, 7168, 129280, 64, 0) < 256 * 129536 * 4 * 1.05  # a small tile: one 256-row block
+    assert f(65536, 7168, 129280, 65536, 0) < 4096 * 129536 * 4 * 1.5  # the chunk is capped
+    # only the 4-byte row index list grows with T
+    assert f(65536, 7168, 129280, 4096, 0) - fw <= (65536 - 16384) * 4 + 256
     assert f(8, 0, 100, 4, 0) == 0 and f(8, 64, 100, 0, 1) == 0
     # backward without the forward's saved normalisers
     st = lib.lp_lm_head_kl_backward(FAKE, 64, FAKE, 64, 64, FAKE, 64, FAKE, 64, 64, 8, 100, None, 4, None, FAKE, FAKE,

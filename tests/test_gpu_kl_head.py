@@ -75,6 +75,29 @@ def test_kl_head_forward_backward(T, hs, ht, V, tile):
     assert not host(dH)[~sc].any()
 
 
+def test_kl_head_several_chunks_per_tile():
+    """More scored rows than one chunk of the teacher buffer (4096 rows):
+    a tile of 8192 rows runs as a full chunk plus a ragged one, in the
+    forward and in the backward's dL/dlogits; rows match a run with one chunk
+    per tile bitwise and the oracle to the fused tolerance."""
+    A = _case(9000, 64, 128, 1000, seed=901, scored=0.7)
+    heads = _dev_heads(A)
+    m, y, dm = to_dev(A["mask"]), to_dev(A["targets"]), to_dev(A["diff_mask"])
+    got = [host(t) for t in _lp().lp_lm_head_kl(*heads, m, y, dm, 8192)]
+    want = O.lm_head_kl(*_wide(A), A["mask"], A["targets"], A["diff_mask"])
+    sc = A["mask"] != 0
+    for name, g, w in zip(("kl", "lp_s", "lp_t", "diff", "lse_s", "lse_t"), got, want):
+        assert max_abs_err(g[sc], w[sc]) <= TOL_FWD, (name, max_abs_err(g[sc], w[sc]))
+    small = [host(t) for t in _lp().lp_lm_head_kl(*heads, m, y, dm, 1000)]
+    assert all(np.array_equal(a, b, equal_nan=True) for a, b in zip(got, small))
+    lse_s, lse_t = to_dev(got[4]), to_dev(got[5])
+    dH, dW = _lp().lp_lm_head_kl_backward(*heads, m, 8192, lse_s, lse_t, to_dev(A["grad_kl"]))
+    dH_o, dW_o = O.lm_head_kl_backward(*_wide(A), A["mask"], A["grad_kl"])
+    for nm, g, w in (("dH", host(dH), dH_o), ("dW", host(dW), dW_o)):
+        fro, mad = grad_errors(g, w)
+        assert fro <= TOL_GRAD and mad <= TOL_GRAD, (nm, fro, mad)
+
+
 def test_kl_head_same_model_is_exactly_zero():
     A = _case(96, 128, 128, 777, seed=5, scored=1.0)
     hs, ws = to_dev_bits(A["student_hidden"], "bf16"), to_dev_bits(A["student_weight"], "bf16")
