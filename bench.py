@@ -395,6 +395,41 @@ def bench_kl_lm_head(lp, torch, np, synth, O, steps, warmup):
     return res
 
 
+def measure_achievable(torch):
+    """Second denominators beside the datasheet peaks, measured on this GPU:
+    a streaming read (torch's sum over a 4 GiB fp32 tensor) and a large
+    library bf16 GEMM (torch.matmul, 8192^3, contiguous operands)."""
+    x = torch.ones(1 << 30, dtype=torch.float32, device="cuda")
+    a = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+    b = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+
+    def hbm():
+        x.sum()
+
+    def gemm():
+        torch.matmul(a, b)
+
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < SETTLE_SECONDS:
+        gemm()
+        torch.cuda.synchronize()
+    hbm_ms = min(_events_ms(torch, hbm, 5) / 5 for _ in range(3))
+    gemm_ms = min(_events_ms(torch, gemm, 10) / 10 for _ in range(3))
+    out = dict(hbm_read_gbs=x.numel() * 4 / (hbm_ms * 1e-3) / 1e9,
+               bf16_gemm_tflops=2.0 * 8192 ** 3 / (gemm_ms * 1e-3) / 1e12,
+               source="torch sum over 4 GiB fp32; torch.matmul bf16 8192^3 (library GEMM)")
+    del x, a, b
+    torch.cuda.empty_cache()
+    return out
+
+
+def _add_achievable(roof, ach):
+    if not roof or roof.get("achieved") is None:
+        return
+    ref = ach["hbm_read_gbs"] if roof.get("unit") == "GB/s" else ach["bf16_gemm_tflops"]
+    roof["frac_of_achievable"] = roof["achieved"] / ref
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -456,6 +491,11 @@ def main():
         log(f"path {p}: done in {time.time() - t0:.1f}s: {results[p]['tokens_per_s']:.4g} tok/s, "
             f"{results[p]['ms_per_step']:.3f} ms/step")
 
+    ach = measure_achievable(torch)
+    log(f"achievable on this GPU: {ach['hbm_read_gbs']:.0f} GB/s read, {ach['bf16_gemm_tflops']:.0f} TFLOP/s bf16 GEMM")
+    for r in results.values():
+        _add_achievable(r.get("roofline"), ach)
+        _add_achievable(r.get("fwd_bwd", {}).get("roofline"), ach)
     head_key = "lm_head_fwd" if "lm_head_fwd" in results else paths[0]
     head = results[head_key]
     line = {
@@ -475,6 +515,7 @@ def main():
         "config": {"workload": head["workload"], "path": head_key},
         "roofline": head["roofline"],
         "cpu_baseline": head.get("cpu_baseline"),
+        "achievable": ach,
         "paths": {k: v for k, v in results.items() if k != head_key},
         "parity": {k: {kk: vv for kk, vv in v.items() if kk.startswith("parity")} for k, v in results.items()},
     }

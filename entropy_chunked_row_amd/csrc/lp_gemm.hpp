@@ -565,158 +565,4 @@ __device__ __forceinline__ void gemm_tile_dtl(const uint16_t* a, int64_t lda, in
   __syncthreads();
 }
 
-// ---------------------------------------------------------------------------
-// Register-staged variant of the fast mainloop (same LDS layout and swizzle):
-// each thread moves its chunks global -> VGPRs -> LDS (ds_write_b128), so the
-// LDS is written through the regular write port.  Loads of the next stage
-// go out during substep 0, their LDS writes during substep S-2, then the
-// stage handoff (barrier) as in the direct-to-LDS loop.
-// ---------------------------------------------------------------------------
-
-template <int BM_, int BN_, int WGM_, int WGN_>
-struct RsCfg {
-  static constexpr int BM = BM_, BN = BN_, BK = 64, WGM = WGM_, WGN = WGN_;
-  static constexpr int NT = 64 * WGM * WGN;
-  static constexpr int NW = WGM * WGN;
-  static constexpr int LW = NW;
-  static constexpr int WTM = BM / WGM, WTN = BN / WGN;
-  static constexpr int MI = WTM / 32, NI = WTN / 32;
-  static constexpr int KC = BK / 8;
-  static constexpr int A_CH = BM * KC / NT;  // chunks per thread per stage
-  static constexpr int B_CH = BN * KC / NT;
-  static constexpr int STAGE_ELEMS = (BM + BN) * BK;
-  static constexpr int LDS_ELEMS = 2 * STAGE_ELEMS;
-  static_assert((BM * KC) % NT == 0 && (BN * KC) % NT == 0, "tile not divisible among threads");
-};
-
-template <class C>
-struct RsRows {
-  uint32_t a[C::A_CH];  // byte offsets of the row starts (K column 0) from the operand bases
-  uint32_t b[C::B_CH];
-};
-
-// chunk i of this thread: slot = tid + i * NT  ->  row = slot / KC, logical 16-byte column kc = slot % KC
-template <class C>
-__device__ __forceinline__ void rs_rows(RsRows<C>& rw, int64_t lda, int M, int64_t ldb, const int* b_rows, int N) {
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < C::A_CH; ++i) {
-    const int slot = tid + i * C::NT;
-    const int r = slot / C::KC, kc = slot % C::KC;
-    const int rr = r < M ? r : M - 1;
-    rw.a[i] = static_cast<uint32_t>((static_cast<int64_t>(rr) * lda + kc * 8) * 2);
-  }
-#pragma unroll
-  for (int i = 0; i < C::B_CH; ++i) {
-    const int slot = tid + i * C::NT;
-    const int r = slot / C::KC, kc = slot % C::KC;
-    const int rr = r < N ? r : N - 1;
-    const int64_t src = b_rows ? static_cast<int64_t>(b_rows[rr]) : static_cast<int64_t>(rr);
-    rw.b[i] = static_cast<uint32_t>((src * ldb + kc * 8) * 2);
-  }
-}
-
-template <class C>
-__device__ __forceinline__ uint16_t* rs_lds_slot(uint16_t* stage, int i, bool is_b) {
-  const int slot = threadIdx.x + i * C::NT;
-  const int r = slot / C::KC, kc = slot % C::KC;
-  return stage + (is_b ? C::BM * C::BK : 0) + r * C::BK + ((kc ^ lds_swz(r)) * 8);
-}
-
-template <class C, bool NEXT>
-__device__ __forceinline__ void rs_kstep(uint16_t* X, uint16_t* Y, const char* anext, const char* bnext,
-                                         const RsRows<C>& rw, int wm, int wn, bf16x8_t (&fa)[2][C::MI],
-                                         bf16x8_t (&fb)[2][C::NI], f32x16_t (&acc)[C::MI][C::NI]) {
-  constexpr int S = C::BK / 16;
-  constexpr int NQ = C::MI * C::NI;
-  constexpr int NF = C::MI + C::NI;
-  constexpr int NCH = C::A_CH + C::B_CH;
-  static_assert(S == 4, "schedule assumes four substeps per stage");
-  u32x4 stg[NCH];
-#pragma unroll
-  for (int s = 0; s < S; ++s) {
-    const int cur = s & 1;
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int f = 2 * q + u;
-        if (f < NF) {
-          if (s + 1 < S)
-            dtl_frag_piece<C>(X, (s + 1) * 16, wm, wn, f, fa[cur ^ 1], fb[cur ^ 1]);
-          else if (NEXT)
-            dtl_frag_piece<C>(Y, 0, wm, wn, f, fa[cur ^ 1], fb[cur ^ 1]);
-        }
-      }
-      if (NEXT && s == 0) {
-        // global loads of the next stage, spread over substep 0
-#pragma unroll
-        for (int u = 0; u < (NCH + NQ - 1) / NQ; ++u) {
-          const int i = q * ((NCH + NQ - 1) / NQ) + u;
-          if (i < C::A_CH)
-            stg[i] = *reinterpret_cast<const u32x4*>(anext + rw.a[i]);
-          else if (i < NCH)
-            stg[i] = *reinterpret_cast<const u32x4*>(bnext + rw.b[i - C::A_CH]);
-        }
-      }
-      if (NEXT && s == S - 2 && q >= NF / 2) {
-        // their LDS writes, after this substep's fragment reads are issued
-        constexpr int SLOTS = NQ - NF / 2;
-#pragma unroll
-        for (int u = 0; u < (NCH + SLOTS - 1) / SLOTS; ++u) {
-          const int i = (q - NF / 2) * ((NCH + SLOTS - 1) / SLOTS) + u;
-          if (i < NCH) *reinterpret_cast<u32x4*>(rs_lds_slot<C>(Y, i < C::A_CH ? i : i - C::A_CH, i >= C::A_CH)) = stg[i];
-        }
-      }
-      const int mi = q / C::NI, ni = q % C::NI;
-      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][mi], fb[cur][ni], acc[mi][ni], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (NEXT && s == S - 2) __syncthreads();
-  }
-}
-
-// Same contract as gemm_tile_dtl.
-template <class C>
-__device__ __forceinline__ void gemm_tile_rs(const uint16_t* a, int64_t lda, int M, const uint16_t* b, int64_t ldb,
-                                             const int* b_rows, int N, int K, uint16_t* lds,
-                                             f32x16_t (&acc)[C::MI][C::NI]) {
-  constexpr int NF = C::MI + C::NI;
-  const int wave = threadIdx.x >> 6;
-  const int wm = wave % C::WGM, wn = wave / C::WGM;
-#pragma unroll
-  for (int mi = 0; mi < C::MI; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < C::NI; ++ni)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
-  const int nk = K / C::BK;
-  if (nk <= 0) return;
-  RsRows<C> rw;
-  rs_rows<C>(rw, lda, M, ldb, b_rows, N);
-  const char* abase = reinterpret_cast<const char*>(a);
-  const char* bbase = reinterpret_cast<const char*>(b);
-  constexpr int KB = C::BK * 2;
-  uint16_t* L0 = lds;
-  uint16_t* L1 = lds + C::STAGE_ELEMS;
-  // prologue: stage 0 through registers into L0
-#pragma unroll
-  for (int i = 0; i < C::A_CH; ++i)
-    *reinterpret_cast<u32x4*>(rs_lds_slot<C>(L0, i, false)) = *reinterpret_cast<const u32x4*>(abase + rw.a[i]);
-#pragma unroll
-  for (int i = 0; i < C::B_CH; ++i)
-    *reinterpret_cast<u32x4*>(rs_lds_slot<C>(L0, i, true)) = *reinterpret_cast<const u32x4*>(bbase + rw.b[i]);
-  __syncthreads();
-  bf16x8_t fa[2][C::MI], fb[2][C::NI];
-#pragma unroll
-  for (int q = 0; q < NF; ++q) dtl_frag_piece<C>(L0, 0, wm, wn, q, fa[0], fb[0]);
-  int kt = 0;
-  for (; kt + 1 < nk; ++kt) {
-    const int64_t kb = static_cast<int64_t>(kt + 1) * KB;
-    rs_kstep<C, true>((kt & 1) ? L1 : L0, (kt & 1) ? L0 : L1, abase + kb, bbase + kb, rw, wm, wn, fa, fb, acc);
-  }
-  rs_kstep<C, false>((kt & 1) ? L1 : L0, (kt & 1) ? L0 : L1, abase, bbase, rw, wm, wn, fa, fb, acc);
-  __syncthreads();
-}
-
 }  // namespace lp

@@ -44,20 +44,11 @@ using FwdCfg = GemmCfg<LP_FWD_TILE>;
 #ifndef LP_FWD_DTL_TILE
 #define LP_FWD_DTL_TILE 256, 256, 4, 2
 #endif
-#ifndef LP_FWD_RS
-#define LP_FWD_RS 0
-#endif
 // Minimum waves per SIMD the forward tile is compiled for (register budget).
 #ifndef LP_FWD_MIN_WAVES
 #define LP_FWD_MIN_WAVES 1
 #endif
-#if LP_FWD_RS
-using FwdDtlCfg = RsCfg<256, 256, 2, 2>;
-#define LP_FWD_MAINLOOP gemm_tile_rs
-#else
 using FwdDtlCfg = DtlCfg<LP_FWD_DTL_TILE>;
-#define LP_FWD_MAINLOOP gemm_tile_dtl
-#endif
 // Backward GEMMs on the fast path (dL/dlogits recompute, dHidden, dW).
 #ifndef LP_BWD_DTL_TILE
 #define LP_BWD_DTL_TILE 256, 256, 4, 2
@@ -371,7 +362,7 @@ __global__ void __launch_bounds__(C::NT, LP_FWD_MIN_WAVES) k_fwd_tile_dtl(FwdArg
   if (n0 >= rows) return;
   const int v0 = vb * C::BM;
   f32x16_t acc[C::MI][C::NI];
-  LP_FWD_MAINLOOP<C>(a.weight + static_cast<int64_t>(v0) * a.ld_w, a.ld_w, a.V - v0, a.hidden, a.ld_h,
+  gemm_tile_dtl<C>(a.weight + static_cast<int64_t>(v0) * a.ld_w, a.ld_w, a.V - v0, a.hidden, a.ld_h,
                      a.idx + a.tile_base + n0, rows - n0, a.h, lds, acc);
   fwd_epilogue<C>(a, acc, vb, n0, rows, lds);
 }
@@ -575,8 +566,8 @@ struct DzArgs {
   uint16_t* dzt;  // [vpad][tpad] or nullptr
 };
 
-// Four consecutive vocab columns vq..vq+3 of tile row r, packed bf16 in pk:
-// four 2-byte stores into dZ^T [vocab][row] ...
+// Four consecutive vocab columns vq..vq+3 of tile row r, packed bf16 in pk
+// (generic tiles): four 2-byte stores into dZ^T [vocab][row] ...
 __device__ __forceinline__ void dzt_store4(uint16_t* dzt, int64_t tpad, int r, int vq, uint2 pk) {
   dzt[static_cast<int64_t>(vq) * tpad + r] = static_cast<uint16_t>(pk.x);
   dzt[static_cast<int64_t>(vq + 1) * tpad + r] = static_cast<uint16_t>(pk.x >> 16);
@@ -621,6 +612,32 @@ __device__ __forceinline__ void dz_flush_rows(const uint16_t* lds, uint16_t* dz,
     const uint2 lo = *reinterpret_cast<const uint2*>(lds + r * P + ch * 8);
     const uint2 hi = *reinterpret_cast<const uint2*>(lds + r * P + ch * 8 + 4);
     *reinterpret_cast<uint4*>(dz + static_cast<int64_t>(n0 + r) * vpad + v) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+  }
+}
+
+// Copies the staged rows [0, nrow) (nrow a multiple of 64) to dZ^T
+// [vocab][row]: each thread gathers 8 consecutive rows of one vocab column
+// from LDS and writes them with one 16-byte store; the 64 lanes of a wave
+// take 8 row octets x 8 columns, so each store instruction fills 8 whole
+// 128-byte lines.  Needs the same barrier as dz_flush_rows.
+template <class C>
+__device__ __forceinline__ void dzt_flush_cols(const uint16_t* lds, uint16_t* dzt, int64_t tpad, int64_t vpad, int v0,
+                                               int n0, int nrow) {
+  constexpr int P = DzStage<C>::P;
+  constexpr int NVO = C::BM / 8;  // vocab octets
+  const int nitems = (nrow / 8) * C::BM;
+  for (int idx = threadIdx.x; idx < nitems; idx += C::NT) {
+    const int blk = idx / 64, w = idx % 64;
+    const int g = (blk / NVO) * 8 + (w & 7);  // row octet
+    const int vl = (blk % NVO) * 8 + (w >> 3);
+    const int64_t v = v0 + vl;
+    if (v >= vpad) continue;
+    uint32_t q[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      q[j] = static_cast<uint32_t>(lds[(g * 8 + 2 * j) * P + vl]) |
+             (static_cast<uint32_t>(lds[(g * 8 + 2 * j + 1) * P + vl]) << 16);
+    *reinterpret_cast<uint4*>(dzt + v * tpad + n0 + g * 8) = make_uint4(q[0], q[1], q[2], q[3]);
   }
 }
 
@@ -687,18 +704,17 @@ __device__ __forceinline__ void dz_epilogue(const DzArgs& a, f32x16_t (&acc)[C::
           }
         }
         const uint2 pk = pack_bf16x4(d);
-        if (STAGED) {
+        if (STAGED)
           dz_stage4(lds, DzStage<C>::P, r - n0, vq - v0, pk);
-          if (a.dzt && vq < a.vpad) dzt_store4(a.dzt, a.tpad, r, vq, pk);
-        } else if (vq < a.vpad) {
+        else if (vq < a.vpad)
           dz_store4(a.dz, a.dzt, a.vpad, a.tpad, r, vq, pk);
-        }
       }
   }
   if (STAGED) {
     __syncthreads();
     const int nrow = (rowsK - n0) < C::BN ? (rowsK - n0) : C::BN;
     dz_flush_rows<C>(lds, a.dz, a.vpad, v0, n0, nrow);
+    if (a.dzt) dzt_flush_cols<C>(lds, a.dzt, a.tpad, a.vpad, v0, n0, nrow);
   }
 }
 
@@ -746,7 +762,7 @@ __global__ void __launch_bounds__(C::NT) k_bwd_dz_dtl(DzArgs a) {
   if (rows <= 0 || n0 >= rowsK) return;
   const int v0 = vb * C::BM;
   f32x16_t acc[C::MI][C::NI];
-  LP_FWD_MAINLOOP<C>(a.weight + static_cast<int64_t>(v0) * a.ld_w, a.ld_w, a.V - v0, a.hidden, a.ld_h,
+  gemm_tile_dtl<C>(a.weight + static_cast<int64_t>(v0) * a.ld_w, a.ld_w, a.V - v0, a.hidden, a.ld_h,
                    a.idx + a.tile_base + n0, rows - n0, a.h, lds, acc);
   dz_epilogue<C, true>(a, acc, v0, n0, rows, rowsK, lds);
 }
@@ -797,7 +813,7 @@ __global__ void __launch_bounds__(C::NT) k_dense_gemm_dtl(DenseGemmArgs g) {
   const int kbeg = ks * g.ksplit;
   const int klen = (K - kbeg < g.ksplit) ? (K - kbeg) : g.ksplit;
   f32x16_t acc[C::MI][C::NI];
-  LP_FWD_MAINLOOP<C>(g.a + static_cast<int64_t>(m0) * g.lda + kbeg, g.lda, M - m0,
+  gemm_tile_dtl<C>(g.a + static_cast<int64_t>(m0) * g.lda + kbeg, g.lda, M - m0,
                    g.b + static_cast<int64_t>(n0) * g.ldb + kbeg, g.ldb, nullptr, g.N - n0, klen > 0 ? klen : 0, lds,
                    acc);
   const int lane = threadIdx.x & 63;
@@ -1651,18 +1667,17 @@ __device__ __forceinline__ void kl_dz_epilogue(const KLDzArgs& a, f32x16_t (&acc
           dv[j] = d;
         }
         const uint2 pk = pack_bf16x4(dv);
-        if (STAGED) {
+        if (STAGED)
           dz_stage4(lds, DzStage<C>::P, r - n0, vq - v0, pk);
-          if (a.dzt && vq < a.vpad) dzt_store4(a.dzt, a.tpad, r, vq, pk);
-        } else if (vq < a.vpad) {
+        else if (vq < a.vpad)
           dz_store4(a.dz, a.dzt, a.vpad, a.tpad, r, vq, pk);
-        }
       }
   }
   if (STAGED) {
     __syncthreads();
     const int nrow = (rowsK - n0) < C::BN ? (rowsK - n0) : C::BN;
     dz_flush_rows<C>(lds, a.dz, a.vpad, v0, n0, nrow);
+    if (a.dzt) dzt_flush_cols<C>(lds, a.dzt, a.tpad, a.vpad, v0, n0, nrow);
   }
 }
 
