@@ -73,6 +73,6 @@ def test_workspace_far_below_a_logits_buffer():
     fw = lib.lp_lm_head_workspace_bytes(32768, 5120, 151936, 4096, 0)
     bw = lib.lp_lm_head_workspace_bytes(114688, 5120, 151936, 4096, 1)
     kl = lib.lp_lm_head_kl_workspace_bytes(16384, 7168, 129280, 4096, 0)
-    assert fw < 32768 * 151936 * 4 / 100
+    assert fw < 32768 * 151936 * 4 / 50  # partial states of up to 8 tiles of 4096 rows
     assert bw < 114688 * 151936 * 4 / 10
     assert kl < 16384 * 129280 * 4 / 3  # one 4096-row chunk of the teacher's fp32 logits, no [T x V]
