@@ -66,9 +66,13 @@ def test_forward_ragged(T, h, V, tile, tau):
     assert np.all(host(lp)[m == 0] == 0)
 
 
-def test_forward_tile_rows_bitwise_invariant():
-    hid, W, y, m = _case(150, 96, 2000, seed=3)
+@pytest.mark.parametrize("h", [96, 128])  # generic tile; direct-to-LDS tile (up to 8 row tiles per launch)
+def test_forward_tile_rows_bitwise_invariant(h):
+    hid, W, y, m = _case(150, h, 2000, seed=3)
     ref = [host(t) for t in _run_fwd(hid, W, y, m, 0.7, 4096)]
+    lp_o, H_o, _ = O.lm_head_logprobs_entropy(O.widen_bf16(hid), O.widen_bf16(W), y, m, 0.7)
+    assert max_abs_err(ref[0], lp_o) <= TOL_FWD and max_abs_err(ref[1], H_o) <= TOL_FWD
+    # 1-row tiles: 150 tiles, 19 launches on the fast path; 7-row tiles: 22 tiles, the last launch partly empty
     for tile in (1, 7, 64, 149):
         got = [host(t) for t in _run_fwd(hid, W, y, m, 0.7, tile)]
         assert all(np.array_equal(a, b) for a, b in zip(ref, got)), tile
