@@ -2,7 +2,8 @@
 
     python -m entropy_chunked_row_amd.build
 
-Objects go to <repo>/_build/, the library to entropy_chunked_row_amd/liblp.so.
+Objects go to <repo>/_build/, the library to entropy_chunked_row_amd/liblp.so;
+the bench-only read probe to entropy_chunked_row_amd/liblp_probe.so.
 Every call recompiles (it is also the "does it build" check).
 """
 from __future__ import annotations
@@ -19,6 +20,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "liblp.so")
 SOURCES = ["lp_api.hip", "lp_rows.hip", "lp_lmhead.hip", "lp_timing.hip"]
+# measurement helper for bench.py (HBM read probe), a library of its own
+PROBE_SRC = os.path.join(PKG, "probe", "lp_probe.hip")
+PROBE_OUT = os.path.join(PKG, "liblp_probe.so")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -53,8 +57,11 @@ def build(verbose: bool = False) -> str:
     os.makedirs(bdir, exist_ok=True)
     objs = [os.path.join(bdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
     cmds = [[cc, *HIPCC_FLAGS, "-I", INCLUDE, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
+    probe_tmp = PROBE_OUT + ".tmp"
+    cmds.append([cc, *HIPCC_FLAGS, "-shared", "-I", INCLUDE, PROBE_SRC, "-o", probe_tmp])
     with ThreadPoolExecutor(len(cmds)) as ex:
         logs = list(ex.map(_run, cmds))
+    os.replace(probe_tmp, PROBE_OUT)
     tmp = OUT + ".tmp"
     logs.append(_run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]))
     os.replace(tmp, OUT)

@@ -38,6 +38,26 @@ def test_every_declared_symbol_is_exported(lib):
         assert name in _lib.SIGNATURES, f"{name} has no ctypes signature"
 
 
+def test_probe_library_exports_its_declaration():
+    """The bench-only read probe (include/lp_probe.h) is a library of its own;
+    it rejects bad arguments before launching anything."""
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "lp_probe.h")).read(), flags=re.S)
+    names = re.findall(r"^\s*int\s+(lp_probe_[a-z_0-9]+)\s*\(", text, flags=re.M)
+    assert names == ["lp_probe_read"]
+    path = os.path.join(ROOT, "entropy_chunked_row_amd", "liblp_probe.so")
+    if not os.path.exists(path):
+        pytest.skip("liblp_probe.so not built")
+    probe = ctypes.CDLL(path)
+    f = probe.lp_probe_read
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    assert f(None, 1024, 64, FAKE, None) == 1
+    assert f(FAKE, 1000, 64, FAKE, None) == 1      # not a multiple of 16
+    assert f(FAKE, 1024, 0, FAKE, None) == 1
+    assert f(FAKE + 8, 1024, 64, FAKE, None) == 1  # misaligned
+    assert "lp_probe" not in " ".join(header_functions())
+
+
 def test_version_and_status_strings(lib):
     assert lib.lp_version() >= 100
     assert lib.lp_status_string(0) == b"LP_OK"
