@@ -49,14 +49,41 @@ def to_dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
 
 
+def _strip_comments(text):
+    """C++ source without comments and with whitespace runs collapsed: two
+    sources hash alike when they differ only in comments or layout."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            i = text.find("\n", i)
+            i = n if i < 0 else i
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def _csrc_sha256():
+    """Hash of the kernel sources (comments and layout ignored) that the PMC
+    summary in profiles/ must match."""
     import glob
     import hashlib
     h = hashlib.sha256()
     for f in sorted(glob.glob(os.path.join(ROOT, "entropy_chunked_row_amd", "csrc", "*"))):
         h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            h.update(_strip_comments(fh.read()).encode())
     return h.hexdigest()
 
 

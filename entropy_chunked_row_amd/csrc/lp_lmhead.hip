@@ -19,10 +19,11 @@
 //                   log-prob, entropy and log-sum-exp.
 //   backward        k_bwd_dz recomputes the tile's logits with the same GEMM
 //                   and writes dL/dlogits (bf16) in both [row][vocab] and
-//                   [vocab][row] order; k_bwd_dhidden (= dZ . W, K = vocab) and
-//                   k_bwd_dweight (dW += dZ^T . H_tile, K = tile rows) are
-//                   NT GEMMs on those buffers and on transposed copies of W
-//                   and of the tile's hidden rows.
+//                   [vocab][row] order; dHidden (= dZ . W, K = vocab, split
+//                   over K) and dW (+= dZ^T . H_tile, K = tile rows) are NT
+//                   GEMMs on those buffers and on transposed copies of W and
+//                   of the tile's hidden rows.
+//   KL              both models' heads: see the KL section below.
 #include "lp_device.hpp"
 #include "lp_gemm.hpp"
 #include "lp_internal.hpp"
@@ -1227,14 +1228,15 @@ hipError_t launch_lmhead_backward(const LMHeadShape& sh, const float* lse, const
 // DeepSeek-V4 book ch.19 (名词速通 "不实例化 logits", §2 "Teacher
 // Scheduling"): only the last hidden states are kept; the logits of both
 // models are rebuilt through their output heads a tile at a time and reduced
-// to the exact KL directly.  Per (vocab block, row block) the kernel runs two
-// MFMA GEMMs into two accumulator sets (teacher v, then student u), folds
-// them into one dual state per row (the state of the KL on given logits),
-// and a merge kernel combines a row's states in a fixed order.  The backward
-// recomputes both tiles and writes dL/du = g (p_u - p_v) as bf16 for the
-// student's dHidden / dW GEMMs; the teacher is not trained.
+// to the exact KL directly.  Fast path, per chunk of scored rows: a teacher
+// pass (GEMM v, stored as fp32 in accumulator order) and a student pass
+// (GEMM u, whose epilogue reads v back and folds both into one dual state per
+// (row, vocab block), the state of the KL on given logits); a merge kernel
+// combines a row's states in a fixed order.  The generic tile runs both GEMMs
+// into two accumulator sets in one kernel.  The backward recomputes both and
+// writes dL/du = g (p_u - p_v) as bf16 for the student's dHidden / dW GEMMs;
+// the teacher is not trained.
 
-// Two accumulator sets must fit next to the mainloop's registers: 128 vocab x
 // Vocab blocks per group in the KL tiles' walk.
 #ifndef LP_KL_GROUP_V
 #define LP_KL_GROUP_V 4
