@@ -142,6 +142,8 @@ static lp_status check_lmhead(const char* fn, const void* hidden, int64_t ld_h, 
   if (!aligned(targets, 8)) return fail(LP_ERR_INVALID_ARGUMENT, "%s: misaligned targets", fn);
   if (!lp::lmhead_workspace_layout(T, h, V, tile_rows, backward, w))
     return fail(LP_ERR_INVALID_ARGUMENT, "%s: sizes overflow the workspace layout", fn);
+  if (!lp::lmhead_launches_fit(T, h, V, tile_rows, backward))
+    return fail(LP_ERR_UNSUPPORTED, "%s: a launch would exceed 2^32-1 work-items; use a smaller tile_rows", fn);
   if (!workspace || workspace_bytes < w->total)
     return fail(LP_ERR_WORKSPACE_TOO_SMALL, "%s: workspace needs %zu bytes, got %zu", fn, w->total,
                 workspace ? workspace_bytes : size_t(0));
@@ -294,6 +296,8 @@ static lp_status check_kl_heads(const char* fn, const void* hs, int64_t ld_hs, c
   if ((st = check_head(fn, "teacher", ht, ld_ht, wt, ld_wt, h_t)) != LP_OK) return st;
   if (!lp::lmhead_workspace_layout(T, h_s, V, tile_rows, backward ? 3 : 2, w))
     return fail(LP_ERR_INVALID_ARGUMENT, "%s: sizes overflow the workspace layout", fn);
+  if (!lp::lmhead_launches_fit(T, h_s > h_t ? h_s : h_t, V, tile_rows, backward ? 3 : 2))
+    return fail(LP_ERR_UNSUPPORTED, "%s: a launch would exceed 2^32-1 work-items; use a smaller tile_rows", fn);
   if (!workspace || workspace_bytes < w->total)
     return fail(LP_ERR_WORKSPACE_TOO_SMALL, "%s: workspace needs %zu bytes, got %zu", fn, w->total,
                 workspace ? workspace_bytes : size_t(0));
@@ -384,6 +388,7 @@ lp_status lp_kl_full_vocab(const void* student, const void* teacher, lp_dtype dt
   a.ld_t = ld_t;
   a.V = static_cast<int>(V);
   a.T = T;
+  a.row0 = 0;
   a.c = static_cast<float>(kLog2eD);
   a.kl = kl;
   a.targets = targets;

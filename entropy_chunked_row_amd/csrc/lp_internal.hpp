@@ -47,6 +47,7 @@ struct KLArgs {
   int64_t ld_s, ld_t;
   int V;
   int64_t T;
+  int64_t row0;  // first row of the launch (set by the launcher)
   float c;  // log2(e)
   float* kl;
   const int64_t* targets;
@@ -103,6 +104,10 @@ struct LMHeadWorkspace {
 // backward: 0 log-prob forward, 1 log-prob backward, 2 KL forward, 3 KL backward.
 bool lmhead_workspace_layout(int64_t T, int64_t h, int64_t V, int64_t tile_rows, int backward,
                              LMHeadWorkspace* w);
+
+// False when some launch of the call would exceed 2^32 - 1 work-items (a
+// smaller tile_rows fixes it); same modes as lmhead_workspace_layout.
+bool lmhead_launches_fit(int64_t T, int64_t h, int64_t V, int64_t tile_rows, int backward);
 
 // Zero-fill with a kernel (not a memset node, so callers may capture it).
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s);

@@ -127,6 +127,39 @@ bool lmhead_fast_path(const LMHeadShape& sh) {
 
 }  // namespace
 
+// One dispatch covers at most 2^32 - 1 work-items per grid dimension.  True
+// when every launch of the call (fast or generic tiles) stays within that.
+bool lmhead_launches_fit(int64_t T, int64_t h, int64_t V, int64_t tile_rows, int backward) {
+  if (T <= 0) return true;
+  auto cdiv = [](int64_t a, int64_t b) { return (a + b - 1) / b; };
+  const int64_t tr = tile_rows < T ? tile_rows : T;
+  int64_t m = 0;
+  auto add = [&](int64_t blocks, int64_t threads) {
+    if (blocks * threads > m) m = blocks * threads;
+  };
+  if (backward == 0) {
+    const int64_t g = cdiv(T, tr) < kFwdTilesPerLaunch ? cdiv(T, tr) : kFwdTilesPerLaunch;
+    add((cdiv(V, FwdDtlCfg::BM) * cdiv(tr, FwdDtlCfg::BN) + 7) / 8 * 8 * g, FwdDtlCfg::NT);
+    add((cdiv(V, FwdCfg::BM) * cdiv(tr, FwdCfg::BN) + 7) / 8 * 8, FwdCfg::NT);
+    add(cdiv(tr * g, 4), 256);
+  } else if (backward == 2) {
+    const int64_t ch = tr < kKLChunk ? tr : kKLChunk;
+    add(cdiv(V, KLCfg::BM) * cdiv(ch, KLCfg::BN), KLCfg::NT);
+    add(cdiv(V, FwdCfg::BM) * cdiv(ch, FwdCfg::BN), FwdCfg::NT);
+    add(cdiv(ch, 4), 256);
+  } else {
+    add(cdiv(V, BwdDtlCfg::BM) * cdiv(tr, BwdDtlCfg::BN), BwdDtlCfg::NT);
+    add(cdiv(V, BwdCfg::BM) * cdiv(tr, BwdCfg::BN), BwdCfg::NT);
+    add(cdiv(tr, BwdDtlCfg::BM) * cdiv(h, BwdDtlCfg::BN) * kSplitK, BwdDtlCfg::NT);
+    add(cdiv(tr, BwdCfg::BM) * cdiv(h, BwdCfg::BN), BwdCfg::NT);
+    add(cdiv(V, BwdDtlCfg::BM) * cdiv(h, BwdDtlCfg::BN), BwdDtlCfg::NT);
+    add(cdiv(V, BwdCfg::BM) * cdiv(h, BwdCfg::BN), BwdCfg::NT);
+    add(cdiv(V, 64) + 1, 256);   // W^T transpose, x dimension
+    add(cdiv(tr, 64) + 1, 256);  // hidden-tile transpose, x dimension
+  }
+  return m <= 0xffffffffll;
+}
+
 bool lmhead_workspace_layout(int64_t T, int64_t h, int64_t V, int64_t tile_rows, int backward,
                              LMHeadWorkspace* w) {
   if (T < 0 || h <= 0 || V <= 0 || tile_rows <= 0) return false;
@@ -577,11 +610,11 @@ hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s) {
 
 __global__ void __launch_bounds__(256) k_zero_unscored_rows(const uint8_t* __restrict__ mask, int64_t T, int h,
                                                             float* __restrict__ out) {
-  const int64_t row = blockIdx.x;
-  if (row >= T) return;
-  if (mask != nullptr && mask[row] == 0) {
-    float* p = out + row * h;
-    for (int j = threadIdx.x; j < h; j += 256) p[j] = 0.f;
+  for (int64_t row = blockIdx.x; row < T; row += gridDim.x) {
+    if (mask != nullptr && mask[row] == 0) {
+      float* p = out + row * h;
+      for (int j = threadIdx.x; j < h; j += 256) p[j] = 0.f;
+    }
   }
 }
 
@@ -1025,8 +1058,8 @@ hipError_t backward_tiles(const LMHeadShape& sh, bool fast, int bm_fast, int bn_
   if (grad_hidden) {
     {
       TimedLaunch tl("k_zero_unscored_rows", s);
-      hipLaunchKernelGGL(k_zero_unscored_rows, dim3(static_cast<unsigned>(sh.T)), dim3(256), 0, s, sh.mask, sh.T, sh.h,
-                         grad_hidden);
+      const unsigned blocks = static_cast<unsigned>(sh.T < 65536 ? sh.T : 65536);
+      hipLaunchKernelGGL(k_zero_unscored_rows, dim3(blocks), dim3(256), 0, s, sh.mask, sh.T, sh.h, grad_hidden);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // W^T [h x vpad], zero past V

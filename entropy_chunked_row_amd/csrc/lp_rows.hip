@@ -94,18 +94,29 @@ __global__ void __launch_bounds__(NT) k_logprobs_entropy(RowArgs args) {
 #define LP_ROWS_U 8
 #endif
 
+// Rows per launch of the one-row-per-workgroup kernels: keeps a dispatch far
+// below 2^32 work-items for any row count.
+constexpr int64_t kRowsPerLaunch = int64_t(1) << 22;
+
 template <class Tr>
 static hipError_t launch_rows_t(const RowArgs& a, hipStream_t s) {
-  const unsigned grid = static_cast<unsigned>(a.rows);
-  TimedLaunch tl("k_logprobs_entropy", s);
-  if (a.V <= 2048) {
-    hipLaunchKernelGGL((k_logprobs_entropy<Tr, 64, 2>), dim3(grid), dim3(64), 0, s, a);
-  } else if (a.V <= 16384) {
-    hipLaunchKernelGGL((k_logprobs_entropy<Tr, 128, 4>), dim3(grid), dim3(128), 0, s, a);
-  } else {
-    hipLaunchKernelGGL((k_logprobs_entropy<Tr, LP_ROWS_NT, LP_ROWS_U>), dim3(grid), dim3(LP_ROWS_NT), 0, s, a);
+  for (int64_t r0 = 0; r0 < a.rows; r0 += kRowsPerLaunch) {
+    RowArgs b = a;
+    b.row0 = a.row0 + r0;
+    b.rows = a.rows - r0 < kRowsPerLaunch ? a.rows - r0 : kRowsPerLaunch;
+    const unsigned grid = static_cast<unsigned>(b.rows);
+    TimedLaunch tl("k_logprobs_entropy", s);
+    if (b.V <= 2048) {
+      hipLaunchKernelGGL((k_logprobs_entropy<Tr, 64, 2>), dim3(grid), dim3(64), 0, s, b);
+    } else if (b.V <= 16384) {
+      hipLaunchKernelGGL((k_logprobs_entropy<Tr, 128, 4>), dim3(grid), dim3(128), 0, s, b);
+    } else {
+      hipLaunchKernelGGL((k_logprobs_entropy<Tr, LP_ROWS_NT, LP_ROWS_U>), dim3(grid), dim3(LP_ROWS_NT), 0, s, b);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 hipError_t launch_logprobs_entropy(int dtype, const RowArgs& a, hipStream_t s) {
@@ -200,7 +211,7 @@ __device__ __forceinline__ KLState scan_kl(const char* up, const char* vp, int V
 template <class Tr, int NT, int U>
 __global__ void __launch_bounds__(NT) k_kl_full_vocab(KLArgs args) {
   __shared__ KLState sm[NT / 64];
-  const int64_t row = blockIdx.x;
+  const int64_t row = args.row0 + blockIdx.x;
   const char* up = static_cast<const char*>(args.student) + row * args.ld_s * Tr::kBytes;
   const char* vp = static_cast<const char*>(args.teacher) + row * args.ld_t * Tr::kBytes;
   const int V = args.V;
@@ -238,14 +249,20 @@ __global__ void __launch_bounds__(NT) k_kl_full_vocab(KLArgs args) {
 
 template <class Tr>
 static hipError_t launch_kl_t(const KLArgs& a, hipStream_t s) {
-  const unsigned grid = static_cast<unsigned>(a.T);
-  TimedLaunch tl("k_kl_full_vocab", s);
-  if (a.V <= 2048) {
-    hipLaunchKernelGGL((k_kl_full_vocab<Tr, 64, 2>), dim3(grid), dim3(64), 0, s, a);
-  } else {
-    hipLaunchKernelGGL((k_kl_full_vocab<Tr, 256, LP_KL_ROWS_U>), dim3(grid), dim3(256), 0, s, a);
+  for (int64_t r0 = 0; r0 < a.T; r0 += kRowsPerLaunch) {
+    KLArgs b = a;
+    b.row0 = r0;
+    const unsigned grid = static_cast<unsigned>(a.T - r0 < kRowsPerLaunch ? a.T - r0 : kRowsPerLaunch);
+    TimedLaunch tl("k_kl_full_vocab", s);
+    if (b.V <= 2048) {
+      hipLaunchKernelGGL((k_kl_full_vocab<Tr, 64, 2>), dim3(grid), dim3(64), 0, s, b);
+    } else {
+      hipLaunchKernelGGL((k_kl_full_vocab<Tr, 256, LP_KL_ROWS_U>), dim3(grid), dim3(256), 0, s, b);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 hipError_t launch_kl_full_vocab(int dtype, const KLArgs& a, hipStream_t s) {

@@ -177,6 +177,25 @@ def test_lm_head_kl_workspace_and_backward_checks(lib):
                              None, None, None, None, None, None, 0, None) == 0
 
 
+def test_launches_beyond_2_32_work_items_are_refused(lib):
+    """Shapes whose launches would exceed 2^32-1 work-items in one dispatch
+    are refused on the host (LP_ERR_UNSUPPORTED, nothing launched); the same
+    rows with a smaller tile pass the check and only miss the workspace."""
+    big = dict(T=1 << 20, V=1 << 30)
+    st = lib.lp_lm_head_logprobs_entropy(FAKE, 64, FAKE, 64, big["T"], 64, big["V"], FAKE, None, 1.0, 1 << 20, FAKE,
+                                         None, None, FAKE, 1 << 30, None)
+    assert st == 2 and b"2^32" in lib.lp_last_error()
+    st = lib.lp_lm_head_logprobs_entropy_backward(FAKE, 64, FAKE, 64, big["T"], 64, big["V"], FAKE, None, 1.0,
+                                                  1 << 20, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert st == 2 and b"2^32" in lib.lp_last_error()
+    st = lib.lp_lm_head_kl(FAKE, 64, FAKE, 64, 64, FAKE, 64, FAKE, 64, 64, big["T"], 1 << 30, None, None, None,
+                           1 << 20, FAKE, None, None, None, None, None, FAKE, 1 << 30, None)
+    assert st == 2 and b"2^32" in lib.lp_last_error()
+    st = lib.lp_lm_head_logprobs_entropy(FAKE, 64, FAKE, 64, big["T"], 64, 151936, FAKE, None, 1.0, 4096, FAKE,
+                                         None, None, FAKE, 1 << 20, None)
+    assert st == 3, lib.lp_last_error()  # fits; the 1 MiB workspace is what is short
+
+
 def test_product_path_has_no_fallback(tmp_path):
     """A missing library is an error, not a silent CPU path."""
     from entropy_chunked_row_amd import _lib

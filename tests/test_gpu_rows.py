@@ -307,3 +307,25 @@ def test_brute_force_adversarial_small_vocab(V, tau):
             want_lp, want_H = bf_row([float(v) for v in Z[t]], y_col, tau)
             assert abs(lp[t] - want_lp) <= TOL * max(1.0, abs(want_lp)), (t, y_col, lp[t], want_lp)
             assert abs(H[t] - want_H) <= TOL, (t, H[t], want_H)
+
+
+@pytest.mark.timeout(600)
+def test_more_rows_than_one_launch():
+    """Row counts past one launch's 2^22 workgroups: the logits kernel (one
+    chunk of all rows) and the KL on given logits split their launches;
+    every row, including both sides of each split, against the oracle."""
+    T, V = (1 << 22) + 4099, 5
+    rng = np.random.default_rng(2222)
+    u = rng.normal(0, 3, size=(T, V)).astype(np.float32)
+    v = u + rng.normal(0, 0.5, size=u.shape).astype(np.float32)
+    ub, vb = synth.f32_to_bf16_bits(u), synth.f32_to_bf16_bits(v)
+    targets = rng.integers(0, V, size=T).astype(np.int64)
+    mask = (rng.random(T) < 0.75).astype(np.uint8)
+    lp, H = _lp().lp_logprobs_entropy(to_dev_bits(ub, "bf16"), to_dev(targets), to_dev(mask), 0.7, 0)
+    lp_o, H_o, _ = O.logprobs_entropy(O.widen_bf16(ub), targets, mask, 0.7)
+    assert max_abs_err(host(lp), lp_o) <= TOL and max_abs_err(host(H), H_o) <= TOL
+    kl, lpu, lpv, d = _lp().lp_kl_full_vocab(to_dev_bits(ub, "bf16"), to_dev_bits(vb, "bf16"), to_dev(targets),
+                                             to_dev(mask))
+    kl_o, lpu_o, lpv_o, d_o = O.kl_and_prob_diff(O.widen_bf16(ub), O.widen_bf16(vb), targets, mask)
+    for g, w in ((kl, kl_o), (lpu, lpu_o), (lpv, lpv_o), (d, d_o)):
+        assert max_abs_err(host(g), w) <= TOL
