@@ -108,7 +108,10 @@ size_t lp_lm_head_workspace_bytes(int64_t T, int64_t h, int64_t V, int64_t tile_
  *             NULL: log-sum-exp of the tempered logits, saved for the backward.
  * workspace   >= lp_lm_head_workspace_bytes(T, h, V, tile_rows, 0) bytes.
  * Restrictions (LP_ERR_UNSUPPORTED): h % 8 != 0, ld_h % 8 != 0, ld_w % 8 != 0,
- *   misaligned (not 16-byte) hidden or weight pointers.
+ *   misaligned (not 16-byte) hidden or weight pointers, and shapes for which
+ *   one launch would exceed 2^32-1 work-items (about V x min(T, tile_rows)
+ *   past 2^36; a smaller tile_rows avoids it).  The same holds for the
+ *   backward and for the KL through the heads.
  */
 lp_status lp_lm_head_logprobs_entropy(const void* hidden, int64_t ld_h, const void* weight, int64_t ld_w,
                                       int64_t T, int64_t h, int64_t V, const int64_t* targets,
