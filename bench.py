@@ -120,7 +120,7 @@ def _events_ms(torch, fn, steps):
     return a.elapsed_time(b)
 
 
-SETTLE_SECONDS = 1.0  # set from --settle-seconds in main()
+SETTLE_SECONDS = 2.0  # set from --settle-seconds in main()
 
 
 def _timed(lp, torch, fn, steps, warmup, kernels):
@@ -484,7 +484,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--paths", default="all", help="comma list of " + ",".join(ALL_PATHS))
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline (0 = skip)")
-    ap.add_argument("--settle-seconds", type=float, default=1.0,
+    ap.add_argument("--settle-seconds", type=float, default=2.0,
                     help="untimed seconds of each path's step before its warm-up steps (steady GPU clocks)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB (reference for HBM counters)")
