@@ -172,7 +172,8 @@ def bench_lm_head_fwd(lp, torch, np, synth, O, steps, warmup, cpu_seconds):
                  f"tau {cfg.temperature}, tile {cfg.tile_rows}",
         T=cfg.T, scored_rows=Ts, h=cfg.h, V=cfg.V, temperature=cfg.temperature, tile_rows=cfg.tile_rows,
         ms_per_step=ms / steps, tokens_per_s=Ts * steps / (ms * 1e-3),
-        roofline=dict(bound="mfma", kernel="k_fwd_tile", achieved=achieved, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+        roofline=dict(bound="mfma", kernel="k_fwd_tile", kernel_ms_per_launch=gemm_ms / n_launch,
+                      achieved=achieved, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
                       frac=achieved / BF16_PEAK_TFLOPS, traffic=measured_traffic("k_fwd_tile"),
                       traffic_unit="HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                       algorithmic_hbm_bytes_per_launch=(n_tiles * cfg.V * cfg.h * 2 + Ts * cfg.h * 2) / (n_launch / steps),
@@ -260,7 +261,8 @@ def bench_logits_input(lp, torch, np, synth, O, steps, warmup):
         workload=f"logits input: bf16 [{cfg.T}, {cfg.V}] ({Ts} scored rows), tau {cfg.temperature}, "
                  f"chunk {cfg.chunk_rows}",
         ms_per_step=ms / steps, tokens_per_s=Ts * steps / (ms * 1e-3),
-        roofline=dict(bound="hbm", kernel="k_logprobs_entropy", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
+        roofline=dict(bound="hbm", kernel="k_logprobs_entropy", kernel_ms_per_launch=kms / n_launch,
+                      achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
                       frac=achieved / HBM_PEAK_GBS, traffic=measured_traffic("k_logprobs_entropy"),
                       traffic_unit="HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                       algorithmic_bytes_per_launch=bytes_step / (n_launch / steps),
@@ -291,7 +293,8 @@ def bench_kl(lp, torch, np, synth, O, steps, warmup):
     res = dict(
         workload=f"exact KL(teacher||student) + target log-probs + masked prob diff: fp16 [{cfg.T}, {cfg.V}] x 2",
         ms_per_step=ms / steps, tokens_per_s=cfg.T * steps / (ms * 1e-3),
-        roofline=dict(bound="hbm", kernel="k_kl_full_vocab", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
+        roofline=dict(bound="hbm", kernel="k_kl_full_vocab", kernel_ms_per_launch=kms / n_launch,
+                      achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
                       frac=achieved / HBM_PEAK_GBS, traffic=measured_traffic("k_kl_full_vocab"),
                       traffic_unit="HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                       algorithmic_bytes_per_launch=bytes_step / (n_launch / steps),
