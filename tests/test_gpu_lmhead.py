@@ -324,3 +324,39 @@ def test_hidden_past_4_gib_takes_generic_tiles():
         assert fro <= TOL_GRAD and mad <= TOL_GRAD, (nm, fro, mad)
     nonzero_rows = (dH != 0).any(dim=1).cpu().numpy()
     assert not nonzero_rows[mask == 0].any()
+
+
+@pytest.mark.parametrize("h", [64, 72])  # direct-to-LDS and generic tiles
+def test_extreme_logit_scales(h):
+    """Large-magnitude logits (|z| in the hundreds: W ~ N(0, 4^2)) and
+    near-one-hot rows (one vocab row of W boosted, so p ~ 1 and H ~ 0):
+    forward against the oracle, backward within the gradient tolerance."""
+    T, V = 70, 1500
+    rng = np.random.default_rng(h + 11)
+    hid = synth.f32_to_bf16_bits(rng.normal(0, 1, size=(T, h)).astype(np.float32))
+    for w_sigma, boost in ((4.0, 0.0), (0.02, 40.0)):
+        W = rng.normal(0, w_sigma, size=(V, h)).astype(np.float32)
+        if boost:
+            W[7] = boost * np.sign(O.widen_bf16(hid).mean(0)).astype(np.float32)  # row 7 wins every token
+        Wb = synth.f32_to_bf16_bits(W)
+        y = rng.integers(0, V, size=T).astype(np.int64)
+        y[::3] = 7
+        m = (rng.random(T) < 0.8).astype(np.uint8)
+        lp, H, lse = _run_fwd(hid, Wb, y, m, 0.7, 32)
+        lp_o, H_o, lse_o = O.lm_head_logprobs_entropy(O.widen_bf16(hid), O.widen_bf16(Wb), y, m, 0.7)
+        # log-probs of unlikely targets reach -1200: fp32 logits of that size carry rounding proportional to
+        # it (2^-24 per operation over the h-term sum), so the bound adds 2e-6 of the value to the fused 2e-3
+        lph = host(lp)
+        assert np.all(np.abs(lph - lp_o) <= TOL_FWD + 2e-6 * np.abs(lp_o)), (w_sigma, np.abs(lph - lp_o).max())
+        assert max_abs_err(host(H), H_o) <= TOL_FWD and np.all(np.isfinite(lph))
+        assert np.all(np.abs(host(lse) - lse_o) <= TOL_FWD + 2e-6 * np.abs(lse_o))
+        rng2 = np.random.default_rng(5)
+        g_lp = rng2.normal(0, 1, size=T).astype(np.float32)
+        g_H = rng2.normal(0, 0.1, size=T).astype(np.float32)
+        dH, dW = _lp().lp_lm_head_logprobs_entropy_backward(
+            to_dev_bits(hid, "bf16"), to_dev_bits(Wb, "bf16"), to_dev(y), to_dev(m), 0.7, 32, lse, H, to_dev(g_lp),
+            to_dev(g_H))
+        dH_o, dW_o = O.lm_head_backward(O.widen_bf16(hid), O.widen_bf16(Wb), y, m, 0.7, g_lp, g_H)
+        for got, want in ((host(dH), dH_o), (host(dW), dW_o)):
+            fro, mad = grad_errors(got, want)
+            assert fro <= TOL_GRAD and mad <= TOL_GRAD, (w_sigma, fro, mad)
