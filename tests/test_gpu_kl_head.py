@@ -178,3 +178,27 @@ def test_kl_head_matches_kl_on_fp32_logits():
     kl_l, lps_l, lpt_l, _ = _lp().lp_kl_full_vocab(to_dev(U), to_dev(Vt), y, None)
     assert max_abs_err(host(kl_f), host(kl_l)) <= 2e-5
     assert max_abs_err(host(lps_f), host(lps_l)) <= 2e-5 and max_abs_err(host(lpt_f), host(lpt_l)) <= 2e-5
+
+
+def test_kl_head_extreme_logit_scales():
+    """Logits in the hundreds (W ~ N(0, 4^2)): an unrelated teacher (KL in the
+    tens) and a teacher that differs from the student in one weight row only
+    (KL small while both logits are large: the cancellation case)."""
+    T, h, V = 60, 64, 1200
+    rng = np.random.default_rng(808)
+    hs = synth.f32_to_bf16_bits(rng.normal(0, 1, size=(T, h)).astype(np.float32))
+    ws = rng.normal(0, 4, size=(V, h)).astype(np.float32)
+    for name, wt, ht in (("unrelated", rng.normal(0, 4, size=(V, h)).astype(np.float32), hs),
+                         ("one row apart", ws.copy(), hs)):
+        if name == "one row apart":
+            wt[3] += rng.normal(0, 0.5, size=h).astype(np.float32)
+        A = dict(student_hidden=hs, student_weight=synth.f32_to_bf16_bits(ws), teacher_hidden=ht,
+                 teacher_weight=synth.f32_to_bf16_bits(wt))
+        y = rng.integers(0, V, size=T).astype(np.int64)
+        got = [host(t) for t in _lp().lp_lm_head_kl(*_dev_heads(A), None, to_dev(y), None, 16)]
+        want = O.lm_head_kl(*_wide(A), None, y, None)
+        kl, kl_o = got[0], want[0]
+        assert np.all(np.isfinite(kl)) and np.all(kl > -1e-3), name
+        assert np.all(np.abs(kl - kl_o) <= TOL_FWD + 2e-6 * np.abs(kl_o)), (name, np.abs(kl - kl_o).max())
+        for g, w in zip(got[4:], want[4:]):  # both log-normalisers, in the hundreds
+            assert np.all(np.abs(g - w) <= TOL_FWD + 2e-6 * np.abs(w)), name
