@@ -493,8 +493,8 @@ def main():
                     help="first run one plain device-to-device copy of this many MiB (reference for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
-              "(rows shard with no exchange; see DESIGN.md for how the path would shard)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(rows would shard across GPUs with no exchange in the forward paths)", file=sys.stderr)
         sys.exit(2)
     paths = ALL_PATHS if args.paths == "all" else tuple(p.strip() for p in args.paths.split(","))
     global SETTLE_SECONDS

@@ -729,27 +729,39 @@ __device__ __forceinline__ void dz_epilogue(const DzArgs& a, f32x16_t (&acc)[C::
   const int vlane = v0 + wm * C::WTM + 4 * (lane >> 5);
   const bool full_block = v0 + C::BM <= a.V;  // uniform: every vocab column of the block exists
   const float it = a.inv_tau;
+  // dZ = it * [sum_k g_k onehot_k - p (gsum + gH (z it - mu))] = it * sum_k g_k onehot_k - p (A + B z).
+  // The per-row constants of all token columns, as two batches of independent
+  // loads (row indices, then the rows' values) rather than one dependent pair
+  // per column; row 0 stands in for columns past the valid rows.
+  int64_t row_n[C::NI], y0_n[C::NI];
+  float l2_n[C::NI], A_n[C::NI], B_n[C::NI], g0_n[C::NI];
+#pragma unroll
+  for (int ni = 0; ni < C::NI; ++ni) {
+    const int r = n0 + wn * C::WTN + ni * 32 + (lane & 31);
+    row_n[ni] = r < rows ? a.idx[a.tile_base + r] : 0;
+  }
+#pragma unroll
+  for (int ni = 0; ni < C::NI; ++ni) {
+    const int64_t row = row_n[ni];
+    const float L = a.lse[row];
+    const float mu = L - a.entropy[row];
+    y0_n[ni] = a.targets[row * a.K];
+    g0_n[ni] = a.g_lp[row * a.K];
+    float gsum = g0_n[ni];
+    for (int k = 1; k < a.K; ++k) gsum += a.g_lp[row * a.K + k];
+    const float gh = a.g_H ? a.g_H[row] : 0.f;
+    l2_n[ni] = L * kLog2eF;
+    A_n[ni] = it * fmaf(-gh, mu, gsum);
+    B_n[ni] = it * it * gh;
+  }
 #pragma unroll
   for (int ni = 0; ni < C::NI; ++ni) {
     const int r = n0 + wn * C::WTN + ni * 32 + (lane & 31);
     if (r >= rowsK) continue;
     const bool valid = r < rows;
-    // dZ = it * [sum_k g_k onehot_k - p (gsum + gH (z it - mu))] = it * sum_k g_k onehot_k - p (A + B z)
-    int64_t row = 0, y0 = -1;
-    float l2 = 0.f, A = 0.f, B = 0.f, g0 = 0.f;
-    if (valid) {
-      row = a.idx[a.tile_base + r];
-      const float L = a.lse[row];
-      l2 = L * kLog2eF;
-      const float mu = L - a.entropy[row];
-      y0 = a.targets[row * a.K];
-      g0 = a.g_lp[row * a.K];
-      float gsum = g0;
-      for (int k = 1; k < a.K; ++k) gsum += a.g_lp[row * a.K + k];
-      const float gh = a.g_H ? a.g_H[row] : 0.f;
-      A = it * fmaf(-gh, mu, gsum);
-      B = it * it * gh;
-    }
+    const int64_t row = row_n[ni], y0 = valid ? y0_n[ni] : -1;
+    const float l2 = valid ? l2_n[ni] : 0.f, A = valid ? A_n[ni] : 0.f, B = valid ? B_n[ni] : 0.f;
+    const float g0 = valid ? g0_n[ni] : 0.f;
 #pragma unroll
     for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll

@@ -36,8 +36,8 @@ same numbers up to rounding order, so the definition *is* the oracle:
   through its own output head: DeepSeek-V4 book ch.19, 名词速通
   "不实例化 logits" and §2 "Teacher Scheduling".
 
-Readings taken where the pages are silent are listed in the design doc; the main
-ones are repeated next to the code that takes them.
+Where the pages are silent, the reading taken is stated next to the code
+that takes it.
 """
 from __future__ import annotations
 
