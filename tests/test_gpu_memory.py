@@ -76,3 +76,58 @@ def test_workspace_far_below_a_logits_buffer():
     assert fw < 32768 * 151936 * 4 / 50  # partial states of up to 8 tiles of 4096 rows
     assert bw < 114688 * 151936 * 4 / 10
     assert kl < 16384 * 129280 * 4 / 3  # one 4096-row chunk of the teacher's fp32 logits, no [T x V]
+
+
+def test_no_rows_through_the_c_abi():
+    """T = 0 (and n = 0): every entry point returns OK; a backward still
+    defines the weight gradient of an empty sum, so a requested dW is
+    overwritten with zeros; the aggregates of no position are count 0 and a
+    NaN Pearson."""
+    import math
+    import torch
+    from entropy_chunked_row_amd import _lib
+    lib = _lib.load()
+    h, V, K, tile = 64, 300, 2, 16
+    dev = "cuda"
+    bf = lambda *shape: torch.zeros(shape, dtype=torch.bfloat16, device=dev)
+    f32 = lambda *shape: torch.zeros(shape, dtype=torch.float32, device=dev)
+    hid, W = bf(1, h), bf(V, h)
+    y = torch.zeros(K, dtype=torch.int64, device=dev)
+    m = torch.ones(1, dtype=torch.uint8, device=dev)
+    outs = [f32(K) for _ in range(6)]
+    dH = f32(1, h)
+    s = torch.cuda.current_stream().cuda_stream
+    p = lambda t: t.data_ptr()
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
+    n = ws.numel()
+
+    def dw_sentinel():
+        return torch.full((V, h), 7.0, dtype=torch.float32, device=dev)
+
+    assert lib.lp_lm_head_logprobs_entropy(p(hid), h, p(W), h, 0, h, V, p(y), p(m), 0.7, tile, p(outs[0]), p(outs[1]),
+                                           p(outs[2]), p(ws), n, s) == 0
+    assert lib.lp_lm_head_logprobs_entropy_k(p(hid), h, p(W), h, 0, h, V, p(y), K, p(m), 0.7, tile, p(outs[0]),
+                                             p(outs[1]), p(outs[2]), p(ws), n, s) == 0
+    assert lib.lp_logprobs_entropy_k(p(W), 0, 0, V, V, p(y), K, p(m), 0.7, 4, p(outs[0]), p(outs[1]), s) == 0
+    assert lib.lp_lm_head_kl(p(hid), h, p(W), h, h, p(hid), h, p(W), h, h, 0, V, p(m), p(y), p(m), tile,
+                             *[p(o) for o in outs], p(ws), n, s) == 0
+    dW = dw_sentinel()
+    assert lib.lp_lm_head_logprobs_entropy_backward(p(hid), h, p(W), h, 0, h, V, p(y), p(m), 0.7, tile, p(outs[2]),
+                                                    p(outs[1]), p(outs[0]), p(outs[3]), p(dH), p(dW), p(ws), n, s) == 0
+    torch.cuda.synchronize()
+    assert not dW.any()
+    dW = dw_sentinel()
+    assert lib.lp_lm_head_logprobs_entropy_backward_k(p(hid), h, p(W), h, 0, h, V, p(y), K, p(m), 0.7, tile,
+                                                      p(outs[2]), p(outs[1]), p(outs[0]), p(outs[3]), p(dH), p(dW),
+                                                      p(ws), n, s) == 0
+    torch.cuda.synchronize()
+    assert not dW.any()
+    dW = dw_sentinel()
+    assert lib.lp_lm_head_kl_backward(p(hid), h, p(W), h, h, p(hid), h, p(W), h, h, 0, V, p(m), tile, p(outs[4]),
+                                      p(outs[5]), p(outs[0]), p(dH), p(dW), p(ws), n, s) == 0
+    torch.cuda.synchronize()
+    assert not dW.any()
+    stats = torch.full((5,), 7.0, dtype=torch.float64, device=dev)
+    assert lib.lp_prob_diff_stats(p(outs[0]), p(outs[1]), None, 0, p(stats), p(ws), n, s) == 0
+    got = stats.cpu().tolist()
+    assert got[:4] == [0.0, 0.0, 0.0, 0.0] and math.isnan(got[4])
