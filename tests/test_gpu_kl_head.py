@@ -46,6 +46,7 @@ def _wide(A):
 @pytest.mark.parametrize("T,hs,ht,V,tile", [
     (50, 40, 72, 1031, 16),      # generic path (h % 64 != 0), ragged tiles and vocab block
     (300, 128, 256, 5000, 128),  # fast path, different widths, partial last vocab block
+    (70, 64, 72, 999, 32),       # student width on the fast path, teacher width not
     (130, 64, 64, 512, 4096),    # fast path, one tile, vocab a multiple of the block
 ])
 def test_kl_head_forward_backward(T, hs, ht, V, tile):

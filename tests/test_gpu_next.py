@@ -44,7 +44,8 @@ def test_k1_matches_single_target_bitwise():
     assert np.array_equal(host(a), host(b)[:, 0]) and np.array_equal(host(ha), host(hb))
 
 
-@pytest.mark.parametrize("T,h,V,K,tile", [(40, 64, 1031, 4, 16), (300, 256, 5000, 16, 128)])
+@pytest.mark.parametrize("T,h,V,K,tile", [(40, 64, 1031, 4, 16), (300, 256, 5000, 16, 128),
+                                            (45, 72, 777, 3, 16)])  # the last: generic tiles (h % 64 != 0)
 def test_lm_head_k_forward_backward(T, h, V, K, tile):
     rng = np.random.default_rng(T + K)
     hid = synth.f32_to_bf16_bits(rng.normal(0, 1, size=(T, h)).astype(np.float32))
