@@ -1,6 +1,7 @@
 // C ABI of liblp.so (declared in include/lp.h): argument validation, chunk /
 // tile scheduling and stream-ordered launches.  Every check runs on the host
 // before anything is launched; a rejected call touches no output.
+#include <initializer_list>
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -42,6 +43,13 @@ float exp2_scale(float temperature) {
 }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Every fp32 array argument (NULL allowed) must be 4-byte aligned.
+bool f32_aligned(std::initializer_list<const float*> ps) {
+  for (const float* p : ps)
+    if (p && !aligned(p, 4)) return false;
+  return true;
+}
 
 size_t dtype_bytes(int d) { return d == LP_FP32 ? 4 : 2; }
 
@@ -183,6 +191,7 @@ static lp_status lm_head_forward_impl(const char* fn, const void* hidden, int64_
   if (st != LP_OK) return st;
   if (T == 0) return ok();
   if (!logprob) return fail(LP_ERR_INVALID_ARGUMENT, "%s: logprob is required", fn);
+  if (!f32_aligned({logprob, entropy, lse})) return fail(LP_ERR_INVALID_ARGUMENT, "%s: misaligned fp32 output", fn);
   lp::LMHeadShape sh = make_shape(hidden, ld_h, weight, ld_w, T, h, V, targets, K, mask, temperature, tile_rows);
   hipError_t e = lp::launch_lmhead_forward(sh, logprob, entropy, lse, static_cast<char*>(workspace), w,
                                            static_cast<hipStream_t>(stream));
@@ -219,6 +228,8 @@ static lp_status lm_head_backward_impl(const char* fn, const void* hidden, int64
   lp_status st = check_lmhead(fn, hidden, ld_h, weight, ld_w, T, h, V, targets, temperature, tile_rows,
                               workspace, workspace_bytes, 1, &w);
   if (st != LP_OK) return st;
+  if (!f32_aligned({lse, entropy, grad_logprob, grad_entropy, grad_hidden, grad_weight}))
+    return fail(LP_ERR_INVALID_ARGUMENT, "%s: misaligned fp32 argument", fn);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (T == 0) {
     // no rows: the weight gradient is still defined (all zero)
@@ -321,6 +332,8 @@ lp_status lp_lm_head_kl(const void* student_hidden, int64_t ld_hs, const void* s
   if (T == 0) return ok();
   if (!kl) return fail(LP_ERR_INVALID_ARGUMENT, "%s: kl is required", fn);
   if (targets && !aligned(targets, 8)) return fail(LP_ERR_INVALID_ARGUMENT, "%s: misaligned targets", fn);
+  if (!f32_aligned({kl, lp_student, lp_teacher, prob_diff, lse_student, lse_teacher}))
+    return fail(LP_ERR_INVALID_ARGUMENT, "%s: misaligned fp32 output", fn);
   const lp::LMHeadShape su = make_shape(student_hidden, ld_hs, student_weight, ld_ws, T, h_student, V, targets, 1,
                                         mask, 1.0f, tile_rows);
   const lp::LMHeadShape te = make_shape(teacher_hidden, ld_ht, teacher_weight, ld_wt, T, h_teacher, V, targets, 1,
@@ -343,6 +356,8 @@ lp_status lp_lm_head_kl_backward(const void* student_hidden, int64_t ld_hs, cons
   lp_status st = check_kl_heads(fn, student_hidden, ld_hs, student_weight, ld_ws, h_student, teacher_hidden, ld_ht,
                                 teacher_weight, ld_wt, h_teacher, T, V, tile_rows, workspace, workspace_bytes, 1, &w);
   if (st != LP_OK) return st;
+  if (!f32_aligned({lse_student, lse_teacher, grad_kl, grad_hidden, grad_weight}))
+    return fail(LP_ERR_INVALID_ARGUMENT, "%s: misaligned fp32 argument", fn);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (T == 0) {
     if (grad_weight) {
@@ -379,7 +394,7 @@ lp_status lp_kl_full_vocab(const void* student, const void* teacher, lp_dtype dt
   if (T > 0x7fffffff) return fail(LP_ERR_UNSUPPORTED, "%s: more than 2^31-1 rows", fn);
   if (!student || !teacher || !kl) return fail(LP_ERR_INVALID_ARGUMENT, "%s: student, teacher, kl required", fn);
   if (!aligned(student, dtype_bytes(dtype)) || !aligned(teacher, dtype_bytes(dtype)) ||
-      (targets && !aligned(targets, 8)))
+      (targets && !aligned(targets, 8)) || !f32_aligned({kl, lp_student, lp_teacher, prob_diff}))
     return fail(LP_ERR_INVALID_ARGUMENT, "%s: misaligned pointer", fn);
   lp::KLArgs a;
   a.student = student;
@@ -406,6 +421,7 @@ lp_status lp_prob_diff(const float* lp_a, const float* lp_b, const uint8_t* mask
   if (n < 0) return fail(LP_ERR_INVALID_ARGUMENT, "lp_prob_diff: n < 0");
   if (n == 0) return ok();
   if (!lp_a || !lp_b || !out) return fail(LP_ERR_INVALID_ARGUMENT, "lp_prob_diff: lp_a, lp_b, out required");
+  if (!f32_aligned({lp_a, lp_b, out})) return fail(LP_ERR_INVALID_ARGUMENT, "lp_prob_diff: misaligned pointer");
   hipError_t e = lp::launch_prob_diff(lp_a, lp_b, mask, n, out, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "lp_prob_diff");
   return ok();
@@ -419,6 +435,7 @@ lp_status lp_prob_diff_stats(const float* lp_a, const float* lp_b, const uint8_t
   if (n < 0) return fail(LP_ERR_INVALID_ARGUMENT, "%s: n < 0", fn);
   if (!out) return fail(LP_ERR_INVALID_ARGUMENT, "%s: out is required", fn);
   if (n > 0 && (!lp_a || !lp_b)) return fail(LP_ERR_INVALID_ARGUMENT, "%s: lp_a and lp_b are required", fn);
+  if (!f32_aligned({lp_a, lp_b})) return fail(LP_ERR_INVALID_ARGUMENT, "%s: misaligned lp_a or lp_b", fn);
   if (!workspace || workspace_bytes < lp::prob_diff_stats_workspace_bytes())
     return fail(LP_ERR_WORKSPACE_TOO_SMALL, "%s: workspace needs %zu bytes", fn, lp::prob_diff_stats_workspace_bytes());
   if (!aligned(workspace, 256) || !aligned(out, 8))

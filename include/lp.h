@@ -13,6 +13,11 @@
  * Layout: row-major.  A [rows x cols] matrix has row r at base + r * ld
  *   elements, ld >= cols.  Targets are int64, one per row.  A mask is uint8,
  *   one per row, nonzero = the row is scored; NULL = every row is scored.
+ * Alignment: every array is aligned to its element size (fp32 to 4 bytes,
+ *   int64 and fp64 to 8, bf16/fp16 logits to 2), or the call returns
+ *   LP_ERR_INVALID_ARGUMENT; the fused paths' bf16 hidden states and weights
+ *   must be 16-byte aligned (LP_ERR_UNSUPPORTED otherwise) and a workspace
+ *   256-byte aligned.
  * Streams: `stream` is a hipStream_t (NULL = the null stream).  Calls are
  *   asynchronous on it; outputs are valid once the stream reaches the call.
  * Errors: every argument is checked on the host before anything is launched.

@@ -216,3 +216,30 @@ def test_package_never_imports_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.replace("Oracle", "").lower() or f.endswith((".hip", ".hpp")) and \
                     "import" not in text, f
+
+
+def test_misaligned_fp32_arguments_are_rejected(lib):
+    """Every fp32 array must be 4-byte aligned: the checks run on the host,
+    before any launch, so fake device addresses are enough here."""
+    mis = FAKE + 2
+    ws = 1 << 30
+    # fused forward: a misaligned output
+    st = lib.lp_lm_head_logprobs_entropy(FAKE, 64, FAKE, 64, 8, 64, 100, FAKE, None, 1.0, 4, mis, None, None,
+                                         FAKE, ws, None)
+    assert st == 1 and b"misaligned" in lib.lp_last_error()
+    # fused backward: a misaligned gradient output, also with no rows (it would be zero-filled)
+    for T in (8, 0):
+        st = lib.lp_lm_head_logprobs_entropy_backward(FAKE, 64, FAKE, 64, T, 64, 100, FAKE, None, 1.0, 4, FAKE, FAKE,
+                                                      FAKE, None, None, mis, FAKE, ws, None)
+        assert st == 1 and b"misaligned" in lib.lp_last_error(), T
+    # KL through the heads, forward and backward
+    st = lib.lp_lm_head_kl(FAKE, 64, FAKE, 64, 64, FAKE, 64, FAKE, 64, 64, 8, 100, None, None, None, 4, mis, None,
+                           None, None, None, None, FAKE, ws, None)
+    assert st == 1 and b"misaligned" in lib.lp_last_error()
+    st = lib.lp_lm_head_kl_backward(FAKE, 64, FAKE, 64, 64, FAKE, 64, FAKE, 64, 64, 8, 100, None, 4, FAKE, FAKE, mis,
+                                    None, None, FAKE, ws, None)
+    assert st == 1 and b"misaligned" in lib.lp_last_error()
+    # KL on given logits, the prob diff and its aggregates
+    assert lib.lp_kl_full_vocab(FAKE, FAKE, 0, 8, 100, 100, 100, mis, None, None, None, None, None, None) == 1
+    assert lib.lp_prob_diff(FAKE, mis, None, 8, FAKE, None) == 1
+    assert lib.lp_prob_diff_stats(mis, FAKE, None, 8, FAKE, FAKE, ws, None) == 1

@@ -360,3 +360,41 @@ def test_extreme_logit_scales(h):
         for got, want in ((host(dH), dH_o), (host(dW), dW_o)):
             fro, mad = grad_errors(got, want)
             assert fro <= TOL_GRAD and mad <= TOL_GRAD, (w_sigma, fro, mad)
+
+
+def test_backward_with_grad_hidden_not_16_byte_aligned():
+    """h % 64 == 0 takes the direct-to-LDS backward only when grad_hidden is
+    16-byte aligned (its split-K reduction stores 16 bytes at a time); a
+    4-byte-aligned grad_hidden takes the generic tiles.  Both match the
+    oracle, and dW agrees between the two within the gradient tolerance."""
+    torch = _torch()
+    from entropy_chunked_row_amd import _lib
+    lib = _lib.load()
+    T, h, V, tile, tau = 90, 128, 1500, 32, 0.7
+    hid, W, y, m = _case(T, h, V, seed=91)
+    rng = np.random.default_rng(92)
+    g = rng.normal(0, 1, T).astype(np.float32)
+    gh = rng.normal(0, 0.1, T).astype(np.float32)
+    hd, Wd = to_dev_bits(hid, "bf16"), to_dev_bits(W, "bf16")
+    yd, md, gd, ghd = to_dev(y), to_dev(m), to_dev(g), to_dev(gh)
+    _, H, lse = _run_fwd(hid, W, y, m, tau, tile)
+    dH_o, dW_o = O.lm_head_backward(O.widen_bf16(hid), O.widen_bf16(W), y, m, tau, g, gh)
+    nb = lib.lp_lm_head_workspace_bytes(T, h, V, tile, 1)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    p = lambda t: t.data_ptr()
+    got = []
+    for off in (0, 1):  # element offset into a padded buffer: 0 = 16-byte aligned, 1 = 4-byte aligned only
+        buf = torch.empty(T * h + 4, dtype=torch.float32, device="cuda")
+        dH = buf[off:off + T * h].view(T, h)
+        assert (dH.data_ptr() % 16 == 0) == (off == 0)
+        dW = torch.empty((V, h), dtype=torch.float32, device="cuda")
+        st = lib.lp_lm_head_logprobs_entropy_backward(p(hd), h, p(Wd), h, T, h, V, p(yd), p(md), tau, tile, p(lse),
+                                                      p(H), p(gd), p(ghd), p(dH), p(dW), p(ws), nb, s)
+        assert st == 0, lib.lp_last_error()
+        got.append((host(dH), host(dW)))
+        for nm, a, b in (("dH", got[-1][0], dH_o), ("dW", got[-1][1], dW_o)):
+            fro, mad = grad_errors(a, b)
+            assert fro <= TOL_GRAD and mad <= TOL_GRAD, (off, nm, fro, mad)
+    fro, mad = grad_errors(got[1][1], got[0][1])
+    assert fro <= TOL_GRAD and mad <= TOL_GRAD
