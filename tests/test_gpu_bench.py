@@ -1,0 +1,39 @@
+"""bench.py's one-line JSON contract, on a short run of the headline path and
+the logits-input path (in-process: no child program is started from a
+process that already uses the GPU)."""
+import json
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+pytestmark = pytest.mark.gpu
+
+
+def test_bench_prints_one_json_line_with_the_contract(monkeypatch, capsys):
+    import bench
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--paths", "lm_head_fwd,logits_input", "--steps", "2",
+                                      "--warmup", "1", "--settle-seconds", "0.2", "--cpu-seconds", "1"])
+    bench.main()
+    lines = [ln for ln in capsys.readouterr().out.splitlines() if ln.strip()]
+    assert len(lines) == 1
+    d = json.loads(lines[0])
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
+                "scaling", "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline"):
+        assert key in d, key
+    assert d["n_gpus"] == 1 and d["steps"] == 2 and d["warmup"] == 1
+    assert d["value"] > 0 and d["ms_per_step"] > 0 and d["higher_is_better"] is True
+    assert d["dtype"] == "bf16" and d["data"] == "synthetic" and d["vs_baseline"] is None
+    assert isinstance(d["config"]["workload"], str) and "model" not in d["config"]
+    r = d["roofline"]
+    assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s" and r["peak"] == 2500.0
+    assert r["achieved"] > 0 and abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-12
+    assert r["traffic"] is None or r["traffic"] > 0
+    c = d["cpu_baseline"]
+    assert c["kind"] == "oracle" and c["value"] > 0 and c["cores"] >= 1 and isinstance(c["sample"], str)
+    assert c["parity_max_abs_err"] <= c["parity_tol"]
+    li = d["paths"]["logits_input"]["roofline"]
+    assert li["bound"] == "hbm" and li["unit"] == "GB/s" and li["peak"] == 8000.0 and 0 < li["frac"] < 1.5
