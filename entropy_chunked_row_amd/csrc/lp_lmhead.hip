@@ -235,33 +235,56 @@ static ZeroOuts zero_outs(float* a = nullptr, int wa = 1, float* b = nullptr, fl
 
 __global__ void __launch_bounds__(1024) k_compact(const uint8_t* __restrict__ mask, int64_t T, int* __restrict__ idx,
                                                   int* __restrict__ count, ZeroOuts z) {
-  __shared__ int sums[1024];
+  // Rounds of 1024 x R rows; thread t owns rows [base + R t, base + R t + R),
+  // so the workgroup reads each round's mask bytes together and an exclusive
+  // scan of the per-thread counts (wave shuffles, then the 16 wave totals)
+  // gives ascending positions.
+  constexpr int R = 16;
+  __shared__ int wsum[16];
   const int tid = threadIdx.x;
-  const int64_t per = (T + 1023) / 1024;
-  const int64_t b = tid * per;
-  const int64_t e = (b + per < T) ? b + per : T;
-  int c = 0;
-  for (int64_t i = b; i < e; ++i) c += (mask == nullptr || mask[i] != 0) ? 1 : 0;
-  sums[tid] = c;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int v = tid >= off ? sums[tid - off] : 0;
-    __syncthreads();
-    sums[tid] += v;
-    __syncthreads();
-  }
-  int pos = sums[tid] - c;
-  for (int64_t i = b; i < e; ++i) {
-    if (mask == nullptr || mask[i] != 0) {
-      idx[pos++] = static_cast<int>(i);
-    } else {
+  const int lane = tid & 63, wave = tid >> 6;
+  int total = 0;  // scored rows before this round (uniform)
+  for (int64_t base = 0; base < T; base += 1024 * R) {
+    const int64_t b = base + static_cast<int64_t>(tid) * R;
+    unsigned bits = 0;
 #pragma unroll
-      for (int q = 0; q < 6; ++q)
-        if (z.p[q])
-          for (int k = 0; k < z.width[q]; ++k) z.p[q][i * z.width[q] + k] = 0.f;
+    for (int j = 0; j < R; ++j) {
+      const int64_t i = b + j;
+      if (i < T && (mask == nullptr || mask[i] != 0)) bits |= 1u << j;
     }
+    const int c = __popc(bits);
+    int incl = c;  // inclusive scan over the wave
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += v;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int before = 0, round_total = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+      const int v = wsum[w];
+      before += w < wave ? v : 0;
+      round_total += v;
+    }
+    int pos = total + before + incl - c;
+    for (int j = 0; j < R; ++j) {
+      const int64_t i = b + j;
+      if (i >= T) break;
+      if ((bits >> j) & 1u) {
+        idx[pos++] = static_cast<int>(i);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 6; ++q)
+          if (z.p[q])
+            for (int k = 0; k < z.width[q]; ++k) z.p[q][i * z.width[q] + k] = 0.f;
+      }
+    }
+    total += round_total;
+    __syncthreads();  // wsum is rewritten by the next round
   }
-  if (tid == 1023) *count = sums[1023];
+  if (tid == 0) *count = total;
 }
 
 // ---------------------------------------------------------------------------
