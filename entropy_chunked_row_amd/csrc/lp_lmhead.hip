@@ -43,7 +43,7 @@ constexpr float kLog2eF = 1.44269504088896340736f;
 #endif
 using FwdCfg = GemmCfg<LP_FWD_TILE>;
 #ifndef LP_FWD_DTL_TILE
-#define LP_FWD_DTL_TILE 256, 256, 4, 2
+#define LP_FWD_DTL_TILE 256, 320, 4, 2
 #endif
 // Minimum waves per SIMD the forward tile is compiled for (register budget).
 #ifndef LP_FWD_MIN_WAVES
@@ -139,7 +139,7 @@ bool lmhead_launches_fit(int64_t T, int64_t h, int64_t V, int64_t tile_rows, int
   };
   if (backward == 0) {
     const int64_t g = cdiv(T, tr) < kFwdTilesPerLaunch ? cdiv(T, tr) : kFwdTilesPerLaunch;
-    add((cdiv(V, FwdDtlCfg::BM) * cdiv(tr, FwdDtlCfg::BN) + 7) / 8 * 8 * g, FwdDtlCfg::NT);
+    add((cdiv(V, FwdDtlCfg::BM) * cdiv(tr * g, FwdDtlCfg::BN) + 7) / 8 * 8, FwdDtlCfg::NT);
     add((cdiv(V, FwdCfg::BM) * cdiv(tr, FwdCfg::BN) + 7) / 8 * 8, FwdCfg::NT);
     add(cdiv(tr * g, 4), 256);
   } else if (backward == 2) {
@@ -302,45 +302,38 @@ struct FwdArgs {
   const int64_t* targets;  // [T x K]
   int K;
   float c;
-  int64_t tile_base;  // first compacted row of the launch's first tile
-  int tile_rows;
-  int n_vb, n_nb;
-  int bpt;      // blocks per tile in the grid (n_vb * n_nb rounded up to a multiple of 8)
-  float* part;  // [tiles x tile_rows][n_vb][3]
-  float* zy;    // [tiles x tile_rows][K]
+  int64_t tile_base;  // first compacted row of the launch
+  int tile_rows;      // rows of the launch (its tiles together)
+  int n_vb, n_nb;     // vocab blocks, row blocks of the launch
+  float* part;        // [tile_rows][n_vb][3]
+  float* zy;          // [tile_rows][K]
 };
 
-// Block -> (tile, vocab block, row block) of a launch over consecutive tiles.
-// Logical order: group of kGroupV vocab blocks -> tile -> row block -> vocab
-// block within the group, and each XCD (hardware puts workgroup b on XCD
-// b % 8) walks one contiguous range of that order.  A group's weight rows thus
-// serve every tile of the launch back to back while they are still cached
-// (1.1 % faster than finishing one tile before the next, which streams the
-// whole weight from HBM once per tile); inside a tile, consecutive workgroups
-// on one XCD share both weight and hidden strips in its L2.  Shifts the
-// arguments to tile t; false for the padding blocks.
-__device__ __forceinline__ bool fwd_block(FwdArgs& a, int& vb, int& nb) {
-  const int ntile = static_cast<int>(gridDim.x) / a.bpt;
-  const int L = xcd_remap(static_cast<int>(blockIdx.x), a.bpt * ntile);
+// Block -> (vocab block, row block) of a launch.  The fast forward blocks the
+// rows of all the tiles of its launch as one sequence (row blocks may straddle
+// tiles; every row's result is the same either way), so only the launch's last
+// row block is partly filled.  Logical order: group of kGroupV vocab blocks ->
+// row block -> vocab block within the group, and each XCD (hardware puts
+// workgroup b on XCD b % 8) walks one contiguous range of that order: a
+// group's weight rows serve every row of the launch back to back while they
+// are still cached (the weight comes from HBM once per launch, not once per
+// tile), and the 32 workgroups an XCD runs at once cover 4 vocab blocks x 8
+// row blocks, which share their strips in its L2.  False for padding blocks.
+__device__ __forceinline__ bool fwd_block(const FwdArgs& a, int& vb, int& nb) {
+  const int L = xcd_remap(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
   constexpr int G = kGroupV;
   const int full = a.n_vb / G;
-  const int span = G * a.n_nb * ntile;  // blocks of a full group
+  const int span = G * a.n_nb;  // blocks of a full group
   const int g = L / span;
   int gsz = G, w = L - g * span, v0 = g * G;
   if (g >= full) {  // the last, smaller group, then padding
     gsz = a.n_vb - full * G;
     w = L - full * span;
     v0 = full * G;
-    if (gsz == 0 || w >= gsz * a.n_nb * ntile) return false;
+    if (gsz == 0 || w >= gsz * a.n_nb) return false;
   }
-  const int t = w / (gsz * a.n_nb);
-  const int w2 = w - t * gsz * a.n_nb;
-  nb = w2 / gsz;
-  vb = v0 + w2 % gsz;
-  const int64_t r0 = static_cast<int64_t>(t) * a.tile_rows;
-  a.tile_base += r0;
-  a.part += r0 * a.n_vb * 3;
-  a.zy += r0 * a.K;
+  nb = w / gsz;
+  vb = v0 + w % gsz;
   return true;
 }
 
@@ -459,7 +452,8 @@ __global__ void __launch_bounds__(C::NT) k_fwd_tile(FwdArgs a) {
   fwd_epilogue<C>(a, acc, vb, n0, rows, lds);
 }
 
-// Fast forward tile (h % 64 == 0): direct-to-LDS loads, 256 x 256 block.
+// Fast forward tile (h % 64 == 0): direct-to-LDS loads, 256 (vocab) x 320
+// (rows) block.
 template <class C>
 __global__ void __launch_bounds__(C::NT, LP_FWD_MIN_WAVES) k_fwd_tile_dtl(FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t lds[C::LDS_ELEMS];
@@ -539,12 +533,13 @@ hipError_t launch_lmhead_forward(const LMHeadShape& sh, float* logprob, float* e
   const int bm = fast ? FwdDtlCfg::BM : FwdCfg::BM;
   const int bn = fast ? FwdDtlCfg::BN : FwdCfg::BN;
   const int n_vb = (sh.V + bm - 1) / bm;
-  const int n_nb = static_cast<int>((tr + bn - 1) / bn);
-  const int bpt = (n_vb * n_nb + 7) / 8 * 8;
   const int64_t group = fast ? kFwdTilesPerLaunch : 1;
   for (int64_t base = 0; base < sh.T; base += group * tr) {
     const int64_t left = (sh.T - base + tr - 1) / tr;
     const int ntile = static_cast<int>(left < group ? left : group);
+    // the launch's ntile * tr rows in row blocks of bn, vocab blocks of bm
+    const int n_nb = static_cast<int>((tr * ntile + bn - 1) / bn);
+    const int grid_blocks = (n_vb * n_nb + 7) / 8 * 8;
     FwdArgs a;
     a.weight = sh.weight;
     a.ld_w = sh.ld_w;
@@ -558,15 +553,14 @@ hipError_t launch_lmhead_forward(const LMHeadShape& sh, float* logprob, float* e
     a.K = sh.K;
     a.c = sh.c;
     a.tile_base = base;
-    a.tile_rows = static_cast<int>(tr);
+    a.tile_rows = static_cast<int>(tr * ntile);
     a.n_vb = n_vb;
     a.n_nb = n_nb;
-    a.bpt = bpt;
     a.part = part;
     a.zy = zy;
     {
       TimedLaunch tl("k_fwd_tile", s);
-      const dim3 grid(static_cast<unsigned>(bpt) * ntile);
+      const dim3 grid(static_cast<unsigned>(grid_blocks));
       if (fast)
         hipLaunchKernelGGL(k_fwd_tile_dtl<FwdDtlCfg>, grid, dim3(FwdDtlCfg::NT), 0, s, a);
       else
