@@ -62,6 +62,11 @@ constexpr int kFwdTilesPerLaunch = LP_FWD_TILES_PER_LAUNCH;
 #define LP_BWD_DTL_TILE 256, 256, 4, 2
 #endif
 using BwdDtlCfg = DtlCfg<LP_BWD_DTL_TILE>;
+// The backward's dense gradient GEMMs (dHidden, dW): N is the hidden width.
+#ifndef LP_DENSE_DTL_TILE
+#define LP_DENSE_DTL_TILE 256, 256, 4, 2
+#endif
+using DenseDtlCfg = DtlCfg<LP_DENSE_DTL_TILE>;
 // KL through both heads on the fast path: two passes per chunk of at most
 // kKLChunk scored rows on this tile.  The teacher pass stores its fp32 logits
 // for the chunk; the student pass's epilogue reads them back.  Measured on
@@ -150,9 +155,9 @@ bool lmhead_launches_fit(int64_t T, int64_t h, int64_t V, int64_t tile_rows, int
   } else {
     add(cdiv(V, BwdDtlCfg::BM) * cdiv(tr, BwdDtlCfg::BN), BwdDtlCfg::NT);
     add(cdiv(V, BwdCfg::BM) * cdiv(tr, BwdCfg::BN), BwdCfg::NT);
-    add(cdiv(tr, BwdDtlCfg::BM) * cdiv(h, BwdDtlCfg::BN) * kSplitK, BwdDtlCfg::NT);
+    add(cdiv(tr, DenseDtlCfg::BM) * cdiv(h, DenseDtlCfg::BN) * kSplitK, DenseDtlCfg::NT);
     add(cdiv(tr, BwdCfg::BM) * cdiv(h, BwdCfg::BN), BwdCfg::NT);
-    add(cdiv(V, BwdDtlCfg::BM) * cdiv(h, BwdDtlCfg::BN), BwdDtlCfg::NT);
+    add(cdiv(V, DenseDtlCfg::BM) * cdiv(h, DenseDtlCfg::BN), DenseDtlCfg::NT);
     add(cdiv(V, BwdCfg::BM) * cdiv(h, BwdCfg::BN), BwdCfg::NT);
     add(cdiv(V, 64) + 1, 256);   // W^T transpose, x dimension
     add(cdiv(tr, 64) + 1, 256);  // hidden-tile transpose, x dimension
@@ -1079,7 +1084,7 @@ hipError_t backward_tiles(const LMHeadShape& sh, bool fast, int bm_fast, int bn_
                           float* grad_weight,
                           char* ws, const LMHeadWorkspace& w, hipStream_t s, LaunchDz&& launch_dz) {
   using C = BwdCfg;
-  using F = BwdDtlCfg;
+  using F = DenseDtlCfg;
   int* idx = reinterpret_cast<int*>(ws + w.idx_off);
   int* count = reinterpret_cast<int*>(ws + w.count_off);
   const int64_t tr = sh.tile_rows < sh.T ? sh.tile_rows : sh.T;
