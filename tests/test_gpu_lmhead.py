@@ -165,8 +165,11 @@ def test_full_size_forward_sampled_rows(lm_full):
     cfg, A, hd, Wd, y, m = lm_full
     lp, H, lse = (host(t) for t in _lp().lp_lm_head_logprobs_entropy(hd, Wd, y, m, cfg.temperature, cfg.tile_rows))
     scored = np.nonzero(A["mask"])[0]
+    # besides random rows: first and last scored row, the first tile boundary (4095 | 4096) and the second
+    # (8191 | 8192), both inside one 320-row block of the forward, and a row-block boundary (3839 | 3840)
     rows = np.unique(np.concatenate([np.random.default_rng(8).choice(scored, 12, replace=False),
-                                     scored[:1], scored[-1:], scored[4095:4097]]))
+                                     scored[:1], scored[-1:], scored[4095:4097], scored[8191:8193],
+                                     scored[3839:3841]]))
     lp_o, H_o, lse_o = _oracle_rows(A, rows, cfg.temperature)
     assert max_abs_err(lp[rows], lp_o) <= TOL_FWD
     assert max_abs_err(H[rows], H_o) <= TOL_FWD
