@@ -2,7 +2,9 @@
 large vocabulary on MI355X.
 
 Functions carry the C names (include/lp.h).  This layer only marshals
-arguments: it checks tensor placement and layout, allocates outputs and
+arguments: it checks dtypes, layouts, the length of every per-row array
+(T, or T x K for the K-target calls) and that every tensor sits on the main
+operand's device, all before anything is launched; it allocates outputs and
 workspace with torch (device memory is all torch is used for) and passes raw
 pointers plus the current HIP stream.  Every number is computed by the HIP
 kernels; if liblp.so is missing, every call raises.
@@ -48,6 +50,17 @@ def _dev(t, name):
         raise ValueError(f"{name} must be a device (GPU) tensor")
 
 
+def _on(device, **tensors):
+    """Every given tensor lives on `device` (checked after all shapes, so a
+    wrong length is reported as such even for host tensors)."""
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        _dev(t, name)
+        if t.device != device:
+            raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
 def _rows(t, name):
     """2-D tensor with unit stride along columns; returns its leading dimension."""
     if t.dim() != 2 or t.stride(1) != 1:
@@ -55,7 +68,10 @@ def _rows(t, name):
     return t.stride(0) if t.size(0) > 1 else max(t.stride(0), t.size(1))
 
 
-def _vec(t, name, dtype=None):
+def _vec(t, name, dtype=None, n=None):
+    """Contiguous tensor of `dtype` (bool accepted for uint8) holding exactly
+    `n` elements when n is given: a short per-row array would be read past
+    its end by the kernels, so it is refused here."""
     if t is None:
         return None
     torch = _torch()
@@ -66,7 +82,17 @@ def _vec(t, name, dtype=None):
             raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    _dev(t, name)
+    if n is not None and t.numel() != n:
+        raise ValueError(f"{name} must have {n} elements, got {t.numel()}")
+    return t
+
+
+def _bf16_2d(t, name):
+    torch = _torch()
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D")
     return t
 
 
@@ -99,11 +125,15 @@ def lp_logprobs_entropy(logits, targets, mask=None, temperature: float = 1.0, ch
     """(logprob[T], entropy[T] or None) of model-precision logits [T, V]."""
     torch = _torch()
     lib = load()
-    _dev(logits, "logits")
+    if logits.dim() != 2:
+        raise ValueError("logits must be 2-D [T, V]")
     T, V = logits.shape
     ld = _rows(logits, "logits")
-    targets = _vec(targets, "targets", torch.int64)
-    mask = _vec(mask, "mask", torch.uint8)
+    targets = _vec(targets, "targets", torch.int64, T)
+    mask = _vec(mask, "mask", torch.uint8, T)
+    logprob = _vec(logprob, "logprob", torch.float32, T)
+    entropy = _vec(entropy, "entropy", torch.float32, T)
+    _on(logits.device, logits=logits, targets=targets, mask=mask, logprob=logprob, entropy=entropy)
     if logprob is None:
         logprob = torch.empty(T, dtype=torch.float32, device=logits.device)
     if want_entropy and entropy is None:
@@ -119,12 +149,29 @@ def lp_lm_head_workspace_bytes(T: int, h: int, V: int, tile_rows: int, backward:
 
 
 def _workspace(nbytes: int, device, workspace):
+    """(tensor, size in bytes): the caller's workspace after checks, or a new one."""
     torch = _torch()
     if workspace is not None:
-        if workspace.numel() * workspace.element_size() < nbytes:
-            raise ValueError("workspace too small")
-        return workspace
-    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        if not workspace.is_contiguous():
+            raise ValueError("workspace must be contiguous")
+        _on(device, workspace=workspace)
+        size = workspace.numel() * workspace.element_size()
+        if size < nbytes:
+            raise ValueError(f"workspace too small: {size} bytes, {nbytes} needed")
+        return workspace, size
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    return ws, ws.numel()
+
+
+def _lm_head_operands(hidden, weight):
+    """(T, h, V) of bf16 hidden [T, h] and weight [V, h]."""
+    _bf16_2d(hidden, "hidden")
+    _bf16_2d(weight, "weight")
+    T, h = hidden.shape
+    V, h2 = weight.shape
+    if h2 != h:
+        raise ValueError("hidden and weight disagree on h")
+    return T, h, V
 
 
 def lp_lm_head_logprobs_entropy(hidden, weight, targets, mask=None, temperature: float = 1.0,
@@ -133,25 +180,19 @@ def lp_lm_head_logprobs_entropy(hidden, weight, targets, mask=None, temperature:
     """(logprob, entropy, lse) of softmax(hidden @ weight^T / temperature); bf16 hidden [T, h], weight [V, h]."""
     torch = _torch()
     lib = load()
-    _dev(hidden, "hidden")
-    _dev(weight, "weight")
-    if hidden.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16:
-        raise TypeError("hidden and weight must be bfloat16")
-    T, h = hidden.shape
-    V, h2 = weight.shape
-    if h2 != h:
-        raise ValueError("hidden and weight disagree on h")
-    targets = _vec(targets, "targets", torch.int64)
-    mask = _vec(mask, "mask", torch.uint8)
+    T, h, V = _lm_head_operands(hidden, weight)
+    ld_h, ld_w = _rows(hidden, "hidden"), _rows(weight, "weight")
+    targets = _vec(targets, "targets", torch.int64, T)
+    mask = _vec(mask, "mask", torch.uint8, T)
     dev = hidden.device
+    _on(dev, hidden=hidden, weight=weight, targets=targets, mask=mask)
     lp = torch.empty(T, dtype=torch.float32, device=dev)
     H = torch.empty(T, dtype=torch.float32, device=dev) if want_entropy else None
     lse = torch.empty(T, dtype=torch.float32, device=dev) if want_lse else None
-    nbytes = lp_lm_head_workspace_bytes(T, h, V, tile_rows, False)
-    ws = _workspace(nbytes, dev, workspace)
-    st = lib.lp_lm_head_logprobs_entropy(_ptr(hidden), _rows(hidden, "hidden"), _ptr(weight), _rows(weight, "weight"),
-                                         T, h, V, _ptr(targets), _ptr(mask), float(temperature), int(tile_rows),
-                                         _ptr(lp), _ptr(H), _ptr(lse), _ptr(ws), ws.numel(), _stream(stream))
+    ws, ws_bytes = _workspace(lp_lm_head_workspace_bytes(T, h, V, tile_rows, False), dev, workspace)
+    st = lib.lp_lm_head_logprobs_entropy(_ptr(hidden), ld_h, _ptr(weight), ld_w, T, h, V, _ptr(targets), _ptr(mask),
+                                         float(temperature), int(tile_rows), _ptr(lp), _ptr(H), _ptr(lse), _ptr(ws),
+                                         ws_bytes, _stream(stream))
     check("lp_lm_head_logprobs_entropy", st)
     return lp, H, lse
 
@@ -163,25 +204,24 @@ def lp_lm_head_logprobs_entropy_backward(hidden, weight, targets, mask, temperat
     """(grad_hidden fp32 [T, h] or None, grad_weight fp32 [V, h] or None)."""
     torch = _torch()
     lib = load()
-    _dev(hidden, "hidden")
-    _dev(weight, "weight")
-    T, h = hidden.shape
-    V = weight.shape[0]
-    targets = _vec(targets, "targets", torch.int64)
-    mask = _vec(mask, "mask", torch.uint8)
-    lse = _vec(lse, "lse", torch.float32)
-    entropy = _vec(entropy, "entropy", torch.float32)
-    grad_logprob = _vec(grad_logprob, "grad_logprob", torch.float32)
-    grad_entropy = _vec(grad_entropy, "grad_entropy", torch.float32)
+    T, h, V = _lm_head_operands(hidden, weight)
+    ld_h, ld_w = _rows(hidden, "hidden"), _rows(weight, "weight")
+    targets = _vec(targets, "targets", torch.int64, T)
+    mask = _vec(mask, "mask", torch.uint8, T)
+    lse = _vec(lse, "lse", torch.float32, T)
+    entropy = _vec(entropy, "entropy", torch.float32, T)
+    grad_logprob = _vec(grad_logprob, "grad_logprob", torch.float32, T)
+    grad_entropy = _vec(grad_entropy, "grad_entropy", torch.float32, T)
     dev = hidden.device
+    _on(dev, hidden=hidden, weight=weight, targets=targets, mask=mask, lse=lse, entropy=entropy,
+        grad_logprob=grad_logprob, grad_entropy=grad_entropy)
     dH = torch.empty((T, h), dtype=torch.float32, device=dev) if need_grad_hidden else None
     dW = torch.empty((V, h), dtype=torch.float32, device=dev) if need_grad_weight else None
-    nbytes = lp_lm_head_workspace_bytes(T, h, V, tile_rows, True)
-    ws = _workspace(nbytes, dev, workspace)
+    ws, ws_bytes = _workspace(lp_lm_head_workspace_bytes(T, h, V, tile_rows, True), dev, workspace)
     st = lib.lp_lm_head_logprobs_entropy_backward(
-        _ptr(hidden), _rows(hidden, "hidden"), _ptr(weight), _rows(weight, "weight"), T, h, V, _ptr(targets),
-        _ptr(mask), float(temperature), int(tile_rows), _ptr(lse), _ptr(entropy), _ptr(grad_logprob),
-        _ptr(grad_entropy), _ptr(dH), _ptr(dW), _ptr(ws), ws.numel(), _stream(stream))
+        _ptr(hidden), ld_h, _ptr(weight), ld_w, T, h, V, _ptr(targets), _ptr(mask), float(temperature),
+        int(tile_rows), _ptr(lse), _ptr(entropy), _ptr(grad_logprob), _ptr(grad_entropy), _ptr(dH), _ptr(dW),
+        _ptr(ws), ws_bytes, _stream(stream))
     check("lp_lm_head_logprobs_entropy_backward", st)
     return dH, dW
 
@@ -191,23 +231,22 @@ def lp_kl_full_vocab(student, teacher, targets=None, diff_mask=None, *, want_tar
     """(kl, lp_student, lp_teacher, prob_diff); the last three are None without targets."""
     torch = _torch()
     lib = load()
-    _dev(student, "student")
-    _dev(teacher, "teacher")
-    if student.dtype != teacher.dtype or student.shape != teacher.shape:
-        raise ValueError("student and teacher must have the same dtype and shape")
+    if student.dtype != teacher.dtype or student.shape != teacher.shape or student.dim() != 2:
+        raise ValueError("student and teacher must be 2-D with the same dtype and shape")
     T, V = student.shape
-    targets = _vec(targets, "targets", torch.int64)
-    diff_mask = _vec(diff_mask, "diff_mask", torch.uint8)
+    ld_s, ld_t = _rows(student, "student"), _rows(teacher, "teacher")
+    targets = _vec(targets, "targets", torch.int64, T)
+    diff_mask = _vec(diff_mask, "diff_mask", torch.uint8, T)
     dev = student.device
+    _on(dev, student=student, teacher=teacher, targets=targets, diff_mask=diff_mask)
     kl = torch.empty(T, dtype=torch.float32, device=dev)
     lps = lpt = diff = None
     if targets is not None and want_target_logprobs:
         lps = torch.empty(T, dtype=torch.float32, device=dev)
         lpt = torch.empty(T, dtype=torch.float32, device=dev)
         diff = torch.empty(T, dtype=torch.float32, device=dev)
-    st = lib.lp_kl_full_vocab(_ptr(student), _ptr(teacher), _dtype_code(student), T, V, _rows(student, "student"),
-                              _rows(teacher, "teacher"), _ptr(kl), _ptr(targets), _ptr(diff_mask), _ptr(lps),
-                              _ptr(lpt), _ptr(diff), _stream(stream))
+    st = lib.lp_kl_full_vocab(_ptr(student), _ptr(teacher), _dtype_code(student), T, V, ld_s, ld_t, _ptr(kl),
+                              _ptr(targets), _ptr(diff_mask), _ptr(lps), _ptr(lpt), _ptr(diff), _stream(stream))
     check("lp_kl_full_vocab", st)
     return kl, lps, lpt, diff
 
@@ -217,11 +256,11 @@ def lp_prob_diff(lp_a, lp_b, mask=None, *, out=None, stream=None):
     torch = _torch()
     lib = load()
     lp_a = _vec(lp_a, "lp_a", torch.float32)
-    lp_b = _vec(lp_b, "lp_b", torch.float32)
-    mask = _vec(mask, "mask", torch.uint8)
     n = lp_a.numel()
-    if lp_b.numel() != n or (mask is not None and mask.numel() != n):
-        raise ValueError("lp_a, lp_b and mask must have the same length")
+    lp_b = _vec(lp_b, "lp_b", torch.float32, n)
+    mask = _vec(mask, "mask", torch.uint8, n)
+    out = _vec(out, "out", torch.float32, n)
+    _on(lp_a.device, lp_a=lp_a, lp_b=lp_b, mask=mask, out=out)
     if out is None:
         out = torch.empty(n, dtype=torch.float32, device=lp_a.device)
     st = lib.lp_prob_diff(_ptr(lp_a), _ptr(lp_b), _ptr(mask), n, _ptr(out), _stream(stream))
@@ -232,7 +271,7 @@ def lp_prob_diff(lp_a, lp_b, mask=None, *, out=None, stream=None):
 def _targets_k(targets, T):
     torch = _torch()
     t = _vec(targets, "targets", torch.int64)
-    if t.dim() != 2 or t.size(0) != T:
+    if t is None or t.dim() != 2 or t.size(0) != T:
         raise ValueError("targets must be [T, K]")
     return t, t.size(1)
 
@@ -242,15 +281,17 @@ def lp_logprobs_entropy_k(logits, targets, mask=None, temperature: float = 1.0, 
     """(logprob [T, K], entropy [T] or None) with K targets per row (targets [T, K] int64)."""
     torch = _torch()
     lib = load()
-    _dev(logits, "logits")
+    if logits.dim() != 2:
+        raise ValueError("logits must be 2-D [T, V]")
     T, V = logits.shape
+    ld = _rows(logits, "logits")
     targets, K = _targets_k(targets, T)
-    mask = _vec(mask, "mask", torch.uint8)
+    mask = _vec(mask, "mask", torch.uint8, T)
+    _on(logits.device, logits=logits, targets=targets, mask=mask)
     lp = torch.empty((T, K), dtype=torch.float32, device=logits.device)
     H = torch.empty(T, dtype=torch.float32, device=logits.device) if want_entropy else None
-    st = lib.lp_logprobs_entropy_k(_ptr(logits), _dtype_code(logits), T, V, _rows(logits, "logits"), _ptr(targets), K,
-                                   _ptr(mask), float(temperature), int(chunk_rows), _ptr(lp), _ptr(H),
-                                   _stream(stream))
+    st = lib.lp_logprobs_entropy_k(_ptr(logits), _dtype_code(logits), T, V, ld, _ptr(targets), K, _ptr(mask),
+                                   float(temperature), int(chunk_rows), _ptr(lp), _ptr(H), _stream(stream))
     check("lp_logprobs_entropy_k", st)
     return lp, H
 
@@ -260,21 +301,19 @@ def lp_lm_head_logprobs_entropy_k(hidden, weight, targets, mask=None, temperatur
     """(logprob [T, K], entropy [T], lse [T]) of the fused LM head with K targets per row."""
     torch = _torch()
     lib = load()
-    _dev(hidden, "hidden")
-    _dev(weight, "weight")
-    T, h = hidden.shape
-    V = weight.shape[0]
+    T, h, V = _lm_head_operands(hidden, weight)
+    ld_h, ld_w = _rows(hidden, "hidden"), _rows(weight, "weight")
     targets, K = _targets_k(targets, T)
-    mask = _vec(mask, "mask", torch.uint8)
+    mask = _vec(mask, "mask", torch.uint8, T)
     dev = hidden.device
+    _on(dev, hidden=hidden, weight=weight, targets=targets, mask=mask)
     lp = torch.empty((T, K), dtype=torch.float32, device=dev)
     H = torch.empty(T, dtype=torch.float32, device=dev)
     lse = torch.empty(T, dtype=torch.float32, device=dev)
-    ws = _workspace(lp_lm_head_workspace_bytes(T, h, V, tile_rows, False), dev, workspace)
-    st = lib.lp_lm_head_logprobs_entropy_k(_ptr(hidden), _rows(hidden, "hidden"), _ptr(weight),
-                                           _rows(weight, "weight"), T, h, V, _ptr(targets), K, _ptr(mask),
-                                           float(temperature), int(tile_rows), _ptr(lp), _ptr(H), _ptr(lse), _ptr(ws),
-                                           ws.numel(), _stream(stream))
+    ws, ws_bytes = _workspace(lp_lm_head_workspace_bytes(T, h, V, tile_rows, False), dev, workspace)
+    st = lib.lp_lm_head_logprobs_entropy_k(_ptr(hidden), ld_h, _ptr(weight), ld_w, T, h, V, _ptr(targets), K,
+                                           _ptr(mask), float(temperature), int(tile_rows), _ptr(lp), _ptr(H),
+                                           _ptr(lse), _ptr(ws), ws_bytes, _stream(stream))
     check("lp_lm_head_logprobs_entropy_k", st)
     return lp, H, lse
 
@@ -286,23 +325,26 @@ def lp_lm_head_logprobs_entropy_backward_k(hidden, weight, targets, mask, temper
     """Backward of the K-target fused LM head; grad_logprob is [T, K]."""
     torch = _torch()
     lib = load()
-    T, h = hidden.shape
-    V = weight.shape[0]
+    T, h, V = _lm_head_operands(hidden, weight)
+    ld_h, ld_w = _rows(hidden, "hidden"), _rows(weight, "weight")
     targets, K = _targets_k(targets, T)
-    mask = _vec(mask, "mask", torch.uint8)
-    grad_logprob = _vec(grad_logprob, "grad_logprob", torch.float32)
-    if grad_logprob.shape != (T, K):
+    mask = _vec(mask, "mask", torch.uint8, T)
+    lse = _vec(lse, "lse", torch.float32, T)
+    entropy = _vec(entropy, "entropy", torch.float32, T)
+    grad_logprob = _vec(grad_logprob, "grad_logprob", torch.float32, T * K)
+    if grad_logprob is None or grad_logprob.shape != (T, K):
         raise ValueError("grad_logprob must be [T, K]")
-    grad_entropy = _vec(grad_entropy, "grad_entropy", torch.float32)
+    grad_entropy = _vec(grad_entropy, "grad_entropy", torch.float32, T)
     dev = hidden.device
+    _on(dev, hidden=hidden, weight=weight, targets=targets, mask=mask, lse=lse, entropy=entropy,
+        grad_logprob=grad_logprob, grad_entropy=grad_entropy)
     dH = torch.empty((T, h), dtype=torch.float32, device=dev) if need_grad_hidden else None
     dW = torch.empty((V, h), dtype=torch.float32, device=dev) if need_grad_weight else None
-    ws = _workspace(lp_lm_head_workspace_bytes(T, h, V, tile_rows, True), dev, workspace)
+    ws, ws_bytes = _workspace(lp_lm_head_workspace_bytes(T, h, V, tile_rows, True), dev, workspace)
     st = lib.lp_lm_head_logprobs_entropy_backward_k(
-        _ptr(hidden), _rows(hidden, "hidden"), _ptr(weight), _rows(weight, "weight"), T, h, V, _ptr(targets), K,
-        _ptr(mask), float(temperature), int(tile_rows), _ptr(_vec(lse, "lse", torch.float32)),
-        _ptr(_vec(entropy, "entropy", torch.float32)), _ptr(grad_logprob), _ptr(grad_entropy), _ptr(dH), _ptr(dW),
-        _ptr(ws), ws.numel(), _stream(stream))
+        _ptr(hidden), ld_h, _ptr(weight), ld_w, T, h, V, _ptr(targets), K, _ptr(mask), float(temperature),
+        int(tile_rows), _ptr(lse), _ptr(entropy), _ptr(grad_logprob), _ptr(grad_entropy), _ptr(dH), _ptr(dW),
+        _ptr(ws), ws_bytes, _stream(stream))
     check("lp_lm_head_logprobs_entropy_backward_k", st)
     return dH, dW
 
@@ -312,11 +354,13 @@ def lp_prob_diff_stats(lp_a, lp_b, mask=None, *, stream=None):
     torch = _torch()
     lib = load()
     lp_a = _vec(lp_a, "lp_a", torch.float32)
-    lp_b = _vec(lp_b, "lp_b", torch.float32)
-    mask = _vec(mask, "mask", torch.uint8)
+    n = lp_a.numel()
+    lp_b = _vec(lp_b, "lp_b", torch.float32, n)
+    mask = _vec(mask, "mask", torch.uint8, n)
+    _on(lp_a.device, lp_a=lp_a, lp_b=lp_b, mask=mask)
     out = torch.empty(5, dtype=torch.float64, device=lp_a.device)
     ws = torch.empty(max(int(lib.lp_prob_diff_stats_workspace_bytes()), 256), dtype=torch.uint8, device=lp_a.device)
-    st = lib.lp_prob_diff_stats(_ptr(lp_a), _ptr(lp_b), _ptr(mask), lp_a.numel(), _ptr(out), _ptr(ws), ws.numel(),
+    st = lib.lp_prob_diff_stats(_ptr(lp_a), _ptr(lp_b), _ptr(mask), n, _ptr(out), _ptr(ws), ws.numel(),
                                 _stream(stream))
     check("lp_prob_diff_stats", st)
     return out
@@ -327,22 +371,21 @@ def lp_lm_head_kl_workspace_bytes(T: int, h_student: int, V: int, tile_rows: int
 
 
 def _heads(student_hidden, student_weight, teacher_hidden, teacher_weight):
-    torch = _torch()
     for t, n in ((student_hidden, "student_hidden"), (student_weight, "student_weight"),
                  (teacher_hidden, "teacher_hidden"), (teacher_weight, "teacher_weight")):
-        _dev(t, n)
-        if t.dtype != torch.bfloat16:
-            raise TypeError(f"{n} must be bfloat16")
+        _bf16_2d(t, n)
     T, hs = student_hidden.shape
     V, hs2 = student_weight.shape
     T2, ht = teacher_hidden.shape
     V2, ht2 = teacher_weight.shape
     if hs2 != hs or ht2 != ht or T2 != T or V2 != V:
         raise ValueError("student / teacher hidden and weight shapes disagree")
-    return (T, V, hs, ht,
-            [_ptr(student_hidden), _rows(student_hidden, "student_hidden"), _ptr(student_weight),
-             _rows(student_weight, "student_weight"), hs, _ptr(teacher_hidden), _rows(teacher_hidden, "teacher_hidden"),
-             _ptr(teacher_weight), _rows(teacher_weight, "teacher_weight"), ht])
+    args = [_ptr(student_hidden), _rows(student_hidden, "student_hidden"), _ptr(student_weight),
+            _rows(student_weight, "student_weight"), hs, _ptr(teacher_hidden), _rows(teacher_hidden, "teacher_hidden"),
+            _ptr(teacher_weight), _rows(teacher_weight, "teacher_weight"), ht]
+    tensors = dict(student_hidden=student_hidden, student_weight=student_weight, teacher_hidden=teacher_hidden,
+                   teacher_weight=teacher_weight)
+    return T, V, hs, ht, args, tensors
 
 
 def lp_lm_head_kl(student_hidden, student_weight, teacher_hidden, teacher_weight, mask=None, targets=None,
@@ -351,11 +394,12 @@ def lp_lm_head_kl(student_hidden, student_weight, teacher_hidden, teacher_weight
     model (bf16 hiddens [T, h_*], weights [V, h_*]); the target outputs are None without targets."""
     torch = _torch()
     lib = load()
-    T, V, hs, ht, head_args = _heads(student_hidden, student_weight, teacher_hidden, teacher_weight)
-    mask = _vec(mask, "mask", torch.uint8)
-    targets = _vec(targets, "targets", torch.int64)
-    diff_mask = _vec(diff_mask, "diff_mask", torch.uint8)
+    T, V, hs, ht, head_args, heads = _heads(student_hidden, student_weight, teacher_hidden, teacher_weight)
+    mask = _vec(mask, "mask", torch.uint8, T)
+    targets = _vec(targets, "targets", torch.int64, T)
+    diff_mask = _vec(diff_mask, "diff_mask", torch.uint8, T)
     dev = student_hidden.device
+    _on(dev, **heads, mask=mask, targets=targets, diff_mask=diff_mask)
     f32 = dict(dtype=torch.float32, device=dev)
     kl = torch.empty(T, **f32)
     lps = lpt = diff = None
@@ -363,9 +407,9 @@ def lp_lm_head_kl(student_hidden, student_weight, teacher_hidden, teacher_weight
         lps, lpt, diff = torch.empty(T, **f32), torch.empty(T, **f32), torch.empty(T, **f32)
     lseu = torch.empty(T, **f32) if want_lse else None
     lsev = torch.empty(T, **f32) if want_lse else None
-    ws = _workspace(lp_lm_head_kl_workspace_bytes(T, hs, V, tile_rows, False), dev, workspace)
+    ws, ws_bytes = _workspace(lp_lm_head_kl_workspace_bytes(T, hs, V, tile_rows, False), dev, workspace)
     st = lib.lp_lm_head_kl(*head_args, T, V, _ptr(mask), _ptr(targets), _ptr(diff_mask), int(tile_rows), _ptr(kl),
-                           _ptr(lps), _ptr(lpt), _ptr(diff), _ptr(lseu), _ptr(lsev), _ptr(ws), ws.numel(),
+                           _ptr(lps), _ptr(lpt), _ptr(diff), _ptr(lseu), _ptr(lsev), _ptr(ws), ws_bytes,
                            _stream(stream))
     check("lp_lm_head_kl", st)
     return kl, lps, lpt, diff, lseu, lsev
@@ -377,17 +421,18 @@ def lp_lm_head_kl_backward(student_hidden, student_weight, teacher_hidden, teach
     """(grad_hidden fp32 [T, h_student] or None, grad_weight fp32 [V, h_student] or None) of sum_t g_t KL_t."""
     torch = _torch()
     lib = load()
-    T, V, hs, ht, head_args = _heads(student_hidden, student_weight, teacher_hidden, teacher_weight)
-    mask = _vec(mask, "mask", torch.uint8)
-    lse_student = _vec(lse_student, "lse_student", torch.float32)
-    lse_teacher = _vec(lse_teacher, "lse_teacher", torch.float32)
-    grad_kl = _vec(grad_kl, "grad_kl", torch.float32)
+    T, V, hs, ht, head_args, heads = _heads(student_hidden, student_weight, teacher_hidden, teacher_weight)
+    mask = _vec(mask, "mask", torch.uint8, T)
+    lse_student = _vec(lse_student, "lse_student", torch.float32, T)
+    lse_teacher = _vec(lse_teacher, "lse_teacher", torch.float32, T)
+    grad_kl = _vec(grad_kl, "grad_kl", torch.float32, T)
     dev = student_hidden.device
+    _on(dev, **heads, mask=mask, lse_student=lse_student, lse_teacher=lse_teacher, grad_kl=grad_kl)
     dH = torch.empty((T, hs), dtype=torch.float32, device=dev) if need_grad_hidden else None
     dW = torch.empty((V, hs), dtype=torch.float32, device=dev) if need_grad_weight else None
-    ws = _workspace(lp_lm_head_kl_workspace_bytes(T, hs, V, tile_rows, True), dev, workspace)
+    ws, ws_bytes = _workspace(lp_lm_head_kl_workspace_bytes(T, hs, V, tile_rows, True), dev, workspace)
     st = lib.lp_lm_head_kl_backward(*head_args, T, V, _ptr(mask), int(tile_rows), _ptr(lse_student),
-                                    _ptr(lse_teacher), _ptr(grad_kl), _ptr(dH), _ptr(dW), _ptr(ws), ws.numel(),
+                                    _ptr(lse_teacher), _ptr(grad_kl), _ptr(dH), _ptr(dW), _ptr(ws), ws_bytes,
                                     _stream(stream))
     check("lp_lm_head_kl_backward", st)
     return dH, dW

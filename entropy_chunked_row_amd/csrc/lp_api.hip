@@ -125,6 +125,12 @@ lp_status lp_logprobs_entropy_k(const void* logits, lp_dtype dtype, int64_t T, i
                                stream);
 }
 
+int lp_lm_head_fast_tiles(int64_t T, int64_t h, int64_t V, int64_t ld_h, int64_t ld_w, int64_t tile_rows,
+                          int backward) {
+  if (T < 0 || h <= 0 || V <= 0 || V > kMaxV || h > kMaxV || ld_h < h || ld_w < h || tile_rows <= 0) return -1;
+  return lp::lmhead_fast_tiles(T, h, V, ld_h, ld_w, tile_rows, backward ? 1 : 0) ? 1 : 0;
+}
+
 size_t lp_lm_head_workspace_bytes(int64_t T, int64_t h, int64_t V, int64_t tile_rows, int backward) {
   lp::LMHeadWorkspace w;
   if (!lp::lmhead_workspace_layout(T, h, V, tile_rows, backward, &w)) return 0;

@@ -109,6 +109,12 @@ bool lmhead_workspace_layout(int64_t T, int64_t h, int64_t V, int64_t tile_rows,
 // smaller tile_rows fixes it); same modes as lmhead_workspace_layout.
 bool lmhead_launches_fit(int64_t T, int64_t h, int64_t V, int64_t tile_rows, int backward);
 
+// True when a call of this shape runs on the direct-to-LDS tiles (every
+// per-lane byte offset of their loads fits in 32 bits and h % 64 == 0);
+// backward: also the dense gradient GEMMs on the dZ buffers.  Otherwise the
+// generic tiles (64-bit addressing) run.
+bool lmhead_fast_tiles(int64_t T, int64_t h, int64_t V, int64_t ld_h, int64_t ld_w, int64_t tile_rows, int backward);
+
 // Zero-fill with a kernel (not a memset node, so callers may capture it).
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s);
 

@@ -124,13 +124,48 @@ __device__ __forceinline__ void tile_coords(int L, int n_vb, int n_nb, int& vb, 
   }
 }
 
-// The direct-to-LDS kernels need K = h in steps of 64 and 32-bit byte offsets
-// from the hidden base to every gathered row.
-bool lmhead_fast_path(const LMHeadShape& sh) {
-  return (sh.h % FwdDtlCfg::BK) == 0 && static_cast<uint64_t>(sh.T) * static_cast<uint64_t>(sh.ld_h) * 2u < (1ull << 32);
+// The direct-to-LDS loads address each operand through a buffer descriptor
+// with a 32-bit per-lane byte offset (row r of pitch ld, plus the 16-byte
+// chunk) and the stage's K offset added on top: `rows` rows of pitch `ld`
+// plus a K span of `k` elements (bf16) must stay below 2^32 bytes.
+bool u32_span(int64_t rows, int64_t ld, int64_t k) {
+  return (static_cast<uint64_t>(rows) * static_cast<uint64_t>(ld) + static_cast<uint64_t>(k)) * 2u < (1ull << 32);
+}
+
+// Largest vocab (A) block of the direct-to-LDS GEMMs that read the weight.
+constexpr int kDtlWeightRows = FwdDtlCfg::BM > BwdDtlCfg::BM ? (FwdDtlCfg::BM > KLCfg::BM ? FwdDtlCfg::BM : KLCfg::BM)
+                                                              : (BwdDtlCfg::BM > KLCfg::BM ? BwdDtlCfg::BM : KLCfg::BM);
+
+// Direct-to-LDS tiles for the logit GEMM of one head: K = h in steps of 64,
+// the gathered hidden rows (any of the T rows) and one weight block of
+// kDtlWeightRows rows within 32-bit offsets.
+bool head_fast(int64_t T, int64_t h, int64_t ld_h, int64_t ld_w) {
+  return h % FwdDtlCfg::BK == 0 && h % KLCfg::BK == 0 && u32_span(T, ld_h, h) && u32_span(kDtlWeightRows, ld_w, h);
+}
+
+// ... and for the backward's dense gradient GEMMs on the dZ buffers: dHidden
+// reads blocks of dZ [rows][vpad] and W^T [h][vpad] rows over K = vpad, dW
+// blocks of dZ^T [vocab][tpad] and H_tile^T [h][tpad] rows over K = tpad.
+bool dense_fast(int64_t vpad, int64_t tpad) {
+  constexpr int R = DenseDtlCfg::BM > DenseDtlCfg::BN ? DenseDtlCfg::BM : DenseDtlCfg::BN;
+  return u32_span(R, vpad, vpad) && u32_span(R, tpad, tpad);
+}
+
+bool lmhead_fast_path(const LMHeadShape& sh) { return head_fast(sh.T, sh.h, sh.ld_h, sh.ld_w); }
+
+int64_t bwd_tpad(int64_t T, int64_t tile_rows) {
+  const int64_t tr = tile_rows < T ? tile_rows : T;
+  return static_cast<int64_t>(align_up(static_cast<size_t>(tr > 0 ? tr : 1), 64));
 }
 
 }  // namespace
+
+bool lmhead_fast_tiles(int64_t T, int64_t h, int64_t V, int64_t ld_h, int64_t ld_w, int64_t tile_rows,
+                       int backward) {
+  if (!head_fast(T, h, ld_h, ld_w)) return false;
+  if (!backward) return true;
+  return dense_fast(static_cast<int64_t>(align_up(static_cast<size_t>(V), 64)), bwd_tpad(T, tile_rows));
+}
 
 // One dispatch covers at most 2^32 - 1 work-items per grid dimension.  True
 // when every launch of the call (fast or generic tiles) stays within that.
@@ -1266,7 +1301,8 @@ hipError_t backward_tiles(const LMHeadShape& sh, bool fast, int bm_fast, int bn_
 hipError_t launch_lmhead_backward(const LMHeadShape& sh, const float* lse, const float* entropy,
                                   const float* grad_logprob, const float* grad_entropy, float* grad_hidden,
                                   float* grad_weight, char* ws, const LMHeadWorkspace& w, hipStream_t s) {
-  const bool fast = lmhead_fast_path(sh) && (reinterpret_cast<uintptr_t>(grad_hidden) & 15u) == 0;
+  const bool fast = lmhead_fast_tiles(sh.T, sh.h, sh.V, sh.ld_h, sh.ld_w, sh.tile_rows, 1) &&
+                    (reinterpret_cast<uintptr_t>(grad_hidden) & 15u) == 0;
   auto launch_dz = [&](int64_t base, int64_t tr, int64_t tpad, int64_t vpad, int n_vb, int n_nb, const int* idx,
                        const int* count, uint16_t* dz, uint16_t* dzt) -> hipError_t {
     DzArgs d;
@@ -1651,8 +1687,11 @@ __global__ void __launch_bounds__(256) k_kl_merge(KLMergeArgs a) {
   }
 }
 
-static bool kl_fast_path(const LMHeadShape& st, const LMHeadShape& te) {
-  return lmhead_fast_path(st) && lmhead_fast_path(te) && st.h % KLCfg::BK == 0 && te.h % KLCfg::BK == 0;
+// Both heads on the direct-to-LDS tiles; the backward's dense GEMMs run on
+// the student's dZ buffers.
+static bool kl_fast_path(const LMHeadShape& st, const LMHeadShape& te, int backward) {
+  return lmhead_fast_tiles(st.T, st.h, st.V, st.ld_h, st.ld_w, st.tile_rows, backward) &&
+         lmhead_fast_path(te);
 }
 
 static KLHeadArgs kl_args(const LMHeadShape& st, const LMHeadShape& te) {
@@ -1687,7 +1726,7 @@ hipError_t launch_lmhead_kl_forward(const LMHeadShape& sh, const LMHeadShape& te
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const bool fast = kl_fast_path(sh, te);
+  const bool fast = kl_fast_path(sh, te, 0);
   // chunks of at most kKLChunk rows (the fast path's teacher buffer holds one)
   const int64_t tr0 = sh.tile_rows < sh.T ? sh.tile_rows : sh.T;
   const int64_t tr = tr0 > kKLChunk ? kKLChunk : tr0;
@@ -1860,7 +1899,7 @@ __global__ void __launch_bounds__(C::NT) k_kl_dz_student_dtl(KLDzArgs a) {
 hipError_t launch_lmhead_kl_backward(const LMHeadShape& sh, const LMHeadShape& te, const float* lse_student,
                                      const float* lse_teacher, const float* grad_kl, float* grad_hidden,
                                      float* grad_weight, char* ws, const LMHeadWorkspace& w, hipStream_t s) {
-  const bool fast = kl_fast_path(sh, te) && (reinterpret_cast<uintptr_t>(grad_hidden) & 15u) == 0;
+  const bool fast = kl_fast_path(sh, te, 1) && (reinterpret_cast<uintptr_t>(grad_hidden) & 15u) == 0;
   float* tbuf = reinterpret_cast<float*>(ws + w.tbuf_off);
   auto launch_dz = [&](int64_t base, int64_t tr, int64_t tpad, int64_t vpad, int n_vb, int n_nb, const int* idx,
                        const int* count, uint16_t* dz, uint16_t* dzt) -> hipError_t {

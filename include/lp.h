@@ -97,6 +97,26 @@ lp_status lp_logprobs_entropy(const void* logits, lp_dtype dtype, int64_t T, int
 size_t lp_lm_head_workspace_bytes(int64_t T, int64_t h, int64_t V, int64_t tile_rows, int backward);
 
 /*
+ * Which GEMM tiles a fused LM-head call of this shape runs on (host only; no
+ * device access): 1 = the direct-to-LDS MFMA tiles, 0 = the generic tiles,
+ * -1 = invalid sizes (T < 0, h or V outside 1..2^30, ld_h or ld_w < h,
+ * tile_rows <= 0).  The fast tiles need h % 64 == 0 and address every operand
+ * with 32-bit per-lane byte offsets, so they also need
+ *   (T x ld_h + h) x 2 < 2^32        (any hidden row may be gathered),
+ *   (256 x ld_w + h) x 2 < 2^32      (one 256-row weight block),
+ * and for the backward (backward != 0), with vpad = V rounded up to 64 and
+ * tpad = min(tile_rows, T) rounded up to 64,
+ *   (256 x vpad + vpad) x 2 < 2^32,  (256 x tpad + tpad) x 2 < 2^32
+ * (blocks of the dZ, dZ^T, W^T and hidden-tile^T buffers of the gradient
+ * GEMMs).  Shapes outside these run on the generic tiles, which use 64-bit
+ * addressing; results are the same up to summation order.  The backward also
+ * takes the generic tiles when grad_hidden is not 16-byte aligned.  The KL
+ * through the heads uses the fast tiles when both heads qualify.
+ */
+int lp_lm_head_fast_tiles(int64_t T, int64_t h, int64_t V, int64_t ld_h, int64_t ld_w, int64_t tile_rows,
+                          int backward);
+
+/*
  * Fused LM head forward: log-prob and entropy of softmax(hidden @ weight^T /
  * temperature) without writing the logits.
  *

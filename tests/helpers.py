@@ -42,3 +42,18 @@ def grad_errors(got, want):
     fro = np.linalg.norm(got - want) / nrm if nrm > 0 else np.linalg.norm(got)
     mad = np.max(np.abs(got - want)) / mx if mx > 0 else np.max(np.abs(got)) if got.size else 0.0
     return float(fro), float(mad)
+
+
+def oracle_by_row_blocks(fn, rows, block=128, workers=None):
+    """fn(rows_subset) -> tuple of per-row arrays, evaluated over blocks of
+    `rows` in a thread pool (numpy releases the GIL inside its kernels) and
+    concatenated in row order.  For full-size parity on every scored row."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+    rows = np.asarray(rows)
+    if workers is None:
+        workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    parts = [rows[i:i + block] for i in range(0, len(rows), block)]
+    with ThreadPoolExecutor(workers) as ex:
+        outs = list(ex.map(fn, parts))
+    return tuple(np.concatenate([o[k] for o in outs]) for k in range(len(outs[0])))

@@ -243,3 +243,34 @@ def test_misaligned_fp32_arguments_are_rejected(lib):
     assert lib.lp_kl_full_vocab(FAKE, FAKE, 0, 8, 100, 100, 100, mis, None, None, None, None, None, None) == 1
     assert lib.lp_prob_diff(FAKE, mis, None, 8, FAKE, None) == 1
     assert lib.lp_prob_diff_stats(mis, FAKE, None, 8, FAKE, FAKE, ws, None) == 1
+
+
+def test_fast_tiles_need_32bit_offsets_for_every_operand(lib):
+    """The direct-to-LDS tiles form 32-bit per-lane byte offsets for every
+    operand; shapes where one would wrap run on the generic tiles (64-bit
+    addressing) instead of giving wrong logits or gradients.  Host-only query,
+    nothing is launched."""
+    f = lib.lp_lm_head_fast_tiles
+    # the shipping shapes take the fast tiles, forward and backward
+    assert f(32768, 5120, 151936, 5120, 5120, 4096, 0) == 1
+    assert f(114688, 5120, 151936, 5120, 5120, 4096, 1) == 1
+    assert f(16384, 7168, 129280, 7168, 7168, 4096, 1) == 1
+    # h % 64 != 0: generic
+    assert f(1024, 520, 4096, 520, 520, 256, 0) == 0
+    # any hidden row may be gathered: T x ld_h x 2 bytes past 4 GiB
+    assert f(420000, 5120, 151936, 5120, 5120, 4096, 0) == 0
+    assert f(419000, 5120, 151936, 5120, 5120, 4096, 0) == 1
+    # one 256-row weight block past 4 GiB: a huge ld_w
+    assert f(1024, 64, 300, 64, 9 * 2 ** 20, 256, 0) == 0
+    assert f(1024, 64, 300, 64, 2 ** 23 - 64, 256, 0) == 1
+    # backward: a 256-row block of the dZ buffers over V ~ 9M columns
+    assert f(1024, 64, 9_000_000, 64, 64, 256, 0) == 1   # the forward never forms those offsets
+    assert f(1024, 64, 9_000_000, 64, 64, 256, 1) == 0
+    assert f(1024, 64, 8_000_000, 64, 64, 256, 1) == 1
+    # backward: tiles of more than ~8.35M rows (dZ^T rows of pitch tpad)
+    assert f(9_000_000, 64, 1000, 64, 64, 9_000_000, 1) == 0
+    assert f(9_000_000, 64, 1000, 64, 64, 4096, 1) == 1
+    # invalid sizes
+    assert f(-1, 64, 100, 64, 64, 4, 0) == -1
+    assert f(8, 64, 100, 32, 64, 4, 0) == -1
+    assert f(8, 64, 100, 64, 64, 0, 0) == -1

@@ -99,6 +99,29 @@ def test_kl_head_several_chunks_per_tile():
         assert fro <= TOL_GRAD and mad <= TOL_GRAD, (nm, fro, mad)
 
 
+@pytest.mark.timeout(600)
+def test_kl_backward_shipping_tile_elementwise():
+    """Student gradients of the KL through the heads at the shipping tile
+    size on the direct-to-LDS tiles: about 12,800 scored rows in tiles (and
+    teacher-buffer chunks) of 4096 -- three full and a ragged fourth --,
+    h = 256 for both heads, V = 5003.  Every element of dHidden and dW
+    against the oracle."""
+    T, h, V, tile = 16000, 256, 5003, 4096
+    assert _lp().load().lp_lm_head_fast_tiles(T, h, V, h, h, tile, 1) == 1
+    A = _case(T, h, h, V, seed=4097)
+    n = int(A["mask"].sum())
+    assert 3 * tile < n < 4 * tile, n
+    heads = _dev_heads(A)
+    m = to_dev(A["mask"])
+    out = _lp().lp_lm_head_kl(*heads, m, None, None, tile)
+    dH, dW = _lp().lp_lm_head_kl_backward(*heads, m, tile, out[4], out[5], to_dev(A["grad_kl"]))
+    dH_o, dW_o = O.lm_head_kl_backward(*_wide(A), A["mask"], A["grad_kl"])
+    for nm, g, w in (("dH", host(dH), dH_o), ("dW", host(dW), dW_o)):
+        fro, mad = grad_errors(g, w)
+        assert fro <= TOL_GRAD and mad <= TOL_GRAD, (nm, fro, mad)
+    assert not host(dH)[A["mask"] == 0].any()
+
+
 def test_kl_head_same_model_is_exactly_zero():
     A = _case(96, 128, 128, 777, seed=5, scored=1.0)
     hs, ws = to_dev_bits(A["student_hidden"], "bf16"), to_dev_bits(A["student_weight"], "bf16")

@@ -272,6 +272,15 @@ def test_backward_full_size_sampled():
     scale = dW.double().abs().sum(0)
     assert torch.isfinite(dW).all().item()
     assert (colsum.abs() <= 1e-2 * scale).all().item()
+    # dW accumulated over 23 tiles of 4096 against 12 tiles of 8192: a tile dropped, doubled or paired with
+    # the wrong hidden rows would change it by far more than the accumulation order does
+    _, dW8 = _lp().lp_lm_head_logprobs_entropy_backward(hd, Wd, y, md, cfg.temperature, 8192, lse, H,
+                                                        to_dev(A["grad_logprob"]), to_dev(A["grad_entropy"]),
+                                                        need_grad_hidden=False)
+    diff = (dW - dW8).double()
+    rel_fro = (diff.norm() / dW8.double().norm()).item()
+    rel_max = (diff.abs().max() / dW8.double().abs().max()).item()
+    assert rel_fro <= TOL_GRAD and rel_max <= TOL_GRAD, (rel_fro, rel_max)
 
 
 @pytest.mark.parametrize("h,tau", [(256, 0.7), (72, 1.0)])
@@ -327,6 +336,66 @@ def test_hidden_past_4_gib_takes_generic_tiles():
         assert fro <= TOL_GRAD and mad <= TOL_GRAD, (nm, fro, mad)
     nonzero_rows = (dH != 0).any(dim=1).cpu().numpy()
     assert not nonzero_rows[mask == 0].any()
+
+
+@pytest.mark.timeout(600)
+def test_weight_blocks_past_4_gib_take_generic_tiles():
+    """Maximum-size case: a weight with a row pitch of 9 Mi elements, so one
+    256-row weight block spans more than 4 GiB and the fast tiles' 32-bit
+    per-lane offsets would wrap.  The host routes the call to the generic
+    tiles (64-bit addressing); forward and backward match the oracle."""
+    torch = _torch()
+    lib = _lp().load()
+    T, h, V, tile, tau = 512, 64, 300, 128, 0.7
+    ld_w = 9 * 2 ** 20
+    assert lib.lp_lm_head_fast_tiles(T, h, V, h, ld_w, tile, 0) == 0
+    assert lib.lp_lm_head_fast_tiles(T, h, V, h, ld_w, tile, 1) == 0
+    assert lib.lp_lm_head_fast_tiles(T, h, V, h, h, tile, 1) == 1  # the same rows, dense weight: fast tiles
+    hid, W, y, m = _case(T, h, V, seed=123)
+    g = np.random.default_rng(124).normal(0, 1, size=T).astype(np.float32)
+    gH = np.random.default_rng(125).normal(0, 0.1, size=T).astype(np.float32)
+    storage = torch.empty((V - 1) * ld_w + h, dtype=torch.bfloat16, device="cuda")  # 5.6 GB
+    Wd = storage.as_strided((V, h), (ld_w, 1))
+    Wd.copy_(to_dev_bits(W, "bf16"))
+    hd = to_dev_bits(hid, "bf16")
+    lp, H, lse = _lp().lp_lm_head_logprobs_entropy(hd, Wd, to_dev(y), to_dev(m), tau, tile)
+    lp_o, H_o, lse_o = O.lm_head_logprobs_entropy(O.widen_bf16(hid), O.widen_bf16(W), y, m, tau)
+    assert max_abs_err(host(lp), lp_o) <= TOL_FWD and max_abs_err(host(H), H_o) <= TOL_FWD
+    assert max_abs_err(host(lse), lse_o) <= TOL_FWD
+    dH, dW = _lp().lp_lm_head_logprobs_entropy_backward(hd, Wd, to_dev(y), to_dev(m), tau, tile, lse, H, to_dev(g),
+                                                        to_dev(gH))
+    dH_o, dW_o = O.lm_head_backward(O.widen_bf16(hid), O.widen_bf16(W), y, m, tau, g, gH)
+    for nm, got, want in (("dH", host(dH), dH_o), ("dW", host(dW), dW_o)):
+        fro, mad = grad_errors(got, want)
+        assert fro <= TOL_GRAD and mad <= TOL_GRAD, (nm, fro, mad)
+    del storage, Wd
+
+
+@pytest.mark.timeout(600)
+def test_backward_shipping_tile_elementwise():
+    """Gradients at the shipping tile size on the direct-to-LDS tiles: about
+    12,600 scored rows in tiles of 4096 (three full tiles and a ragged
+    fourth), h = 256, V = 5003 (a ragged last vocab block), tau 0.7 and an
+    entropy gradient.  Every element of dHidden and dW against the oracle
+    (miles PR #4645 "Testing": equality of the hidden and weight gradients
+    against hidden @ W.T, uneven tiles); a dropped, doubled or mis-paired tile
+    of dZ^T . H fails the dW comparison."""
+    T, h, V, tile, tau = 18000, 256, 5003, 4096, 0.7
+    lib = _lp().load()
+    assert lib.lp_lm_head_fast_tiles(T, h, V, h, h, tile, 1) == 1
+    dH, dW, dH_o, dW_o, m = _backward_case(T, h, V, tile, tau, seed=4096)
+    n = int(m.sum())
+    assert 3 * tile < n < 4 * tile, n
+    for nm, got, want in (("dH", dH, dH_o), ("dW", dW, dW_o)):
+        fro, mad = grad_errors(got, want)
+        assert fro <= TOL_GRAD and mad <= TOL_GRAD, (nm, fro, mad)
+    # the rows on either side of each tile boundary, one by one
+    rows = np.nonzero(m)[0]
+    for b in (tile, 2 * tile, 3 * tile):
+        for r in rows[b - 1:b + 1]:
+            fro, mad = grad_errors(dH[r], dH_o[r])
+            assert fro <= TOL_GRAD and mad <= TOL_GRAD, (b, r, fro, mad)
+    assert not dH[m == 0].any()
 
 
 @pytest.mark.parametrize("h", [64, 72])  # direct-to-LDS and generic tiles
