@@ -26,6 +26,8 @@ SIGNATURES = {
     "lp_lm_head_fast_tiles": (c_int, [c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, c_int]),
     "lp_lm_head_logprobs_entropy": (c_int, [c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_f, c_i64,
                                             c_vp, c_vp, c_vp, c_vp, ctypes.c_size_t, c_vp]),
+    "lp_lm_head_logprobs_entropy_noalloc": (c_int, [c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp,
+                                                    c_f, c_i64, c_vp, c_vp, c_vp, c_vp]),
     "lp_lm_head_logprobs_entropy_backward": (c_int, [c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_f,
                                                      c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                                      ctypes.c_size_t, c_vp]),

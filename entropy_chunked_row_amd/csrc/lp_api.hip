@@ -2,6 +2,7 @@
 // tile scheduling and stream-ordered launches.  Every check runs on the host
 // before anything is launched; a rejected call touches no output.
 #include <initializer_list>
+#include <mutex>
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -52,6 +53,38 @@ bool f32_aligned(std::initializer_list<const float*> ps) {
 }
 
 size_t dtype_bytes(int d) { return d == LP_FP32 ? 4 : 2; }
+
+}  // namespace
+
+// Scratch of lp_lm_head_logprobs_entropy_noalloc: one copy per GPU the
+// library runs on, held until the process ends.  Host code never passes this
+// name to a kernel (on the host it is only a stand-in for the symbol): the
+// device address of each GPU's copy comes from hipGetSymbolAddress below.
+static __device__ __align__(256) unsigned char scratch[LP_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch, looked up once per device
+// (with that device current) and kept.
+hipError_t scratch_of_current_device(int* device, void** out) {
+  hipError_t e = hipGetDevice(device);
+  if (e != hipSuccess) return e;
+  if (*device < 0 || *device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[*device]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[*device] = p;
+  }
+  *out = g_scratch_ptr[*device];
+  return hipSuccess;
+}
 
 }  // namespace
 
@@ -137,10 +170,12 @@ size_t lp_lm_head_workspace_bytes(int64_t T, int64_t h, int64_t V, int64_t tile_
   return w.total;
 }
 
+// static_scratch: the call brings no workspace (the no-alloc form checks its
+// own scratch), so `workspace` is not examined.
 static lp_status check_lmhead(const char* fn, const void* hidden, int64_t ld_h, const void* weight, int64_t ld_w,
                               int64_t T, int64_t h, int64_t V, const int64_t* targets, float temperature,
                               int64_t tile_rows, void* workspace, size_t workspace_bytes, int backward,
-                              lp::LMHeadWorkspace* w) {
+                              lp::LMHeadWorkspace* w, bool static_scratch = false) {
   if (T < 0) return fail(LP_ERR_INVALID_ARGUMENT, "%s: T < 0", fn);
   if (h <= 0 || V <= 0 || V > kMaxV || h > kMaxV)
     return fail(LP_ERR_INVALID_ARGUMENT, "%s: h and V must be in 1..2^30", fn);
@@ -158,6 +193,7 @@ static lp_status check_lmhead(const char* fn, const void* hidden, int64_t ld_h, 
     return fail(LP_ERR_INVALID_ARGUMENT, "%s: sizes overflow the workspace layout", fn);
   if (!lp::lmhead_launches_fit(T, h, V, tile_rows, backward))
     return fail(LP_ERR_UNSUPPORTED, "%s: a launch would exceed 2^32-1 work-items; use a smaller tile_rows", fn);
+  if (static_scratch) return LP_OK;
   if (!workspace || workspace_bytes < w->total)
     return fail(LP_ERR_WORKSPACE_TOO_SMALL, "%s: workspace needs %zu bytes, got %zu", fn, w->total,
                 workspace ? workspace_bytes : size_t(0));
@@ -221,6 +257,42 @@ lp_status lp_lm_head_logprobs_entropy_k(const void* hidden, int64_t ld_h, const 
                                         void* stream) {
   return lm_head_forward_impl("lp_lm_head_logprobs_entropy_k", hidden, ld_h, weight, ld_w, T, h, V, targets, K, mask,
                               temperature, tile_rows, logprob, entropy, lse, workspace, workspace_bytes, stream);
+}
+
+lp_status lp_lm_head_logprobs_entropy_noalloc(const void* hidden, int64_t ld_h, const void* weight, int64_t ld_w,
+                                              int64_t T, int64_t h, int64_t V, const int64_t* targets,
+                                              const uint8_t* mask, float temperature, int64_t tile_rows,
+                                              float* logprob, float* entropy, float* lse, void* stream) {
+  const char* fn = "lp_lm_head_logprobs_entropy_noalloc";
+  lp::LMHeadWorkspace w;
+  lp_status st = check_lmhead(fn, hidden, ld_h, weight, ld_w, T, h, V, targets, temperature, tile_rows, nullptr, 0,
+                              0, &w, true);
+  if (st != LP_OK) return st;
+  if (T == 0) return ok();
+  if (w.total > LP_NOALLOC_SCRATCH_BYTES)
+    return fail(LP_ERR_WORKSPACE_TOO_SMALL,
+                "%s: this shape needs %zu bytes of scratch, the static scratch holds %zu; use a smaller tile_rows "
+                "or the workspace form",
+                fn, w.total, static_cast<size_t>(LP_NOALLOC_SCRATCH_BYTES));
+  if (!logprob) return fail(LP_ERR_INVALID_ARGUMENT, "%s: logprob is required", fn);
+  if (!f32_aligned({logprob, entropy, lse})) return fail(LP_ERR_INVALID_ARGUMENT, "%s: misaligned fp32 output", fn);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int device = 0;
+  void* ws = nullptr;
+  hipError_t e = scratch_of_current_device(&device, &ws);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  if (s) {
+    hipDevice_t sd = 0;
+    e = hipStreamGetDevice(s, &sd);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    if (sd != device)
+      return fail(LP_ERR_INVALID_ARGUMENT, "%s: the stream belongs to device %d, the current device is %d", fn,
+                  static_cast<int>(sd), device);
+  }
+  lp::LMHeadShape sh = make_shape(hidden, ld_h, weight, ld_w, T, h, V, targets, 1, mask, temperature, tile_rows);
+  e = lp::launch_lmhead_forward(sh, logprob, entropy, lse, static_cast<char*>(ws), w, s);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return ok();
 }
 
 static lp_status lm_head_backward_impl(const char* fn, const void* hidden, int64_t ld_h, const void* weight,

@@ -145,6 +145,30 @@ lp_status lp_lm_head_logprobs_entropy(const void* hidden, int64_t ld_h, const vo
                                       size_t workspace_bytes, void* stream);
 
 /*
+ * The fused LM-head forward above for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): same arguments and results (bit for bit) without the
+ * workspace.  Its scratch is a static device array of
+ * LP_NOALLOC_SCRATCH_BYTES bytes that every GPU the library runs on holds
+ * until the process ends; the call itself allocates and frees nothing.
+ * The scratch used is the calling thread's current device's; a non-NULL
+ * stream must belong to that device (LP_ERR_INVALID_ARGUMENT otherwise).
+ * Shapes whose lp_lm_head_workspace_bytes(T, h, V, tile_rows, 0) exceeds the
+ * scratch are refused with LP_ERR_WORKSPACE_TOO_SMALL (a smaller tile_rows
+ * shrinks it: at V = 151936, tile_rows <= 1024 fits for T up to about 500k).
+ * All calls on one GPU share its scratch: calls that overlap in time on one
+ * GPU (different streams or threads) race and give undefined results; calls
+ * ordered on one stream are safe.  The first call on a device looks up that
+ * device's copy of the array (hipGetSymbolAddress).
+ */
+#define LP_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+lp_status lp_lm_head_logprobs_entropy_noalloc(const void* hidden, int64_t ld_h, const void* weight, int64_t ld_w,
+                                              int64_t T, int64_t h, int64_t V, const int64_t* targets,
+                                              const uint8_t* mask, float temperature, int64_t tile_rows,
+                                              float* logprob, float* entropy, float* lse, void* stream);
+
+/*
  * Backward of the fused LM head for the loss
  *   L = sum over scored rows t of grad_logprob[t] * logprob[t] + grad_entropy[t] * entropy[t].
  * Recompute-based, as miles PR #4645 "How it works" describes: each tile's

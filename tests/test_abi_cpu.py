@@ -274,3 +274,20 @@ def test_fast_tiles_need_32bit_offsets_for_every_operand(lib):
     assert f(-1, 64, 100, 64, 64, 4, 0) == -1
     assert f(8, 64, 100, 32, 64, 4, 0) == -1
     assert f(8, 64, 100, 64, 64, 0, 0) == -1
+
+
+def test_noalloc_forward_checks_before_touching_the_device(lib):
+    """The no-alloc forward refuses shapes beyond its static scratch (and bad
+    arguments) on the host, before it looks up any device; T = 0 is OK."""
+    st = lib.lp_lm_head_logprobs_entropy_noalloc(FAKE, 5120, FAKE, 5120, 32768, 5120, 151936, FAKE, None, 0.7, 4096,
+                                                 FAKE, None, None, None)
+    assert st == 3 and b"static scratch" in lib.lp_last_error()
+    # the same rows in 512-row tiles fit the 64 MiB scratch: the workspace form's size query agrees
+    assert lib.lp_lm_head_workspace_bytes(32768, 5120, 151936, 512, 0) <= 64 << 20
+    assert lib.lp_lm_head_workspace_bytes(32768, 5120, 151936, 4096, 0) > 64 << 20
+    assert lib.lp_lm_head_logprobs_entropy_noalloc(FAKE, 64, FAKE, 64, 8, 64, 100, FAKE, None, 0.7, 0, FAKE, None,
+                                                   None, None) == 1
+    assert lib.lp_lm_head_logprobs_entropy_noalloc(FAKE, 64, FAKE, 64, 8, 64, 100, FAKE, None, 0.7, 4, FAKE + 2,
+                                                   None, None, None) == 1
+    assert lib.lp_lm_head_logprobs_entropy_noalloc(None, 64, None, 64, 0, 64, 100, None, None, 0.7, 4, None, None,
+                                                   None, None) == 0
