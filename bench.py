@@ -7,18 +7,18 @@ Headline (`value`): scored tokens/s of the fused LM-head forward (log-prob +
 entropy of softmax(hidden @ W^T / 0.7)) on T = 32768 packed rows (about 70 %
 scored), h = 5120, V = 151936, bf16, tile 4096 rows.  One step is one call of
 lp_lm_head_logprobs_entropy with inputs already resident in HBM.  The same
-JSON line carries the other paths of the hot path measured the same way
-(logits-input rows, exact KL + prob diff, fused forward + backward, KL through
-both heads), the roofline of the dominant kernel from live per-launch
-HIP-event timing, and the fp64 oracle timed on the host cores over a bounded
-sample.  Each path runs its step untimed for --settle-seconds (steady GPU
+JSON line carries the other paths measured the same way (the tiny fused head
+in absolute microseconds, logits-input rows, exact KL + prob diff, fused
+forward + backward, KL through both heads), each with the roofline of its
+dominant kernels from live per-launch HIP-event timing, the fp64 oracle timed
+on the host cores over a bounded sample of the same workload (and compared
+with the GPU's outputs on those rows), and the device memory one call
+allocates.  Each path runs its step untimed for --settle-seconds (steady GPU
 clocks after the host-side input generation), then W warm-up steps, then
 exactly K timed steps.
 
 Inputs are seeded and synthetic (see synth/).  The fp64 oracle is used only in
-the CPU-baseline leg, which also compares its outputs on the rows it timed with
-the GPU's outputs of the same rows (the headline path's sampled parity; every
-path's parity at full size is in tests/).
+the CPU-baseline legs; every path's parity at full size is in tests/.
 """
 from __future__ import annotations
 
@@ -34,7 +34,8 @@ sys.path.insert(0, ROOT)
 METRIC = "scored tokens/s, fused LM-head logprob+entropy; % of MFMA / HBM peak"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
-ALL_PATHS = ("lm_head_fwd", "logits_input", "kl_prob_diff", "lm_head_fwd_bwd", "kl_lm_head")
+ALL_PATHS = ("lm_head_fwd", "tiny_lm_head", "logits_input", "kl_prob_diff", "lm_head_fwd_bwd", "kl_lm_head")
+MFMA_FLOP = 2 * 32 * 32 * 16   # one v_mfma_f32_32x32x16_bf16
 
 
 def to_dev_bits(bits, dtype):
@@ -89,9 +90,7 @@ def _csrc_sha256():
     return h.hexdigest()
 
 
-def measured_traffic(kernel):
-    """HBM bytes per launch of `kernel` from the committed PMC summary, or None
-    when the kernel sources changed since the counters were taken."""
+def _pmc_doc():
     path = os.path.join(ROOT, "profiles", "hbm_traffic.md")
     try:
         text = open(path).read()
@@ -100,6 +99,16 @@ def measured_traffic(kernel):
     except (OSError, IndexError, ValueError):
         return None
     if doc.get("source_sha256") != _csrc_sha256():
+        return None
+    return doc
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` (a timing name) from the committed PMC
+    summary, or None when the kernel sources changed since the counters were
+    taken."""
+    doc = _pmc_doc()
+    if doc is None:
         return None
     k = doc.get("kernels", {}).get(kernel)
     return None if k is None else k["bytes_per_launch"]
@@ -144,55 +153,22 @@ def _timed(lp, torch, fn, steps, warmup, kernels):
     return ms, per_kernel
 
 
-def bench_lm_head_fwd(lp, torch, np, synth, steps, warmup, cpu_seconds):
-    cfg = synth.LMHead().build()
-    A = cfg.arrays
-    hid, W = to_dev_bits(A["hidden"], "bf16"), to_dev_bits(A["weight"], "bf16")
-    y, m = to_dev(A["targets"]), to_dev(A["mask"])
-    Ts = int(A["mask"].sum())
-    ws = torch.empty(lp.lp_lm_head_workspace_bytes(cfg.T, cfg.h, cfg.V, cfg.tile_rows, False), dtype=torch.uint8,
-                     device="cuda")
-    out = {}
-
-    def step():
-        out["r"] = lp.lp_lm_head_logprobs_entropy(hid, W, y, m, cfg.temperature, cfg.tile_rows, workspace=ws)
-
-    ms, kt = _timed(lp, torch, step, steps, warmup, ["k_fwd_tile", "k_fwd_merge", "k_compact"])
-    flop_step = 2.0 * Ts * cfg.V * cfg.h
-    n_launch, gemm_ms = kt["k_fwd_tile"]
-    n_tiles = (Ts + cfg.tile_rows - 1) // cfg.tile_rows
-    achieved = flop_step * steps / (gemm_ms * 1e-3) / 1e12
-    res = dict(
-        workload=f"fused LM-head forward: T={cfg.T} packed rows ({Ts} scored), h={cfg.h}, V={cfg.V}, bf16, "
-                 f"tau {cfg.temperature}, tile {cfg.tile_rows}",
-        T=cfg.T, scored_rows=Ts, h=cfg.h, V=cfg.V, temperature=cfg.temperature, tile_rows=cfg.tile_rows,
-        ms_per_step=ms / steps, tokens_per_s=Ts * steps / (ms * 1e-3),
-        roofline=dict(bound="mfma", kernel="k_fwd_tile", kernel_ms_per_launch=gemm_ms / n_launch,
-                      achieved=achieved, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                      frac=achieved / BF16_PEAK_TFLOPS, traffic=measured_traffic("k_fwd_tile"),
-                      traffic_unit="HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-                      algorithmic_hbm_bytes_per_launch=(n_tiles * cfg.V * cfg.h * 2 + Ts * cfg.h * 2) / (n_launch / steps),
-                      launches_per_step=n_launch / steps, kernel_ms_per_step=gemm_ms / steps,
-                      algorithmic_flop_per_step=flop_step,
-                      algorithmic_flop_per_launch=flop_step / (n_launch / steps)),
-        kernel_ms_per_step={k: v[1] / steps for k, v in kt.items()},
-    )
-    if cpu_seconds > 0:
-        lpv, Hv, _ = (t.cpu().numpy() for t in out["r"])
-        res["cpu_baseline"] = _cpu_baseline_lm_head(np, A, cfg, np.nonzero(A["mask"])[0], cpu_seconds, lpv, Hv)
-    del hid, W, y, m, ws, out
-    torch.cuda.empty_cache()
-    return res
-
-
-class _LazyWeight:
-    """Widens bf16 weight rows to fp64 only for the vocab block asked for."""
-
-    def __init__(self, O, bits):
-        self.O, self.bits, self.shape = O, bits, bits.shape
-
-    def __getitem__(self, sl):
-        return self.O.widen_bf16(self.bits[sl])
+def _memory_audit(torch, call, workspace_bytes, output_bytes, fp32_logits_bytes):
+    """Device memory one call allocates: the peak of torch's allocated bytes
+    across the call (its outputs and, here, its workspace, both allocated by
+    the binding) against workspace + outputs, and against the [T x V] fp32
+    logits the method never forms."""
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    out = call()
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated() - base
+    del out
+    bound = workspace_bytes + output_bytes
+    return dict(peak_delta_bytes=int(peak), workspace_bytes=int(workspace_bytes), output_bytes=int(output_bytes),
+                within_workspace_plus_outputs=bool(peak <= bound + (1 << 20)),
+                fp32_logits_bytes=int(fp32_logits_bytes), frac_of_fp32_logits=peak / fp32_logits_bytes)
 
 
 def _blas_threads():
@@ -202,30 +178,6 @@ def _blas_threads():
         return max(n) if n else 1
     except Exception:  # pragma: no cover
         return 1
-
-
-def _cpu_baseline_lm_head(np, A, cfg, scored, seconds, lp_gpu, H_gpu):
-    """The fp64 oracle on a bounded sample of scored rows, timed and scaled to
-    tokens/s; its outputs on those rows are then compared with the GPU's
-    (lp_gpu, H_gpu: the GPU's log-probs and entropies of every row)."""
-    from oracle import lp_oracle as O  # the only use of the oracle in this script
-    W = _LazyWeight(O, A["weight"])
-    n = 8
-    t = 0.0
-    while True:
-        rows = scored[:n]
-        t0 = time.perf_counter()
-        lp_o, H_o, _ = O.lm_head_logprobs_entropy(O.widen_bf16(A["hidden"][rows]), W, A["targets"][rows], None,
-                                                  cfg.temperature)
-        t = time.perf_counter() - t0
-        if t >= 0.6 * seconds or n >= len(scored):
-            break
-        n = min(len(scored), int(n * min(8.0, max(2.0, seconds / max(t, 1e-3)))))
-    return dict(value=n / t, unit="scored tokens/s", cores=_blas_threads(), kind="oracle",
-                sample=f"{n} scored rows of the same workload through the fp64 oracle (full V={cfg.V}, h={cfg.h})",
-                seconds=t, cpu_model=_cpu_model(), parity_rows=int(len(rows)),
-                parity_max_abs_err=float(max(np.abs(lp_gpu[rows] - lp_o).max(), np.abs(H_gpu[rows] - H_o).max())),
-                parity_tol=2e-3)
 
 
 def _cpu_model():
@@ -239,7 +191,121 @@ def _cpu_model():
     return None
 
 
-def bench_logits_input(lp, torch, np, synth, steps, warmup):
+def _sample_rows(np, rows, n):
+    """n rows spread over `rows` (seeded, sorted)."""
+    if n >= len(rows):
+        return np.asarray(rows)
+    return np.sort(np.random.default_rng(20261202).choice(rows, n, replace=False))
+
+
+def _oracle_timed(np, run, rows, seconds, n0):
+    """Times run(sample) on growing samples of `rows` until one takes at least
+    0.6 x `seconds` (or covers every row); returns (sample, seconds, result)."""
+    n = min(n0, len(rows))
+    while True:
+        sample = _sample_rows(np, rows, n)
+        t0 = time.perf_counter()
+        res = run(sample)
+        t = time.perf_counter() - t0
+        if t >= 0.6 * seconds or n >= len(rows):
+            return sample, t, res
+        n = min(len(rows), int(n * min(8.0, max(2.0, seconds / max(t, 1e-3)))))
+
+
+def _baseline(n, t, unit, sample, parity_err, parity_tol, **extra):
+    d = dict(value=n / t, unit=unit, cores=_blas_threads(), kind="oracle", sample=sample, seconds=t,
+             cpu_model=_cpu_model(), parity_rows=int(n), parity_max_abs_err=float(parity_err),
+             parity_tol=parity_tol)
+    d.update(extra)
+    return d
+
+
+class _LazyWeight:
+    """Widens bf16 weight rows to fp64 only for the vocab block asked for."""
+
+    def __init__(self, O, bits):
+        self.O, self.bits, self.shape = O, bits, bits.shape
+
+    def __getitem__(self, sl):
+        return self.O.widen_bf16(self.bits[sl])
+
+
+# ---------------------------------------------------------------------------
+# paths
+# ---------------------------------------------------------------------------
+
+def bench_lm_head_fwd(lp, torch, np, synth, steps, warmup, cpu_seconds, cfg=None, tiny=False):
+    cfg = cfg or synth.LMHead().build()
+    A = cfg.arrays
+    hid, W = to_dev_bits(A["hidden"], "bf16"), to_dev_bits(A["weight"], "bf16")
+    y, m = to_dev(A["targets"]), to_dev(A["mask"])
+    Ts = int(A["mask"].sum())
+    ws_bytes = lp.lp_lm_head_workspace_bytes(cfg.T, cfg.h, cfg.V, cfg.tile_rows, False)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    out = {}
+
+    def step():
+        out["r"] = lp.lp_lm_head_logprobs_entropy(hid, W, y, m, cfg.temperature, cfg.tile_rows, workspace=ws)
+
+    ms, kt = _timed(lp, torch, step, steps, warmup, ["k_fwd_tile", "k_fwd_merge", "k_compact"])
+    flop_step = 2.0 * Ts * cfg.V * cfg.h
+    n_launch, gemm_ms = kt["k_fwd_tile"]
+    n_tiles = (Ts + cfg.tile_rows - 1) // cfg.tile_rows
+    achieved = flop_step * steps / (gemm_ms * 1e-3) / 1e12
+    rows_desc = f"T={cfg.T} rows, all scored" if tiny else f"T={cfg.T} packed rows ({Ts} scored)"
+    wl = (f"{'tiny ' if tiny else ''}fused LM-head forward: {rows_desc}, h={cfg.h}, V={cfg.V}, bf16, "
+          f"tau {cfg.temperature}, tile {cfg.tile_rows}")
+    res = dict(workload=wl, T=cfg.T, scored_rows=Ts, h=cfg.h, V=cfg.V, temperature=cfg.temperature,
+               tile_rows=cfg.tile_rows, ms_per_step=ms / steps, tokens_per_s=Ts * steps / (ms * 1e-3),
+               kernel_ms_per_step={k: v[1] / steps for k, v in kt.items()})
+    if tiny:
+        # launch-bound: three launches of a few microseconds, no roofline claim; the call time is taken again
+        # without the per-kernel events, which add their own few microseconds per launch
+        plain_ms = _events_ms(torch, step, steps)
+        res["ms_per_step"] = plain_ms / steps
+        res["tokens_per_s"] = Ts * steps / (plain_ms * 1e-3)
+        res["us_per_call"] = 1e3 * plain_ms / steps
+        res["kernel_us_per_call"] = {k: 1e3 * v[1] / steps for k, v in kt.items()}
+        res["roofline"] = None
+    else:
+        res["roofline"] = dict(
+            bound="mfma", kernel="k_fwd_tile", kernel_ms_per_launch=gemm_ms / n_launch, achieved=achieved,
+            peak=BF16_PEAK_TFLOPS, unit="TFLOP/s", frac=achieved / BF16_PEAK_TFLOPS,
+            traffic=measured_traffic("k_fwd_tile"),
+            traffic_unit="HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+            algorithmic_hbm_bytes_per_launch=(n_tiles * cfg.V * cfg.h * 2 + Ts * cfg.h * 2) / (n_launch / steps),
+            launches_per_step=n_launch / steps, kernel_ms_per_step=gemm_ms / steps,
+            algorithmic_flop_per_step=flop_step, algorithmic_flop_per_launch=flop_step / (n_launch / steps))
+    res["memory"] = _memory_audit(
+        torch, lambda: lp.lp_lm_head_logprobs_entropy(hid, W, y, m, cfg.temperature, cfg.tile_rows),
+        ws_bytes, 3 * 4 * cfg.T, 4 * cfg.T * cfg.V)
+    if cpu_seconds > 0:
+        lpv, Hv, lsev = (t.cpu().numpy() for t in out["r"])
+        from oracle import lp_oracle as O  # CPU-baseline leg only
+        Wl = _LazyWeight(O, A["weight"])
+
+        def run(rows):
+            return O.lm_head_logprobs_entropy(O.widen_bf16(A["hidden"][rows]), Wl, A["targets"][rows], None,
+                                              cfg.temperature)
+
+        rows, t, (lp_o, H_o, lse_o) = _oracle_timed(np, run, np.nonzero(A["mask"])[0], cpu_seconds, 8)
+        err = max(np.abs(lpv[rows] - lp_o).max(), np.abs(Hv[rows] - H_o).max(), np.abs(lsev[rows] - lse_o).max())
+        res["cpu_baseline"] = _baseline(
+            len(rows), t, "scored tokens/s",
+            f"{len(rows)} scored rows of the same workload through the fp64 oracle (full V={cfg.V}, h={cfg.h})",
+            err, 2e-3)
+    del hid, W, y, m, ws, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_tiny_lm_head(lp, torch, np, synth, steps, warmup, cpu_seconds):
+    """T=64, h=256, V=1024, tile 16: launch-bound, reported in microseconds."""
+    return bench_lm_head_fwd(lp, torch, np, synth, max(steps, 100), max(warmup, 10), cpu_seconds,
+                             cfg=synth.tiny_lm_head(), tiny=True)
+
+
+def bench_logits_input(lp, torch, np, synth, steps, warmup, cpu_seconds):
     cfg = synth.LogitsInput().build()
     A = cfg.arrays
     x, y, m = to_dev_bits(A["logits"], "bf16"), to_dev(A["targets"]), to_dev(A["mask"])
@@ -264,12 +330,26 @@ def bench_logits_input(lp, torch, np, synth, steps, warmup):
                       traffic_unit="HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                       algorithmic_bytes_per_launch=bytes_step / (n_launch / steps),
                       launches_per_step=n_launch / steps, algorithmic_bytes_per_step=bytes_step))
+    res["memory"] = _memory_audit(torch, lambda: lp.lp_logprobs_entropy(x, y, m, cfg.temperature, cfg.chunk_rows),
+                                  0, 2 * 4 * cfg.T, 4 * cfg.T * cfg.V)
+    if cpu_seconds > 0:
+        from oracle import lp_oracle as O  # CPU-baseline leg only
+        lpv, Hv = lpo.cpu().numpy(), Ho.cpu().numpy()
+
+        def run(rows):
+            return O.logprobs_entropy(O.widen_bf16(A["logits"][rows]), A["targets"][rows], None, cfg.temperature)
+
+        rows, t, (lp_o, H_o, _) = _oracle_timed(np, run, np.nonzero(A["mask"])[0], cpu_seconds, 64)
+        err = max(np.abs(lpv[rows] - lp_o).max(), np.abs(Hv[rows] - H_o).max())
+        res["cpu_baseline"] = _baseline(len(rows), t, "scored tokens/s",
+                                        f"{len(rows)} scored rows of the same logits through the fp64 oracle", err,
+                                        1e-5)
     del x, y, m, lpo, Ho
     torch.cuda.empty_cache()
     return res
 
 
-def bench_kl(lp, torch, np, synth, steps, warmup):
+def bench_kl(lp, torch, np, synth, steps, warmup, cpu_seconds):
     cfg = synth.KLPair().build()
     A = cfg.arrays
     u, v = to_dev_bits(A["student"], "fp16"), to_dev_bits(A["teacher"], "fp16")
@@ -292,22 +372,37 @@ def bench_kl(lp, torch, np, synth, steps, warmup):
                       traffic_unit="HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                       algorithmic_bytes_per_launch=bytes_step / (n_launch / steps),
                       launches_per_step=n_launch / steps, algorithmic_bytes_per_step=bytes_step))
+    res["memory"] = _memory_audit(torch, lambda: lp.lp_kl_full_vocab(u, v, y, dm), 0, 4 * 4 * cfg.T,
+                                  2 * 4 * cfg.T * cfg.V)
+    if cpu_seconds > 0:
+        from oracle import lp_oracle as O  # CPU-baseline leg only
+        got = [t.cpu().numpy() for t in out["r"]]
+
+        def run(rows):
+            return O.kl_and_prob_diff(O.widen_fp16(A["student"][rows]), O.widen_fp16(A["teacher"][rows]),
+                                      A["targets"][rows], A["diff_mask"][rows])
+
+        rows, t, want = _oracle_timed(np, run, np.arange(cfg.T), cpu_seconds, 32)
+        err = max(np.abs(g[rows] - w).max() for g, w in zip(got, want))
+        res["cpu_baseline"] = _baseline(len(rows), t, "tokens/s",
+                                        f"{len(rows)} rows of both models' logits through the fp64 oracle "
+                                        "(KL, both target log-probs, masked diff)", err, 1e-5)
     del u, v, y, dm, out
     torch.cuda.empty_cache()
     return res
 
 
-def bench_lm_head_fwd_bwd(lp, torch, np, synth, steps, warmup):
+def bench_lm_head_fwd_bwd(lp, torch, np, synth, steps, warmup, cpu_seconds):
     cfg = synth.LMHead(T=114688, prompt_frac=0.2, temperature=1.0, grads=True, workload=synth.W_LM_HEAD_BWD).build()
     A = cfg.arrays
     hid, W = to_dev_bits(A["hidden"], "bf16"), to_dev_bits(A["weight"], "bf16")
     y, m = to_dev(A["targets"]), to_dev(A["mask"])
     glp, gH = to_dev(A["grad_logprob"]), to_dev(A["grad_entropy"])
     Ts = int(A["mask"].sum())
-    wsf = torch.empty(lp.lp_lm_head_workspace_bytes(cfg.T, cfg.h, cfg.V, cfg.tile_rows, False), dtype=torch.uint8,
-                      device="cuda")
-    wsb = torch.empty(lp.lp_lm_head_workspace_bytes(cfg.T, cfg.h, cfg.V, cfg.tile_rows, True), dtype=torch.uint8,
-                      device="cuda")
+    wsf_bytes = lp.lp_lm_head_workspace_bytes(cfg.T, cfg.h, cfg.V, cfg.tile_rows, False)
+    wsb_bytes = lp.lp_lm_head_workspace_bytes(cfg.T, cfg.h, cfg.V, cfg.tile_rows, True)
+    wsf = torch.empty(wsf_bytes, dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(wsb_bytes, dtype=torch.uint8, device="cuda")
     out = {}
 
     def step():
@@ -316,25 +411,74 @@ def bench_lm_head_fwd_bwd(lp, torch, np, synth, steps, warmup):
                                                            glp, gH, workspace=wsb)
         out["f"] = (lpv, Hv, lse)
 
-    kernels = ["k_fwd_tile", "k_bwd_dz", "k_out_gemm_dhidden", "k_out_gemm_dweight", "k_transpose_bf16"]
+    gemms = ("k_fwd_tile", "k_bwd_dz", "k_out_gemm_dhidden", "k_out_gemm_dweight")
+    kernels = list(gemms) + ["k_transpose_bf16", "k_splitk_reduce", "k_fwd_merge", "k_compact",
+                             "k_zero_unscored_rows"]
     ms, kt = _timed(lp, torch, step, steps, warmup, kernels)
     flop_step = 8.0 * Ts * cfg.V * cfg.h
-    mfma_ms = sum(kt[k][1] for k in ("k_fwd_tile", "k_bwd_dz", "k_out_gemm_dhidden", "k_out_gemm_dweight"))
+    mfma_ms = sum(kt[k][1] for k in gemms)
     achieved = flop_step * steps / (mfma_ms * 1e-3) / 1e12
+    # HBM traffic of the GEMMs per step from the PMC summary (per-launch bytes x launches per step)
+    traffic = None
+    per = [measured_traffic(k) for k in gemms]
+    if all(p is not None for p in per):
+        traffic = sum(p * kt[k][0] / steps for p, k in zip(per, gemms))
     res = dict(
         workload=f"fused LM-head forward + recompute backward: T={cfg.T} packed rows ({Ts} scored), h={cfg.h}, "
                  f"V={cfg.V}, bf16, tau {cfg.temperature}, tile {cfg.tile_rows}, dHidden and dW in fp32",
         ms_per_step=ms / steps, tokens_per_s=Ts * steps / (ms * 1e-3),
+        frac_of_peak_per_step=flop_step / (ms / steps * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
         roofline=dict(bound="mfma", kernel="all MFMA GEMMs (fwd + dZ recompute + dHidden + dW)", achieved=achieved,
-                      peak=BF16_PEAK_TFLOPS, unit="TFLOP/s", frac=achieved / BF16_PEAK_TFLOPS, traffic=None,
-                      algorithmic_flop_per_step=flop_step),
-        kernel_ms_per_step={k: v[1] / steps for k, v in kt.items()})
+                      peak=BF16_PEAK_TFLOPS, unit="TFLOP/s", frac=achieved / BF16_PEAK_TFLOPS, traffic=traffic,
+                      traffic_unit="HBM bytes per step of the four GEMM kinds (FETCH_SIZE + WRITE_SIZE, "
+                                   "copy-calibrated)",
+                      algorithmic_flop_per_step=flop_step,
+                      per_gemm_frac={k: (2.0 * Ts * cfg.V * cfg.h) * steps / (kt[k][1] * 1e-3) / 1e12
+                                     / BF16_PEAK_TFLOPS for k in gemms}),
+        kernel_ms_per_step={k: v[1] / steps for k, v in kt.items()},
+        launches_per_step={k: v[0] / steps for k, v in kt.items()})
+    fwd_mem = _memory_audit(torch, lambda: lp.lp_lm_head_logprobs_entropy(hid, W, y, m, cfg.temperature,
+                                                                          cfg.tile_rows),
+                            wsf_bytes, 3 * 4 * cfg.T, 4 * cfg.T * cfg.V)
+    lpv, Hv, lse = out["f"]
+    bwd_mem = _memory_audit(torch, lambda: lp.lp_lm_head_logprobs_entropy_backward(
+        hid, W, y, m, cfg.temperature, cfg.tile_rows, lse, Hv, glp, gH), wsb_bytes, 4 * (cfg.T + cfg.V) * cfg.h,
+        4 * cfg.T * cfg.V)
+    res["memory"] = dict(forward=fwd_mem, backward=bwd_mem)
+    if cpu_seconds > 0:
+        from oracle import lp_oracle as O  # CPU-baseline leg only
+        Wl = _LazyWeight(O, A["weight"])
+        dH_gpu = out["g"][0]
+
+        def run(rows):
+            # the oracle's per-row work of a forward + backward: logits, dZ, the rows' dHidden and their share
+            # of dW (formed block by block and dropped: dW sums over every row of the step)
+            Hr = O.widen_bf16(A["hidden"][rows])
+            _, dZ = O.lm_head_logit_grad(Hr, Wl, A["targets"][rows], None, cfg.temperature,
+                                         A["grad_logprob"][rows], A["grad_entropy"][rows])
+            dH = np.zeros((len(rows), cfg.h))
+            for j0 in range(0, cfg.V, 16384):
+                blk = dZ[:, j0:j0 + 16384]
+                dH += blk @ Wl[j0:j0 + 16384]
+                _ = blk.T @ Hr
+            return dH
+
+        rows, t, dH_o = _oracle_timed(np, run, np.nonzero(A["mask"])[0], cpu_seconds, 8)
+        got = dH_gpu[torch.as_tensor(rows, device="cuda")].double().cpu().numpy()
+        rel_fro = float(np.linalg.norm(got - dH_o) / np.linalg.norm(dH_o))
+        rel_max = float(np.abs(got - dH_o).max() / np.abs(dH_o).max())
+        res["cpu_baseline"] = _baseline(
+            len(rows), t, "scored tokens/s",
+            f"{len(rows)} scored rows of the same workload through the fp64 oracle's forward + backward "
+            f"(logits, dZ, the rows' dHidden and their dW share; full V={cfg.V}, h={cfg.h})",
+            max(rel_fro, rel_max), 1e-2, parity_metric="dHidden rows: max of relative Frobenius and "
+                                                       "max|diff| / max|ref|")
     del hid, W, y, m, glp, gH, wsf, wsb, out
     torch.cuda.empty_cache()
     return res
 
 
-def bench_kl_lm_head(lp, torch, np, synth, steps, warmup):
+def bench_kl_lm_head(lp, torch, np, synth, steps, warmup, cpu_seconds):
     """KL(teacher || student) rebuilt through both heads: forward timed over
     `steps`, forward + student backward over max(1, steps // 5)."""
     cfg = synth.KLHeads(grads=True).build()
@@ -342,10 +486,10 @@ def bench_kl_lm_head(lp, torch, np, synth, steps, warmup):
     heads = [to_dev_bits(A[k], "bf16") for k in ("student_hidden", "student_weight", "teacher_hidden",
                                                   "teacher_weight")]
     y, dm, g = to_dev(A["targets"]), to_dev(A["diff_mask"]), to_dev(A["grad_kl"])
-    wsf = torch.empty(lp.lp_lm_head_kl_workspace_bytes(cfg.T, cfg.h, cfg.V, cfg.tile_rows, False),
-                      dtype=torch.uint8, device="cuda")
-    wsb = torch.empty(lp.lp_lm_head_kl_workspace_bytes(cfg.T, cfg.h, cfg.V, cfg.tile_rows, True),
-                      dtype=torch.uint8, device="cuda")
+    wsf_bytes = lp.lp_lm_head_kl_workspace_bytes(cfg.T, cfg.h, cfg.V, cfg.tile_rows, False)
+    wsb_bytes = lp.lp_lm_head_kl_workspace_bytes(cfg.T, cfg.h, cfg.V, cfg.tile_rows, True)
+    wsf = torch.empty(wsf_bytes, dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(wsb_bytes, dtype=torch.uint8, device="cuda")
     out = {}
 
     def fwd():
@@ -369,7 +513,7 @@ def bench_kl_lm_head(lp, torch, np, synth, steps, warmup):
     pass_bytes = cfg.V * cfg.h * 2 + chunk_rows * cfg.h * 2 + chunk_rows * cfg.V * 4
     bsteps = max(1, steps // 5)
     bkernels = ["k_kl_teacher", "k_kl_student", "k_kl_dz", "k_out_gemm_dhidden", "k_out_gemm_dweight",
-                "k_transpose_bf16"]
+                "k_transpose_bf16", "k_splitk_reduce"]
     ms_b, kt_b = _timed(lp, torch, fwd_bwd, bsteps, min(1, warmup), bkernels)
     flop_fb = flop_fwd * 2 + 4.0 * cfg.T * cfg.V * cfg.h
     mfma_ms = sum(kt_b[k][1] for k in bkernels[:5])
@@ -393,20 +537,93 @@ def bench_kl_lm_head(lp, torch, np, synth, steps, warmup):
                                    achieved=achieved_b, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
                                    frac=achieved_b / BF16_PEAK_TFLOPS, algorithmic_flop_per_step=flop_fb),
                      kernel_ms_per_step={k: v[1] / bsteps for k, v in kt_b.items()}))
+    res["memory"] = _memory_audit(torch, lambda: lp.lp_lm_head_kl(*heads, None, y, dm, cfg.tile_rows), wsf_bytes,
+                                  6 * 4 * cfg.T, 2 * 4 * cfg.T * cfg.V)
+    if cpu_seconds > 0:
+        from oracle import lp_oracle as O  # CPU-baseline leg only
+        got = [t.cpu().numpy() for t in out["f"]]
+        Ws, Wt = _LazyWeight(O, A["student_weight"]), _LazyWeight(O, A["teacher_weight"])
+
+        def run(rows):
+            return O.lm_head_kl(O.widen_bf16(A["student_hidden"][rows]), Ws, O.widen_bf16(A["teacher_hidden"][rows]),
+                                Wt, None, A["targets"][rows], A["diff_mask"][rows])
+
+        rows, t, want = _oracle_timed(np, run, np.arange(cfg.T), cpu_seconds, 8)
+        err = max(np.abs(gv[rows] - w).max() for gv, w in zip(got, want))
+        res["cpu_baseline"] = _baseline(len(rows), t, "tokens/s",
+                                        f"{len(rows)} rows of the same workload through the fp64 oracle (both "
+                                        f"heads' logits, full V={cfg.V}, h={cfg.h}; forward)", err, 2e-3)
     del heads, y, dm, g, wsf, wsb, out
     torch.cuda.empty_cache()
     return res
 
 
+# ---------------------------------------------------------------------------
+# second denominators: what this GPU reaches
+# ---------------------------------------------------------------------------
+
+def _probe_lib():
+    import ctypes
+    path = os.path.join(ROOT, "entropy_chunked_row_amd", "liblp_probe.so")
+    if not os.path.exists(path):
+        return None
+    probe = ctypes.CDLL(path)
+    probe.lp_probe_read.restype = ctypes.c_int
+    probe.lp_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    probe.lp_probe_mfma.restype = ctypes.c_int
+    probe.lp_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    probe.lp_probe_clock_rates.restype = ctypes.c_int
+    probe.lp_probe_clock_rates.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
+    return probe
+
+
+def measure_mfma(torch, probe):
+    """Back-to-back v_mfma_f32_32x32x16_bf16 at two waves per SIMD on every CU
+    (liblp_probe.so), after SETTLE_SECONDS of the same work: the best of three
+    timed launches, and the shader clock the matrix cores ran at (ratio of the
+    shader-clock and fixed-frequency counters read inside the launch)."""
+    import ctypes
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    iters = 200000
+    clocks = torch.zeros(4 * cus, dtype=torch.int64, device="cuda")
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def run():
+        assert probe.lp_probe_mfma(cus, iters, clocks.data_ptr(), sink.data_ptr(), stream) == 0
+
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < SETTLE_SECONDS:
+        run()
+        torch.cuda.synchronize()
+    best, sclk = None, None
+    wall, peak = ctypes.c_int(0), ctypes.c_int(0)
+    rates_ok = probe.lp_probe_clock_rates(ctypes.byref(wall), ctypes.byref(peak)) == 0
+    flop = cus * 8 * iters * 8 * MFMA_FLOP
+    for _ in range(3):
+        ms = _events_ms(torch, run, 1)
+        tf = flop / (ms * 1e-3) / 1e12
+        if best is None or tf > best:
+            best = tf
+            c = clocks.cpu().numpy().reshape(-1, 4).astype("float64")
+            dt, dr = c[:, 1] - c[:, 0], c[:, 3] - c[:, 2]
+            if rates_ok and (dr > 0).all():
+                sclk = float((dt / dr).mean() * wall.value / 1e3)  # MHz
+    del clocks, sink
+    return dict(bf16_mfma_tflops=best, mfma_probe_sclk_mhz=sclk,
+                peak_sclk_mhz=peak.value / 1e3 if rates_ok else None,
+                mfma_probe=f"{cus} workgroups x 8 waves x {iters} x 8 back-to-back v_mfma_f32_32x32x16_bf16 "
+                           "(two waves per SIMD), best of 3 after the settle")
+
+
 def measure_achievable(torch):
     """Second denominators beside the datasheet peaks, measured on this GPU:
-    the read bandwidth of a streaming read of 4 GiB (the bench-only probe in
-    liblp_probe.so: one contiguous slice per workgroup, 16-byte non-temporal
-    loads; best of 4096-32768 workgroups) and a large library bf16 GEMM
-    (torch.matmul, 8192^3, contiguous operands)."""
-    import ctypes
-    out = dict(hbm_read_gbs=None, bf16_gemm_tflops=None,
-               source="liblp_probe.so streaming read of 4 GiB; torch.matmul bf16 8192^3 (library GEMM)")
+    the read bandwidth of a streaming read of 4 GiB and the bf16 matrix-core
+    rate of back-to-back MFMAs (both from the bench-only liblp_probe.so), and,
+    as context, a large library bf16 GEMM (torch.matmul, 8192^3)."""
+    out = dict(hbm_read_gbs=None, bf16_mfma_tflops=None, mfma_probe_sclk_mhz=None, bf16_gemm_tflops=None,
+               source="liblp_probe.so: streaming read of 4 GiB (best of 5 grid sizes), back-to-back MFMAs; "
+                      "torch.matmul bf16 8192^3 (library GEMM, context only)")
     a = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
     b = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
 
@@ -420,12 +637,9 @@ def measure_achievable(torch):
     gemm_ms = min(_events_ms(torch, gemm, 10) / 10 for _ in range(3))
     out["bf16_gemm_tflops"] = 2.0 * 8192 ** 3 / (gemm_ms * 1e-3) / 1e12
     del a, b
-    path = os.path.join(ROOT, "entropy_chunked_row_amd", "liblp_probe.so")
-    if os.path.exists(path):
-        probe = ctypes.CDLL(path)
-        probe.lp_probe_read.restype = ctypes.c_int
-        probe.lp_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
-                                        ctypes.c_void_p]
+    probe = _probe_lib()
+    if probe is not None:
+        out.update(measure_mfma(torch, probe))
         nbytes = 4 << 30
         buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
         sink = torch.zeros(1, dtype=torch.int32, device="cuda")
@@ -447,10 +661,14 @@ def measure_achievable(torch):
 def _add_achievable(roof, ach):
     if not roof or roof.get("achieved") is None:
         return
-    ref = ach["hbm_read_gbs"] if roof.get("unit") == "GB/s" else ach["bf16_gemm_tflops"]
-    if not ref:
-        return
-    roof["frac_of_achievable"] = roof["achieved"] / ref
+    if roof.get("unit") == "GB/s":
+        ref = ach.get("hbm_read_gbs")
+    else:
+        ref = ach.get("bf16_mfma_tflops")
+        if ach.get("bf16_gemm_tflops"):
+            roof["frac_of_library_gemm"] = roof["achieved"] / ach["bf16_gemm_tflops"]
+    if ref:
+        roof["frac_of_achievable"] = roof["achieved"] / ref
 
 
 def main():
@@ -459,11 +677,15 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--paths", default="all", help="comma list of " + ",".join(ALL_PATHS))
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline (0 = skip)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="budget of the headline path's oracle CPU baseline (0 = skip every CPU baseline)")
+    ap.add_argument("--cpu-seconds-path", type=float, default=6.0,
+                    help="budget of each other path's oracle CPU baseline")
     ap.add_argument("--settle-seconds", type=float, default=2.0,
                     help="untimed seconds of each path's step before its warm-up steps (steady GPU clocks)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB (reference for HBM counters)")
+    ap.add_argument("--no-achievable", action="store_true", help="skip the probes (profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -493,32 +715,40 @@ def main():
         log(f"calibration copy of {args.copy_calibration_mib} MiB done")
         del src, dst
         torch.cuda.empty_cache()
+    head_key = "lm_head_fwd" if "lm_head_fwd" in paths else paths[0]
+    cpu_head = args.cpu_seconds
+    cpu_path = args.cpu_seconds_path if args.cpu_seconds > 0 else 0.0
     results = {}
     for p in paths:
         log(f"path {p}: building inputs and timing")
         t0 = time.time()
+        cs = cpu_head if p == head_key else cpu_path
         if p == "lm_head_fwd":
-            results[p] = bench_lm_head_fwd(lp, torch, np, synth, args.steps, args.warmup, args.cpu_seconds)
+            results[p] = bench_lm_head_fwd(lp, torch, np, synth, args.steps, args.warmup, cs)
+        elif p == "tiny_lm_head":
+            results[p] = bench_tiny_lm_head(lp, torch, np, synth, args.steps, args.warmup, cs)
         elif p == "logits_input":
-            results[p] = bench_logits_input(lp, torch, np, synth, args.steps, args.warmup)
+            results[p] = bench_logits_input(lp, torch, np, synth, args.steps, args.warmup, cs)
         elif p == "kl_prob_diff":
-            results[p] = bench_kl(lp, torch, np, synth, args.steps, args.warmup)
+            results[p] = bench_kl(lp, torch, np, synth, args.steps, args.warmup, cs)
         elif p == "kl_lm_head":
-            results[p] = bench_kl_lm_head(lp, torch, np, synth, args.steps, args.warmup)
+            results[p] = bench_kl_lm_head(lp, torch, np, synth, args.steps, args.warmup, cs)
         elif p == "lm_head_fwd_bwd":
-            results[p] = bench_lm_head_fwd_bwd(lp, torch, np, synth, max(1, args.steps // 5),
-                                               min(1, args.warmup))
+            results[p] = bench_lm_head_fwd_bwd(lp, torch, np, synth, max(1, args.steps // 5), min(1, args.warmup),
+                                               cs)
         else:
             raise SystemExit(f"unknown path {p}")
         log(f"path {p}: done in {time.time() - t0:.1f}s: {results[p]['tokens_per_s']:.4g} tok/s, "
             f"{results[p]['ms_per_step']:.3f} ms/step")
 
-    ach = measure_achievable(torch)
-    log(f"achievable on this GPU: {ach['hbm_read_gbs'] or 0:.0f} GB/s read, {ach['bf16_gemm_tflops']:.0f} TFLOP/s bf16 GEMM")
+    ach = {} if args.no_achievable else measure_achievable(torch)
+    if ach:
+        log(f"achievable on this GPU: {ach['hbm_read_gbs'] or 0:.0f} GB/s read, "
+            f"{ach['bf16_mfma_tflops'] or 0:.0f} TFLOP/s bf16 MFMA at {ach['mfma_probe_sclk_mhz'] or 0:.0f} MHz, "
+            f"library GEMM {ach['bf16_gemm_tflops']:.0f} TFLOP/s")
     for r in results.values():
         _add_achievable(r.get("roofline"), ach)
         _add_achievable(r.get("fwd_bwd", {}).get("roofline"), ach)
-    head_key = "lm_head_fwd" if "lm_head_fwd" in results else paths[0]
     head = results[head_key]
     line = {
         "metric": METRIC,
@@ -537,10 +767,11 @@ def main():
         "config": {"workload": head["workload"], "path": head_key},
         "roofline": head["roofline"],
         "cpu_baseline": head.get("cpu_baseline"),
+        "memory": head.get("memory"),
         "achievable": ach,
         "paths": {k: v for k, v in results.items() if k != head_key},
-        "parity": ({head_key: {k: v for k, v in head["cpu_baseline"].items() if k.startswith("parity")}}
-                   if head.get("cpu_baseline") else {}),
+        "parity": {k: {f: v for f, v in r["cpu_baseline"].items() if f.startswith("parity")}
+                   for k, r in results.items() if r.get("cpu_baseline")},
     }
     print(json.dumps(line), flush=True)
 

@@ -122,8 +122,12 @@ static lp_status logprobs_entropy_impl(const void* logits, lp_dtype dtype, int64
   if (!aligned(logits, dtype_bytes(dtype)) || !aligned(logprob, 4) || (entropy && !aligned(entropy, 4)) ||
       !aligned(targets, 8))
     return fail(LP_ERR_INVALID_ARGUMENT, "lp_logprobs_entropy: misaligned pointer");
-  const int64_t chunk = (chunk_rows <= 0 || chunk_rows > T) ? T : chunk_rows;
-  if (chunk > 0x7fffffff) return fail(LP_ERR_UNSUPPORTED, "lp_logprobs_entropy: more than 2^31-1 rows per chunk");
+  // Chunks bound the rows whose fp32 copy exists at once in the page's
+  // design; here no fp32 copy exists (rows are widened in registers), so all
+  // chunks of the call run back to back in one launch, in row order: one
+  // drain of the grid per call instead of one per chunk, and results that do
+  // not depend on chunk_rows.
+  (void)chunk_rows;
   hipStream_t s = static_cast<hipStream_t>(stream);
   lp::RowArgs a;
   a.x = logits;
@@ -135,12 +139,10 @@ static lp_status logprobs_entropy_impl(const void* logits, lp_dtype dtype, int64
   a.c = exp2_scale(temperature);
   a.logprob = logprob;
   a.entropy = entropy;
-  for (int64_t r0 = 0; r0 < T; r0 += chunk) {
-    a.row0 = r0;
-    a.rows = (T - r0 < chunk) ? (T - r0) : chunk;
-    hipError_t e = lp::launch_logprobs_entropy(static_cast<int>(dtype), a, s);
-    if (e != hipSuccess) return hip_fail(e, "lp_logprobs_entropy launch");
-  }
+  a.row0 = 0;
+  a.rows = T;
+  hipError_t e = lp::launch_logprobs_entropy(static_cast<int>(dtype), a, s);
+  if (e != hipSuccess) return hip_fail(e, "lp_logprobs_entropy launch");
   return ok();
 }
 

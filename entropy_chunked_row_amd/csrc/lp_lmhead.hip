@@ -352,25 +352,37 @@ struct FwdArgs {
 // Block -> (vocab block, row block) of a launch.  The fast forward blocks the
 // rows of all the tiles of its launch as one sequence (row blocks may straddle
 // tiles; every row's result is the same either way), so only the launch's last
-// row block is partly filled.  Logical order: group of kGroupV vocab blocks ->
-// row block -> vocab block within the group, and each XCD (hardware puts
-// workgroup b on XCD b % 8) walks one contiguous range of that order: a
-// group's weight rows serve every row of the launch back to back while they
-// are still cached (the weight comes from HBM once per launch, not once per
-// tile), and the 32 workgroups an XCD runs at once cover 4 vocab blocks x 8
-// row blocks, which share their strips in its L2.  False for padding blocks.
-__device__ __forceinline__ bool fwd_block(const FwdArgs& a, int& vb, int& nb) {
-  const int L = xcd_remap(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
+// row block is partly filled.  The grid is sized on the host for every row of
+// the launch's tiles, but only the row blocks holding scored rows (the count
+// is on the device) are mapped: blocks 0 .. n_vb * live - 1 take them and the
+// rest exit at once, so empty row blocks take no place in the walk below.
+// Logical order: group of kGroupV vocab blocks -> row block -> vocab block
+// within the group, and each XCD (hardware puts workgroup b on XCD b % 8)
+// walks one contiguous range of that order: a group's weight rows serve every
+// row of the launch back to back while they are still cached (the weight
+// comes from HBM once per launch, not once per tile), and the 32 workgroups
+// an XCD runs at once cover 4 vocab blocks x 8 row blocks, which share their
+// strips in its L2.  False for blocks without work; `rows` = scored rows of
+// the launch.
+template <int BN>
+__device__ __forceinline__ bool fwd_block(const FwdArgs& a, int& vb, int& nb, int& rows) {
+  const int64_t rem = static_cast<int64_t>(*a.count) - a.tile_base;
+  rows = static_cast<int>(rem < a.tile_rows ? rem : a.tile_rows);
+  if (rows <= 0) return false;
+  const int n_nb = (rows + BN - 1) / BN;  // live row blocks (<= a.n_nb)
+  const int live = a.n_vb * n_nb;
+  const int b = static_cast<int>(blockIdx.x);
+  if (b >= live) return false;
+  const int L = xcd_remap(b, live);
   constexpr int G = kGroupV;
   const int full = a.n_vb / G;
-  const int span = G * a.n_nb;  // blocks of a full group
+  const int span = G * n_nb;  // blocks of a full group
   const int g = L / span;
   int gsz = G, w = L - g * span, v0 = g * G;
-  if (g >= full) {  // the last, smaller group, then padding
+  if (g >= full) {  // the last, smaller group
     gsz = a.n_vb - full * G;
     w = L - full * span;
     v0 = full * G;
-    if (gsz == 0 || w >= gsz * a.n_nb) return false;
   }
   nb = w / gsz;
   vb = v0 + w % gsz;
@@ -470,13 +482,9 @@ __device__ __forceinline__ void fwd_epilogue(const FwdArgs& a, f32x16_t (&acc)[C
 template <class C>
 __global__ void __launch_bounds__(C::NT) k_fwd_tile(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
-  int vb, nb;
-  if (!fwd_block(a, vb, nb)) return;
-  const int count = *a.count;
-  const int64_t rem = static_cast<int64_t>(count) - a.tile_base;
-  const int rows = static_cast<int>(rem < a.tile_rows ? rem : a.tile_rows);
+  int vb, nb, rows;
+  if (!fwd_block<C::BN>(a, vb, nb, rows)) return;
   const int n0 = nb * C::BN;
-  if (n0 >= rows) return;
   const int v0 = vb * C::BM;
   GemmOperands op;
   op.a = a.weight + static_cast<int64_t>(v0) * a.ld_w;
@@ -497,13 +505,9 @@ __global__ void __launch_bounds__(C::NT) k_fwd_tile(FwdArgs a) {
 template <class C>
 __global__ void __launch_bounds__(C::NT, LP_FWD_MIN_WAVES) k_fwd_tile_dtl(FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t lds[C::LDS_ELEMS];
-  int vb, nb;
-  if (!fwd_block(a, vb, nb)) return;
-  const int count = *a.count;
-  const int64_t rem = static_cast<int64_t>(count) - a.tile_base;
-  const int rows = static_cast<int>(rem < a.tile_rows ? rem : a.tile_rows);
+  int vb, nb, rows;
+  if (!fwd_block<C::BN>(a, vb, nb, rows)) return;
   const int n0 = nb * C::BN;
-  if (n0 >= rows) return;
   const int v0 = vb * C::BM;
   f32x16_t acc[C::MI][C::NI];
   gemm_tile_dtl<C>(a.weight + static_cast<int64_t>(v0) * a.ld_w, a.ld_w, a.V - v0, a.hidden, a.ld_h,
@@ -579,7 +583,7 @@ hipError_t launch_lmhead_forward(const LMHeadShape& sh, float* logprob, float* e
     const int ntile = static_cast<int>(left < group ? left : group);
     // the launch's ntile * tr rows in row blocks of bn, vocab blocks of bm
     const int n_nb = static_cast<int>((tr * ntile + bn - 1) / bn);
-    const int grid_blocks = (n_vb * n_nb + 7) / 8 * 8;
+    const int grid_blocks = n_vb * n_nb;  // blocks past the scored rows' blocks exit at once
     FwdArgs a;
     a.weight = sh.weight;
     a.ld_w = sh.ld_w;

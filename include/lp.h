@@ -7,8 +7,9 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * Pointers: every tensor argument is a DEVICE pointer owned by the caller.
- *   The library never allocates, frees or keeps device memory; scratch comes
- *   only from the caller's `workspace`.  Inputs are read-only and are never
+ *   The library never allocates or frees device memory; scratch comes from
+ *   the caller's `workspace`, except for the no-alloc forward, whose static
+ *   scratch array each GPU holds from the library's first use on it.  Inputs are read-only and are never
  *   modified (unlike an in-place cross-entropy).
  * Layout: row-major.  A [rows x cols] matrix has row r at base + r * ld
  *   elements, ld >= cols.  Targets are int64, one per row.  A mask is uint8,
@@ -79,9 +80,12 @@ const char* lp_last_error(void);
  * logits      [T x ld] of `dtype` (LP_BF16, LP_FP16 or LP_FP32), ld >= V.
  * targets     int64 [T].  mask: uint8 [T] or NULL.
  * temperature see the file header.
- * chunk_rows  rows per launch; <= 0 means all rows in one launch.  Chunks have
- *             chunk_rows rows with a short last chunk (5 rows in chunks of 2
- *             -> 2, 2, 1).  Results do not depend on chunk_rows, bit for bit.
+ * chunk_rows  the page's chunk size (<= 0: one chunk).  On the page it bounds
+ *             the rows widened to an fp32 tensor at once; this kernel never
+ *             forms such a tensor (each row is widened in registers), so the
+ *             chunks of a call (chunk_rows rows each, a short last one: 5 rows
+ *             in chunks of 2 -> 2, 2, 1) run back to back in one launch.
+ *             Memory use and results do not depend on it, bit for bit.
  * logprob     fp32 [T] (required).  entropy: fp32 [T] or NULL.
  * T == 0 returns LP_OK without launching.  Needs no workspace.
  */

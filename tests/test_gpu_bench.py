@@ -15,8 +15,9 @@ pytestmark = pytest.mark.gpu
 
 def test_bench_prints_one_json_line_with_the_contract(monkeypatch, capsys):
     import bench
-    monkeypatch.setattr(sys, "argv", ["bench.py", "--paths", "lm_head_fwd,logits_input", "--steps", "2",
-                                      "--warmup", "1", "--settle-seconds", "0.2", "--cpu-seconds", "1"])
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--paths", "lm_head_fwd,logits_input,tiny_lm_head", "--steps",
+                                      "2", "--warmup", "1", "--settle-seconds", "0.2", "--cpu-seconds", "1",
+                                      "--cpu-seconds-path", "0.5"])
     bench.main()
     lines = [ln for ln in capsys.readouterr().out.splitlines() if ln.strip()]
     assert len(lines) == 1
@@ -37,3 +38,18 @@ def test_bench_prints_one_json_line_with_the_contract(monkeypatch, capsys):
     assert c["parity_max_abs_err"] <= c["parity_tol"]
     li = d["paths"]["logits_input"]["roofline"]
     assert li["bound"] == "hbm" and li["unit"] == "GB/s" and li["peak"] == 8000.0 and 0 < li["frac"] < 1.5
+    # every path: the oracle timed beside it (with parity on its rows) and the memory one call allocates
+    for name, path in [("lm_head_fwd", d)] + list(d["paths"].items()):
+        c = path["cpu_baseline"]
+        assert c["kind"] == "oracle" and c["value"] > 0 and c["parity_max_abs_err"] <= c["parity_tol"], name
+        mem = path["memory"]
+        assert mem["within_workspace_plus_outputs"], (name, mem)
+        if name != "tiny_lm_head":  # 64 x 1024 logits are smaller than the workspace's fixed parts
+            assert mem["peak_delta_bytes"] < 0.05 * mem["fp32_logits_bytes"], (name, mem)
+    tiny = d["paths"]["tiny_lm_head"]
+    assert tiny["roofline"] is None and tiny["us_per_call"] > 0
+    # second denominators measured on this GPU: read probe, MFMA probe with its clock, library GEMM
+    a = d["achievable"]
+    assert a["hbm_read_gbs"] > 1000 and a["bf16_mfma_tflops"] > 500 and a["bf16_gemm_tflops"] > 100
+    assert a["mfma_probe_sclk_mhz"] is None or 100 < a["mfma_probe_sclk_mhz"] < 5000
+    assert r["frac_of_achievable"] == pytest.approx(r["achieved"] / a["bf16_mfma_tflops"])
