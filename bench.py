@@ -412,8 +412,8 @@ def bench_lm_head_fwd_bwd(lp, torch, np, synth, steps, warmup, cpu_seconds):
         out["f"] = (lpv, Hv, lse)
 
     gemms = ("k_fwd_tile", "k_bwd_dz", "k_out_gemm_dhidden", "k_out_gemm_dweight")
-    kernels = list(gemms) + ["k_transpose_bf16", "k_splitk_reduce", "k_fwd_merge", "k_compact",
-                             "k_zero_unscored_rows"]
+    kernels = list(gemms) + ["k_gather_rows", "k_splitk_reduce", "k_fwd_merge", "k_compact",
+                             "k_zero_unscored_rows", "k_transpose_bf16"]
     ms, kt = _timed(lp, torch, step, steps, warmup, kernels)
     flop_step = 8.0 * Ts * cfg.V * cfg.h
     mfma_ms = sum(kt[k][1] for k in gemms)
@@ -513,7 +513,7 @@ def bench_kl_lm_head(lp, torch, np, synth, steps, warmup, cpu_seconds):
     pass_bytes = cfg.V * cfg.h * 2 + chunk_rows * cfg.h * 2 + chunk_rows * cfg.V * 4
     bsteps = max(1, steps // 5)
     bkernels = ["k_kl_teacher", "k_kl_student", "k_kl_dz", "k_out_gemm_dhidden", "k_out_gemm_dweight",
-                "k_transpose_bf16", "k_splitk_reduce"]
+                "k_gather_rows", "k_splitk_reduce", "k_transpose_bf16"]
     ms_b, kt_b = _timed(lp, torch, fwd_bwd, bsteps, min(1, warmup), bkernels)
     flop_fb = flop_fwd * 2 + 4.0 * cfg.T * cfg.V * cfg.h
     mfma_ms = sum(kt_b[k][1] for k in bkernels[:5])

@@ -1,11 +1,13 @@
-// bf16 MFMA GEMM mainloop for gfx950, both operands K-contiguous ("NT"):
+// bf16 MFMA GEMM mainloops for gfx950:
 //   D[m][n] = sum_k A[m][k] * B[n][k]
-// A rows come from a row-major matrix (row m at a + m * lda); B rows are
-// either contiguous or gathered through an index list (the scored rows of the
-// hidden states).  Accumulators are fp32 and stay in registers; the caller's
-// epilogue consumes them.
+// The generic loop (gemm_tile) takes K-contiguous ("NT") operands: A rows
+// from a row-major matrix (row m at a + m * lda), B rows contiguous or
+// gathered through an index list (the scored rows of the hidden states).  The
+// fast loop further down (gemm_tile_dtl*) also takes K-major operands.
+// Accumulators are fp32 and stay in registers; the caller's epilogue
+// consumes them.
 //
-// Tiling: a workgroup of NT = 64 * WGM * WGN threads computes a BM x BN tile;
+// Generic tiling: a workgroup of NT = 64 * WGM * WGN threads computes a BM x BN tile;
 // wave (wm, wn) owns a (BM / WGM) x (BN / WGN) sub-tile made of 32x32
 // v_mfma_f32_32x32x16_bf16 tiles.  K advances BK at a time through two LDS
 // buffers: while the waves multiply out of one buffer, the next K-slice is
@@ -200,19 +202,32 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
 
 
 // ---------------------------------------------------------------------------
-// Fast NT mainloop for K % BK == 0: global -> LDS with buffer_load_dwordx4 ...
+// Fast mainloop for K % BK == 0: global -> LDS with buffer_load_dwordx4 ...
 // lds (no register staging), XOR-swizzled LDS rows, NS LDS stages, fragment
 // prefetch one K-substep ahead.
 //
-// LDS row = BK bf16 = KC chunks of 16 bytes; the chunk holding logical 16-byte
-// column kc of row r sits at position kc ^ swz(r), so the 32 lanes reading one
-// fragment column (rows r..r+31, same kc) spread over all banks:
+// Each operand is either K-contiguous ("NT", element (m, k) at m * ld + k)
+// or K-major (element (m, k) at k * ld + m: the m index is contiguous).
+//
+// K-contiguous operand: LDS row = one m, BK bf16 = KC chunks of 16 bytes; the
+// chunk holding logical 16-byte column kc of row r sits at position
+// kc ^ swz(r), so the 32 lanes reading one fragment column (rows r..r+31,
+// same kc) spread over all banks:
 //   BK = 64 (128-byte rows): swz(r) = (r & 7) ^ ((r >> 3) & 1);
 //   BK = 32 (64-byte rows, two rows per 128-byte bank line): swz(r) = (r >> 1) & 3.
+// K-major operand: LDS row = one k, ROWS (= BM or BN) bf16 = ROWS / 8 chunks;
+// chunk mc of row k sits at mc ^ (4 (k & 3)).  Its MFMA fragments come from
+// gfx950's transposing LDS read (ds_read_b64_tr_b16): within each 16-lane
+// group, lane (r, c) = ((lane & 15) >> 2, lane & 3) names 4 consecutive
+// elements of row r, and after the read lane j holds element j of each of
+// the 4 rows; two reads give a lane its 8 consecutive k of one m, the layout
+// the MFMA takes.  With the swizzle the 16 (row, chunk) pairs a half-wave
+// touches fall in distinct banks.
 // Each wave-wide load instruction fills 64 consecutive chunk slots (1 KB), so
 // every lane loads the global chunk that belongs in its slot.
-// Rows past the valid range are clamped to the last valid row (their results
-// are discarded by the caller); K must be a multiple of BK.
+// Rows (K-contiguous) or chunks (K-major) past the valid range are clamped to
+// the last valid one (their results are discarded by the caller); K-major
+// rows past `kvalid` are clamped likewise.  K must be a multiple of BK.
 // ---------------------------------------------------------------------------
 
 #ifndef LP_FRAG_PER_SLOT
@@ -223,11 +238,14 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
 #endif
 
 typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 
-template <int BM_, int BN_, int WGM_, int WGN_, int BK_ = 64, int NS_ = 2>
+template <int BM_, int BN_, int WGM_, int WGN_, int BK_ = 64, int NS_ = 2, bool AKM_ = false, bool BKM_ = false>
 struct DtlCfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, WGM = WGM_, WGN = WGN_;
   static constexpr int NS = NS_;                      // LDS stages
+  static constexpr bool AKM = AKM_, BKM = BKM_;       // K-major operands
   static constexpr int NT = 64 * WGM * WGN;
   static constexpr int NW = WGM * WGN;
   static constexpr int WTM = BM / WGM, WTN = BN / WGN;
@@ -258,6 +276,8 @@ struct DtlCfg {
   static_assert((BM * KC) % (64 * LW) == 0 && (BN * KC) % (64 * LW) == 0, "tile not divisible among waves");
   static_assert(BK == 64 || BK == 32, "LDS swizzle defined for 64- and 128-byte rows");
   static_assert(NS >= 2 && (NS & (NS - 1)) == 0, "stage count must be a power of two >= 2");
+  static_assert(!AKM || (BM % 128 == 0 && BK % 16 == 0), "K-major A: rows of at least 16 chunks");
+  static_assert(!BKM || (BN % 128 == 0 && BK % 16 == 0), "K-major B: rows of at least 16 chunks");
 };
 
 __device__ __forceinline__ int lds_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
@@ -270,10 +290,13 @@ __device__ __forceinline__ int lds_swz_k(int r) {
     return (r >> 1) & 3;
 }
 
+// K-major rows: chunk position of logical chunk mc in LDS row k is mc ^ lds_swz_km(k).
+__device__ __forceinline__ int lds_swz_km(int k) { return 4 * (k & 3); }
+
 // Row sources of one operand for this thread: a buffer resource on the
 // operand base and the byte offset of the global chunk each of its load
-// instructions moves; the stage's K offset goes in the scalar offset, so a
-// load needs no vector address arithmetic.
+// instructions moves; the stage's K offset (kstart x kstride bytes) goes in
+// the scalar offset, so a load needs no vector address arithmetic.
 // The buffer-resource type exists only in the device pass; the host pass
 // parses device code without generating it.
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -288,6 +311,8 @@ template <int NINST>
 struct DtlRows {
   dtl_rsrc_t rsrc;
   uint32_t off[NINST];  // byte offsets from the operand base (the caller checks they fit in 32 bits)
+  uint32_t kstride;     // bytes per unit of K: 2 (K-contiguous) or ld * 2 (K-major)
+  int kvalid;           // K-major: rows of K that exist (the rest are clamped to the last)
 };
 
 // Raw buffer over [base, base + 4 GiB): offsets are kept in range by the row
@@ -313,7 +338,7 @@ __device__ __forceinline__ void dtl_load16(const dtl_rsrc_t& rsrc, uint16_t* dst
 #endif
 }
 
-// A operand: rows m0 + r of a row-major matrix (clamped to M - 1).
+// K-contiguous operand: rows m0 + r of a row-major matrix (clamped to M - 1).
 template <class C, int NINST>
 __device__ __forceinline__ void dtl_rows_dense(DtlRows<NINST>& rw, int64_t ld, int M) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -325,9 +350,11 @@ __device__ __forceinline__ void dtl_rows_dense(DtlRows<NINST>& rw, int64_t ld, i
     const int rr = r < M ? r : M - 1;
     rw.off[j] = static_cast<uint32_t>((static_cast<int64_t>(rr) * ld + kc * 8) * 2);
   }
+  rw.kstride = 2;
+  rw.kvalid = 0x7fffffff;
 }
 
-// B operand: gathered rows rows[r], or rows r when rows is null (clamped to N - 1).
+// K-contiguous operand, gathered rows rows[r], or rows r when rows is null (clamped to N - 1).
 template <class C, int NINST>
 __device__ __forceinline__ void dtl_rows_gather(DtlRows<NINST>& rw, int64_t ld, const int* rows, int N) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -340,9 +367,72 @@ __device__ __forceinline__ void dtl_rows_gather(DtlRows<NINST>& rw, int64_t ld, 
     const int64_t src = rows ? static_cast<int64_t>(rows[rr]) : static_cast<int64_t>(rr);
     rw.off[j] = static_cast<uint32_t>((src * ld + kc * 8) * 2);
   }
+  rw.kstride = 2;
+  rw.kvalid = 0x7fffffff;
 }
 
-// One 16-byte fragment read: piece q < MI reads A fragment q, else B fragment q - MI.
+// K-major operand of ROWS (= BM or BN) m-columns per LDS row: element (m, k)
+// at base + k * ld + m; columns from `mvalid` on are clamped to the last valid
+// 8-column chunk, K rows from `kvalid` on to row kvalid - 1 (at issue time).
+template <class C, int NINST, int ROWS>
+__device__ __forceinline__ void dtl_rows_km(DtlRows<NINST>& rw, int64_t ld, int mvalid, int kvalid) {
+  constexpr int CPR = ROWS / 8;  // chunks per LDS row
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int cmax = (mvalid - 1) >> 3;
+#pragma unroll
+  for (int j = 0; j < NINST; ++j) {
+    const int slot = (j * C::LW + wave) * 64 + lane;
+    const int k = slot / CPR, pc = slot % CPR;
+    int mc = pc ^ lds_swz_km(k);
+    mc = mc < cmax ? mc : cmax;
+    rw.off[j] = static_cast<uint32_t>((static_cast<int64_t>(k) * ld + mc * 8) * 2);
+  }
+  rw.kstride = static_cast<uint32_t>(ld * 2);
+  rw.kvalid = kvalid;
+}
+
+// 8 bf16 of one K-major fragment: rows kk + 8 (g >> 1) + [0, 8) of column
+// mb + 16 (g & 1) + (lane & 15), g = lane >> 4, from an LDS stage region of
+// ROWS columns per row -- the MFMA operand layout (lane l: m = l % 32,
+// k = 8 (l / 32) + [0, 8)).
+//
+// The two reads are issued as inline assembly: through the compiler builtin,
+// the compiler cannot tell them from the in-flight direct-to-LDS loads of
+// other stages and waits for all global loads before each one.  The
+// compiler therefore does not track these reads either; the K loop waits for
+// them itself (dtl_wait_frags before the MFMAs that use them, and before each
+// stage barrier, so no read of a stage is in flight once it is reloaded).
+template <int ROWS>
+__device__ __forceinline__ bf16x8_t dtl_frag_km(const uint16_t* region, int kk, int mb) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, r = (lane >> 2) & 3, c = lane & 3;
+  const int m = mb + 16 * (g & 1) + 4 * c;
+  const int k0 = kk + 8 * (g >> 1) + r;
+  const int pos = (((m >> 3) ^ lds_swz_km(r)) << 3) + (m & 7);  // k0 & 3 == r
+  const uint32_t a = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)(region + k0 * ROWS + pos)));
+  typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+  u32x2_t lo, hi;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(lo) : "v"(a));
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi) : "v"(a), "i"(4 * ROWS * 2));
+  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+  return __builtin_bit_cast(bf16x8_t, u32x4_t{lo[0], lo[1], hi[0], hi[1]});
+}
+
+// Waits until every LDS read this wave issued has returned; the fragment
+// registers are tied to the wait so that no MFMA reading them is scheduled
+// before it.  Needed only when a fragment comes from dtl_frag_km.
+template <class C>
+__device__ __forceinline__ void dtl_wait_frags(bf16x8_t (&fa)[C::MI], bf16x8_t (&fb)[C::NI]) {
+  if constexpr (C::AKM || C::BKM) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < C::MI; ++i) asm volatile("" : "+v"(fa[i]));
+#pragma unroll
+    for (int i = 0; i < C::NI; ++i) asm volatile("" : "+v"(fb[i]));
+  }
+}
+
+// One fragment: piece q < MI reads A fragment q, else B fragment q - MI.
 template <class C>
 __device__ __forceinline__ void dtl_frag_piece(const uint16_t* stage, int kk, int wm, int wn, int q,
                                                bf16x8_t (&af)[C::MI], bf16x8_t (&bfr)[C::NI]) {
@@ -350,30 +440,52 @@ __device__ __forceinline__ void dtl_frag_piece(const uint16_t* stage, int kk, in
   const int r32 = lane & 31;
   const int pc = ((kk >> 3) + (lane >> 5)) ^ lds_swz_k<C::KC>(r32);
   if (q < C::MI) {
-    af[q] = *reinterpret_cast<const bf16x8_t*>(stage + (wm * C::WTM + q * 32 + r32) * C::BK + pc * 8);
+    if constexpr (C::AKM)
+      af[q] = dtl_frag_km<C::BM>(stage, kk, wm * C::WTM + q * 32);
+    else
+      af[q] = *reinterpret_cast<const bf16x8_t*>(stage + (wm * C::WTM + q * 32 + r32) * C::BK + pc * 8);
   } else {
     const int ni = q - C::MI;
-    bfr[ni] = *reinterpret_cast<const bf16x8_t*>(stage + (C::BM + wn * C::WTN + ni * 32 + r32) * C::BK + pc * 8);
+    if constexpr (C::BKM)
+      bfr[ni] = dtl_frag_km<C::BN>(stage + C::BM * C::BK, kk, wn * C::WTN + ni * 32);
+    else
+      bfr[ni] = *reinterpret_cast<const bf16x8_t*>(stage + (C::BM + wn * C::WTN + ni * 32 + r32) * C::BK + pc * 8);
   }
 }
 
-// Issue global load instruction j (A for j < A_INST, else B) of a stage; the
-// bases already include the stage's K offset (uniform), the per-lane part is a
-// 32-bit offset.  Only the first LW waves load (see DtlCfg::LW).
+// Per-lane offset of load instruction j of a K-major operand for the stage
+// starting at K index kstart: rows past kvalid - 1 are moved back to it
+// (only in a stage that reaches past kvalid; the test is uniform).
+template <class C, int NINST, int ROWS>
+__device__ __forceinline__ uint32_t dtl_km_off(const DtlRows<NINST>& rw, int j, int kstart, int wave) {
+  uint32_t voff = rw.off[j];
+  if (kstart + C::BK > rw.kvalid) {
+    const int lane = threadIdx.x & 63;
+    const int k = ((j * C::LW + wave) * 64 + lane) / (ROWS / 8);
+    const int over = kstart + k - (rw.kvalid - 1);
+    if (over > 0) voff -= static_cast<uint32_t>(over) * rw.kstride;
+  }
+  return voff;
+}
+
+// Issue global load instruction j (A for j < A_INST, else B) of the stage
+// starting at K index kstart; the per-lane part is a 32-bit offset, the
+// stage's K offset a scalar one.  Only the first LW waves load (see DtlCfg::LW).
 template <class C, int NA, int NB>
-__device__ __forceinline__ void dtl_issue_one(int j, uint32_t kbytes, const DtlRows<NA>& ra, const DtlRows<NB>& rb,
+__device__ __forceinline__ void dtl_issue_one(int j, int kstart, const DtlRows<NA>& ra, const DtlRows<NB>& rb,
                                               uint16_t* stage, int wave) {
   // `wave` is the uniform (scalar) wave index, so the LDS destination (M0) is scalar arithmetic
   if (j < NA) {
     uint16_t* dst = stage + (j * C::LW + wave) * 64 * 8;
-    dtl_load16(ra.rsrc, dst, ra.off[j], kbytes);
+    const uint32_t voff = C::AKM ? dtl_km_off<C, NA, C::BM>(ra, j, kstart, wave) : ra.off[j];
+    dtl_load16(ra.rsrc, dst, voff, static_cast<uint32_t>(kstart) * ra.kstride);
   } else {
     const int jb = j - NA;
     uint16_t* dst = stage + C::BM * C::BK + (jb * C::LW + wave) * 64 * 8;
-    dtl_load16(rb.rsrc, dst, rb.off[jb], kbytes);
+    const uint32_t voff = C::BKM ? dtl_km_off<C, NB, C::BN>(rb, jb, kstart, wave) : rb.off[jb];
+    dtl_load16(rb.rsrc, dst, voff, static_cast<uint32_t>(kstart) * rb.kstride);
   }
 }
-
 // Wait until at most `pending` stages' worth of this wave's global loads are
 // still in flight (pending is uniform and at most 3).
 template <class C>
@@ -400,9 +512,10 @@ __device__ __forceinline__ void dtl_wait_vm(int pending) {
 //                      complete in Y; every wave is done reading X).
 //   substep S-1:       MFMAs on X (fragments already in registers); between them,
 //                      the first fragments of the next stage (from Y) and the
-//                      global loads of the stage NS steps ahead (into X).
+//                      global loads of the stage NS steps ahead (into X),
+//                      which starts at K index k2.
 template <class C, bool NEXT, bool NEXT2>
-__device__ __forceinline__ void dtl_kstep(uint16_t* X, uint16_t* Y, uint32_t kb2, const DtlRows<C::A_INST>& ra,
+__device__ __forceinline__ void dtl_kstep(uint16_t* X, uint16_t* Y, int k2, const DtlRows<C::A_INST>& ra,
                                           const DtlRows<C::B_INST>& rb, int wm, int wn,
                                           bf16x8_t (&fa)[2][C::MI], bf16x8_t (&fb)[2][C::NI],
                                           f32x16_t (&acc)[C::MI][C::NI], int pending, int wave) {
@@ -417,6 +530,7 @@ __device__ __forceinline__ void dtl_kstep(uint16_t* X, uint16_t* Y, uint32_t kb2
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     const int cur = s & 1;
+    dtl_wait_frags<C>(fa[cur], fb[cur]);
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       // fragment reads of the next substep, PER per MFMA slot from the start
@@ -436,7 +550,7 @@ __device__ __forceinline__ void dtl_kstep(uint16_t* X, uint16_t* Y, uint32_t kb2
 #pragma unroll
         for (int u = 0; u < (NL + NQ - 1) / NQ; ++u) {
           const int j = q * ((NL + NQ - 1) / NQ) + u;
-          if (j < NL) dtl_issue_one<C, C::A_INST, C::B_INST>(j, kb2, ra, rb, X, wave);
+          if (j < NL) dtl_issue_one<C, C::A_INST, C::B_INST>(j, k2, ra, rb, X, wave);
         }
       }
       const int mi = q / C::NI, ni = q % C::NI;
@@ -444,6 +558,7 @@ __device__ __forceinline__ void dtl_kstep(uint16_t* X, uint16_t* Y, uint32_t kb2
       __builtin_amdgcn_sched_barrier(0);
     }
     if (NEXT && s == S - 2) {
+      dtl_wait_frags<C>(fa[cur ^ 1], fb[cur ^ 1]);
       dtl_wait_vm<C>(pending);
       __syncthreads();
     }
@@ -457,7 +572,7 @@ __device__ __forceinline__ void dtl_kstep(uint16_t* X, uint16_t* Y, uint32_t kb2
 // The last column's B fragment is read after the substep's last MFMA, before
 // the stage barrier, so no wave reads a stage that others may overwrite.
 template <class C, bool NEXT, bool NEXT2>
-__device__ __forceinline__ void dtl_kstep_bi(uint16_t* X, uint16_t* Y, uint32_t kb2, const DtlRows<C::A_INST>& ra,
+__device__ __forceinline__ void dtl_kstep_bi(uint16_t* X, uint16_t* Y, int k2, const DtlRows<C::A_INST>& ra,
                                              const DtlRows<C::B_INST>& rb, int wm, int wn,
                                              bf16x8_t (&fa)[2][C::MI], bf16x8_t (&fb)[C::NI],
                                              f32x16_t (&acc)[C::MI][C::NI], int pending, int wave) {
@@ -465,6 +580,7 @@ __device__ __forceinline__ void dtl_kstep_bi(uint16_t* X, uint16_t* Y, uint32_t 
   constexpr int NQ = C::MI * C::NI;
   constexpr int NL = C::A_INST + C::B_INST;
   static_assert(S % 2 == 0, "substep 0 of every stage must use A fragment set 0");
+  static_assert(!C::AKM && !C::BKM, "in-place B fragments: K-contiguous operands only");
   const bool loader = C::LW == C::NW || wave < C::LW;
   bf16x8_t dummy[C::MI];
 #pragma unroll
@@ -482,7 +598,7 @@ __device__ __forceinline__ void dtl_kstep_bi(uint16_t* X, uint16_t* Y, uint32_t 
 #pragma unroll
         for (int u = 0; u < (NL + NQ - 1) / NQ; ++u) {
           const int j = q * ((NL + NQ - 1) / NQ) + u;
-          if (j < NL) dtl_issue_one<C, C::A_INST, C::B_INST>(j, kb2, ra, rb, X, wave);
+          if (j < NL) dtl_issue_one<C, C::A_INST, C::B_INST>(j, k2, ra, rb, X, wave);
         }
       }
       const int ni = q / C::MI, mi = q % C::MI;
@@ -497,15 +613,11 @@ __device__ __forceinline__ void dtl_kstep_bi(uint16_t* X, uint16_t* Y, uint32_t 
   }
 }
 
-// D[m][n] = sum_k A[m][k] * B[rows[n]][k] over K (multiple of 64, may be 0).
-// a: bf16 rows of the block (row 0 = the block's first row, column 0 = the
-// first K column used), M valid rows; b: bf16 base of the gathered matrix,
-// b_rows the gather list (null: rows 0..N-1 of b), N valid rows.  Byte
-// offsets of every row read from a and b must fit in 32 bits.
+// The K loop of one block on prepared row sources (see gemm_tile_dtl and
+// gemm_tile_dtl_dense below).  K is a multiple of BK and may be 0 (D = 0).
 template <class C>
-__device__ __forceinline__ void gemm_tile_dtl(const uint16_t* a, int64_t lda, int M, const uint16_t* b,
-                                              int64_t ldb, const int* b_rows, int N, int K, uint16_t* lds,
-                                              f32x16_t (&acc)[C::MI][C::NI]) {
+__device__ __forceinline__ void gemm_dtl_loop(const DtlRows<C::A_INST>& ra, const DtlRows<C::B_INST>& rb, int K,
+                                              uint16_t* lds, f32x16_t (&acc)[C::MI][C::NI]) {
   constexpr int NF = C::MI + C::NI;
   constexpr int NL = C::A_INST + C::B_INST;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar registers
@@ -516,14 +628,6 @@ __device__ __forceinline__ void gemm_tile_dtl(const uint16_t* a, int64_t lda, in
     for (int ni = 0; ni < C::NI; ++ni)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
-
-  DtlRows<C::A_INST> ra;
-  DtlRows<C::B_INST> rb;
-  dtl_rows_dense<C, C::A_INST>(ra, lda, M);
-  dtl_rows_gather<C, C::B_INST>(rb, ldb, b_rows, N);
-  ra.rsrc = dtl_rsrc(a);
-  rb.rsrc = dtl_rsrc(b);
-  constexpr int KB = C::BK * 2;  // bytes per stage along K
   const int nk = K / C::BK;
   if (nk <= 0) return;  // empty K: D = 0
   // prologue: the first min(NS, nk) stages in flight, wait for stage 0, read its first fragments
@@ -534,8 +638,7 @@ __device__ __forceinline__ void gemm_tile_dtl(const uint16_t* a, int64_t lda, in
       if (st < npro) {
 #pragma unroll
         for (int j = 0; j < NL; ++j)
-          dtl_issue_one<C, C::A_INST, C::B_INST>(j, static_cast<uint32_t>(st * KB), ra, rb,
-                                                 lds + st * C::STAGE_ELEMS, wave);
+          dtl_issue_one<C, C::A_INST, C::B_INST>(j, st * C::BK, ra, rb, lds + st * C::STAGE_ELEMS, wave);
       }
     }
     dtl_wait_vm<C>(npro - 1);
@@ -546,23 +649,70 @@ __device__ __forceinline__ void gemm_tile_dtl(const uint16_t* a, int64_t lda, in
   for (int q = 0; q < NF; ++q) dtl_frag_piece<C>(lds, 0, wm, wn, q, fa[0], fb[0]);
 
   auto stage = [&](int k) { return lds + (k & (C::NS - 1)) * C::STAGE_ELEMS; };
-  auto kstep = [&](auto next, auto next2, int kt, uint32_t kbn, int pending) {
+  auto kstep = [&](auto next, auto next2, int kt, int k2, int pending) {
     if constexpr (C::B_INPLACE)
-      dtl_kstep_bi<C, decltype(next)::value, decltype(next2)::value>(stage(kt), stage(kt + 1), kbn, ra, rb, wm, wn,
+      dtl_kstep_bi<C, decltype(next)::value, decltype(next2)::value>(stage(kt), stage(kt + 1), k2, ra, rb, wm, wn,
                                                                      fa, fb[0], acc, pending, wave);
     else
-      dtl_kstep<C, decltype(next)::value, decltype(next2)::value>(stage(kt), stage(kt + 1), kbn, ra, rb, wm, wn, fa,
+      dtl_kstep<C, decltype(next)::value, decltype(next2)::value>(stage(kt), stage(kt + 1), k2, ra, rb, wm, wn, fa,
                                                                   fb, acc, pending, wave);
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
   int kt = 0;
   // steady state: stage kt + NS is loaded into stage kt's buffer; NS - 2 later stages stay in flight
-  for (; kt + C::NS < nk; ++kt) kstep(T_{}, T_{}, kt, static_cast<uint32_t>((kt + C::NS) * KB), C::NS - 2);
+  for (; kt + C::NS < nk; ++kt) kstep(T_{}, T_{}, kt, (kt + C::NS) * C::BK, C::NS - 2);
   // drain: no more loads; stages kt + 2 .. nk - 1 are still in flight
-  for (; kt + 1 < nk; ++kt) kstep(T_{}, F_{}, kt, 0u, nk - kt - 2);
-  kstep(F_{}, F_{}, kt, 0u, 0);
+  for (; kt + 1 < nk; ++kt) kstep(T_{}, F_{}, kt, 0, nk - kt - 2);
+  kstep(F_{}, F_{}, kt, 0, 0);
   __syncthreads();
+}
+
+// D[m][n] = sum_k A[m][k] * B[rows[n]][k] over K (multiple of 64, may be 0),
+// both operands K-contiguous.  a: bf16 rows of the block (row 0 = the block's
+// first row, column 0 = the first K column used), M valid rows; b: bf16 base
+// of the gathered matrix, b_rows the gather list (null: rows 0..N-1 of b), N
+// valid rows.  Byte offsets of every row read from a and b must fit in 32 bits.
+template <class C>
+__device__ __forceinline__ void gemm_tile_dtl(const uint16_t* a, int64_t lda, int M, const uint16_t* b,
+                                              int64_t ldb, const int* b_rows, int N, int K, uint16_t* lds,
+                                              f32x16_t (&acc)[C::MI][C::NI]) {
+  static_assert(!C::AKM && !C::BKM, "K-contiguous operands");
+  DtlRows<C::A_INST> ra;
+  DtlRows<C::B_INST> rb;
+  dtl_rows_dense<C, C::A_INST>(ra, lda, M);
+  dtl_rows_gather<C, C::B_INST>(rb, ldb, b_rows, N);
+  ra.rsrc = dtl_rsrc(a);
+  rb.rsrc = dtl_rsrc(b);
+  gemm_dtl_loop<C>(ra, rb, K, lds, acc);
+}
+
+// D[m][n] = sum_k A(m, k) * B(n, k) over K (multiple of 64, may be 0) on
+// dense operands, each K-contiguous or K-major as C::AKM / C::BKM say:
+//   K-contiguous: element (m, k) at a + m * lda + k, M valid rows;
+//   K-major:      element (m, k) at a + k * lda + m, M valid columns, and
+//                 rows k >= kvalid_a clamped to kvalid_a - 1 (zero
+//                 multipliers on the other side must make them irrelevant).
+// a and b point at the block's element (0, 0).  Every per-lane byte offset
+// (one BM- or BN-row block of a K-contiguous operand, BK rows of a K-major
+// one) and K x the K-major pitch in bytes must fit in 32 bits.
+template <class C>
+__device__ __forceinline__ void gemm_tile_dtl_dense(const uint16_t* a, int64_t lda, int M, int kvalid_a,
+                                                    const uint16_t* b, int64_t ldb, int N, int kvalid_b, int K,
+                                                    uint16_t* lds, f32x16_t (&acc)[C::MI][C::NI]) {
+  DtlRows<C::A_INST> ra;
+  DtlRows<C::B_INST> rb;
+  if constexpr (C::AKM)
+    dtl_rows_km<C, C::A_INST, C::BM>(ra, lda, M, kvalid_a);
+  else
+    dtl_rows_dense<C, C::A_INST>(ra, lda, M);
+  if constexpr (C::BKM)
+    dtl_rows_km<C, C::B_INST, C::BN>(rb, ldb, N, kvalid_b);
+  else
+    dtl_rows_gather<C, C::B_INST>(rb, ldb, nullptr, N);
+  ra.rsrc = dtl_rsrc(a);
+  rb.rsrc = dtl_rsrc(b);
+  gemm_dtl_loop<C>(ra, rb, K, lds, acc);
 }
 
 }  // namespace lp

@@ -18,11 +18,14 @@
 //   k_fwd_merge     merges a row's partial states in a fixed order and writes
 //                   log-prob, entropy and log-sum-exp.
 //   backward        k_bwd_dz recomputes the tile's logits with the same GEMM
-//                   and writes dL/dlogits (bf16) in both [row][vocab] and
-//                   [vocab][row] order; dHidden (= dZ . W, K = vocab, split
-//                   over K) and dW (+= dZ^T . H_tile, K = tile rows) are NT
-//                   GEMMs on those buffers and on transposed copies of W and
-//                   of the tile's hidden rows.
+//                   and writes dL/dlogits (bf16) as dZ [row][vocab];
+//                   dHidden (= dZ . W, K = vocab, split over K) reads the
+//                   weight as stored (a K-major operand) and dW (+= dZ^T .
+//                   H, K = the rows of two consecutive tiles) reads dZ and a
+//                   dense copy of the tiles' hidden rows as K-major operands,
+//                   through the LDS transposing reads.  The generic tiles
+//                   (h % 64 != 0) write dZ in both orders and multiply
+//                   against transposed copies of W and of the tile's rows.
 //   KL              both models' heads: see the KL section below.
 #include "lp_device.hpp"
 #include "lp_gemm.hpp"
@@ -62,11 +65,16 @@ constexpr int kFwdTilesPerLaunch = LP_FWD_TILES_PER_LAUNCH;
 #define LP_BWD_DTL_TILE 256, 256, 4, 2
 #endif
 using BwdDtlCfg = DtlCfg<LP_BWD_DTL_TILE>;
-// The backward's dense gradient GEMMs (dHidden, dW): N is the hidden width.
+// The backward's dense gradient GEMMs (N is the hidden width), straight on
+// the dZ buffer [rows][vocab] and the weight / the tile's hidden rows as
+// stored: dHidden = dZ . W takes W as a K-major operand (its rows are the K
+// index), dW = dZ^T . H_tile takes both operands K-major (K = the tile's rows).
 #ifndef LP_DENSE_DTL_TILE
 #define LP_DENSE_DTL_TILE 256, 256, 4, 2
 #endif
-using DenseDtlCfg = DtlCfg<LP_DENSE_DTL_TILE>;
+using DenseDhCfg = DtlCfg<LP_DENSE_DTL_TILE, 64, 2, false, true>;
+using DenseDwCfg = DtlCfg<LP_DENSE_DTL_TILE, 64, 2, true, true>;
+using DenseDtlCfg = DenseDhCfg;  // block shape shared by both
 // KL through both heads on the fast path: two passes per chunk of at most
 // kKLChunk scored rows on this tile.  The teacher pass stores its fp32 logits
 // for the chunk; the student pass's epilogue reads them back.  Measured on
@@ -143,12 +151,17 @@ bool head_fast(int64_t T, int64_t h, int64_t ld_h, int64_t ld_w) {
   return h % FwdDtlCfg::BK == 0 && h % KLCfg::BK == 0 && u32_span(T, ld_h, h) && u32_span(kDtlWeightRows, ld_w, h);
 }
 
-// ... and for the backward's dense gradient GEMMs on the dZ buffers: dHidden
-// reads blocks of dZ [rows][vpad] and W^T [h][vpad] rows over K = vpad, dW
-// blocks of dZ^T [vocab][tpad] and H_tile^T [h][tpad] rows over K = tpad.
-bool dense_fast(int64_t vpad, int64_t tpad) {
+// ... and for the backward's gradient GEMMs, per tile of tpad rows (tile_rows
+// rounded up to 64) and vpad vocab columns (V rounded up to 64): dHidden reads
+// 256-row blocks of dZ [rows][vpad] and the weight as a K-major operand (K
+// index = vocab row, up to vpad rows of pitch ld_w); dW reads dZ and the
+// tile's hidden rows [rows][h] as K-major operands over K = the rows of one
+// tile, or of two (tiles_per_dw) when that also fits.
+bool dense_fast(int64_t vpad, int64_t tpad, int64_t h, int64_t ld_w, int tiles_per_dw = 1) {
   constexpr int R = DenseDtlCfg::BM > DenseDtlCfg::BN ? DenseDtlCfg::BM : DenseDtlCfg::BN;
-  return u32_span(R, vpad, vpad) && u32_span(R, tpad, tpad);
+  const int64_t ksplit = static_cast<int64_t>(align_up(static_cast<size_t>((vpad + kSplitK - 1) / kSplitK), 64));
+  const int64_t kt = tiles_per_dw * tpad;
+  return u32_span(R, vpad, vpad) && u32_span(ksplit, ld_w, R) && u32_span(kt, vpad, R) && u32_span(kt, h, R);
 }
 
 bool lmhead_fast_path(const LMHeadShape& sh) { return head_fast(sh.T, sh.h, sh.ld_h, sh.ld_w); }
@@ -164,7 +177,44 @@ bool lmhead_fast_tiles(int64_t T, int64_t h, int64_t V, int64_t ld_h, int64_t ld
                        int backward) {
   if (!head_fast(T, h, ld_h, ld_w)) return false;
   if (!backward) return true;
-  return dense_fast(static_cast<int64_t>(align_up(static_cast<size_t>(V), 64)), bwd_tpad(T, tile_rows));
+  return dense_fast(static_cast<int64_t>(align_up(static_cast<size_t>(V), 64)), bwd_tpad(T, tile_rows), h, ld_w);
+}
+
+// The backward's buffers from the workspace base + dz_off.  Generic tiles: dZ,
+// dZ^T, W^T, H_tile^T, dHidden partials.  Direct-to-LDS tiles: the dZ of two
+// consecutive tiles (the dW GEMM runs once per pair, with K = both tiles'
+// rows) and the two tiles' hidden rows, dHidden partials.  The scratch is the
+// larger of the two, so either path runs in a workspace sized for the call.
+struct BwdBuffers {
+  uint16_t *dz, *dzt, *wt, *ht;  // generic
+  uint16_t *dz2, *ht2;           // direct-to-LDS (pair of tiles)
+  float* hpart;
+};
+
+size_t bwd_scratch_bytes(int64_t tr, int64_t h, int64_t vpad) {
+  const size_t tpad = align_up(static_cast<size_t>(tr), 64), V = static_cast<size_t>(vpad), H = static_cast<size_t>(h);
+  const size_t part = align_up(static_cast<size_t>(kSplitK) * tr * H * 4, 256);
+  const size_t generic = align_up(tpad * V * 2, 256) * 2 + align_up(H * V * 2, 256) + align_up(H * tpad * 2, 256);
+  const size_t fast = align_up(2 * tpad * V * 2, 256) + align_up(2 * tpad * H * 2, 256);
+  return (generic > fast ? generic : fast) + part;
+}
+
+BwdBuffers bwd_buffers(char* base, int64_t tr, int64_t h, int64_t vpad) {
+  const size_t tpad = align_up(static_cast<size_t>(tr), 64), V = static_cast<size_t>(vpad), H = static_cast<size_t>(h);
+  BwdBuffers b;
+  size_t off = 0;
+  b.dz = b.dz2 = reinterpret_cast<uint16_t*>(base);
+  off = align_up(tpad * V * 2, 256);
+  b.dzt = reinterpret_cast<uint16_t*>(base + off);
+  off += align_up(tpad * V * 2, 256);
+  b.wt = reinterpret_cast<uint16_t*>(base + off);
+  off += align_up(H * V * 2, 256);
+  b.ht = reinterpret_cast<uint16_t*>(base + off);
+  off += align_up(H * tpad * 2, 256);
+  b.ht2 = reinterpret_cast<uint16_t*>(base + align_up(2 * tpad * V * 2, 256));
+  const size_t fast = align_up(2 * tpad * V * 2, 256) + align_up(2 * tpad * H * 2, 256);
+  b.hpart = reinterpret_cast<float*>(base + (off > fast ? off : fast));
+  return b;
 }
 
 // One dispatch covers at most 2^32 - 1 work-items per grid dimension.  True
@@ -238,13 +288,11 @@ bool lmhead_workspace_layout(int64_t T, int64_t h, int64_t V, int64_t tile_rows,
     w->zy_off = off;
     off = align_up(off + zrows * per_row * 4, 256);
   } else {  // backward == 1 or 3
-    const size_t tpad = align_up(static_cast<size_t>(tr), 64);
-    w->dz_off = off;  // dZ [tpad x vpad], dZ^T [vpad x tpad], W^T [h x vpad], H_tile^T [h x tpad]
-    off = align_up(off + tpad * static_cast<size_t>(w->vpad) * 2, 256);
-    off = align_up(off + tpad * static_cast<size_t>(w->vpad) * 2, 256);
-    off = align_up(off + static_cast<size_t>(h) * static_cast<size_t>(w->vpad) * 2, 256);
-    off = align_up(off + static_cast<size_t>(h) * tpad * 2, 256);
-    off = align_up(off + static_cast<size_t>(kSplitK) * tr * static_cast<size_t>(h) * 4, 256);  // dHidden partials
+    // generic tiles: dZ [tpad x vpad], dZ^T [vpad x tpad], W^T [h x vpad], H_tile^T [h x tpad];
+    // direct-to-LDS tiles: dZ of two tiles [2 tpad x vpad], their hidden rows [2 tpad x h];
+    // both: the split-K partials of dHidden [kSplitK x tr x h] fp32 (see bwd_buffers)
+    w->dz_off = off;
+    off += bwd_scratch_bytes(tr, h, w->vpad);
   }
   if (backward >= 2) {
     // teacher logits of one chunk: [vocab block][row block][BM x BN] floats
@@ -933,23 +981,30 @@ __global__ void __launch_bounds__(C::NT) k_bwd_dz_dtl(DzArgs a) {
   dz_epilogue<C, true>(a, acc, v0, n0, rows, rowsK, lds);
 }
 
-// Fast gradient GEMMs on dense K-contiguous operands (K multiple of 64):
-//   dHidden: A = dZ [rows x vpad], B = W^T [h x vpad], K split into `splits`
-//            ranges; each split writes an fp32 partial [rows x h] that
-//            k_splitk_reduce sums in a fixed order.
-//   dW:      A = dZ^T [V x tpad], B = H_tile^T [h x tpad], K = the tile's rows
-//            rounded up to 64; dW is written (first tile) or accumulated.
+// Fast gradient GEMMs (K multiple of 64) on the dZ buffer [rows][vpad] as
+// written by the dZ kernels:
+//   dHidden: A = dZ (K-contiguous, K = vpad), B = W (K-major: row v of the
+//            weight is K index v; rows past V are clamped, their dZ columns
+//            are 0), K split into `splits` ranges; each split writes an fp32
+//            partial [rows x h] that k_splitk_reduce sums in a fixed order.
+//   dW:      A = dZ (K-major, M = vocab), B = the tiles' hidden rows [rows][h]
+//            (K-major), K = the rows of one or two consecutive tiles (the
+//            second tile's rows start at row tpad); dW is written (first
+//            launch) or accumulated.
 struct DenseGemmArgs {
   const uint16_t* a;
   int64_t lda;
-  int M;              // A rows; if count != nullptr: the tile's valid rows instead
+  int M;              // if m_from_count: the tile's valid rows instead
   const uint16_t* b;
   int64_t ldb;
   int N;
-  int K;              // if k_from_count: rows of the tile rounded up to 64
+  int K;              // if k_from_count: the tiles' rows, each tile rounded up to 64
+  int kvalid_b;       // K-major B: rows of B that exist
   const int* count;
   int64_t tile_base;
   int tile_rows;
+  int64_t tpad;       // k_from_count: row offset of the second tile
+  int ntiles;         // k_from_count: tiles in this launch (1 or 2)
   int m_from_count, k_from_count;
   int splits;         // K ranges (blockIdx spans n_mb * n_nb * splits)
   int ksplit;         // K per split (multiple of 64)
@@ -959,29 +1014,48 @@ struct DenseGemmArgs {
   int n_mb, n_nb;
 };
 
-template <class C>
+// Valid rows of tile `t` of a launch (device count).
+__device__ __forceinline__ int tile_rows_of(const int* count, int64_t base, int tile_rows, int t) {
+  const int64_t rem = static_cast<int64_t>(*count) - base - static_cast<int64_t>(t) * tile_rows;
+  return static_cast<int>(rem < tile_rows ? (rem > 0 ? rem : 0) : tile_rows);
+}
+
+// Row blocks per group in the walk of the gradient GEMMs (tile_coords): the
+// hidden-gradient GEMM's rows are the tile's rows, the weight-gradient GEMM's
+// the vocabulary.
+#ifndef LP_DH_GROUP
+#define LP_DH_GROUP 4
+#endif
+#ifndef LP_DW_GROUP
+#define LP_DW_GROUP 4
+#endif
+
+template <class C, int G>
 __global__ void __launch_bounds__(C::NT) k_dense_gemm_dtl(DenseGemmArgs g) {
   __shared__ __attribute__((aligned(1024))) uint16_t lds[C::LDS_ELEMS];
   const int per = g.n_mb * g.n_nb;
   const int ks = blockIdx.x / per;
   int mb, nb;
-  tile_coords(xcd_remap(blockIdx.x - ks * per, per), g.n_mb, g.n_nb, mb, nb);
-  int rows = 0;
+  tile_coords<G>(xcd_remap(blockIdx.x - ks * per, per), g.n_mb, g.n_nb, mb, nb);
+  int rows = 0, K = g.K;
   if (g.count) {
-    const int64_t rem = static_cast<int64_t>(*g.count) - g.tile_base;
-    rows = static_cast<int>(rem < g.tile_rows ? (rem > 0 ? rem : 0) : g.tile_rows);
+    rows = tile_rows_of(g.count, g.tile_base, g.tile_rows, 0);
+    if (g.k_from_count) {
+      const int rows2 = g.ntiles > 1 ? tile_rows_of(g.count, g.tile_base, g.tile_rows, 1) : 0;
+      K = rows2 > 0 ? static_cast<int>(g.tpad) + ((rows2 + 63) & ~63) : ((rows + 63) & ~63);
+    }
   }
   const int M = g.m_from_count ? rows : g.M;
-  const int K = g.k_from_count ? ((rows + 63) & ~63) : g.K;
   const int m0 = mb * C::BM, n0 = nb * C::BN;
   if (m0 >= M) return;
   if (g.k_from_count && K == 0 && g.accumulate) return;
   const int kbeg = ks * g.ksplit;
   const int klen = (K - kbeg < g.ksplit) ? (K - kbeg) : g.ksplit;
   f32x16_t acc[C::MI][C::NI];
-  gemm_tile_dtl<C>(g.a + static_cast<int64_t>(m0) * g.lda + kbeg, g.lda, M - m0,
-                   g.b + static_cast<int64_t>(n0) * g.ldb + kbeg, g.ldb, nullptr, g.N - n0, klen > 0 ? klen : 0, lds,
-                   acc);
+  const uint16_t* a = C::AKM ? g.a + m0 + static_cast<int64_t>(kbeg) * g.lda : g.a + static_cast<int64_t>(m0) * g.lda + kbeg;
+  const uint16_t* b = C::BKM ? g.b + n0 + static_cast<int64_t>(kbeg) * g.ldb : g.b + static_cast<int64_t>(n0) * g.ldb + kbeg;
+  gemm_tile_dtl_dense<C>(a, g.lda, M - m0, 0x7fffffff, b, g.ldb, g.N - n0, g.kvalid_b - kbeg, klen > 0 ? klen : 0, lds,
+                         acc);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave % C::WGM, wn = wave / C::WGM;
@@ -1021,6 +1095,26 @@ __global__ void __launch_bounds__(C::NT) k_dense_gemm_dtl(DenseGemmArgs g) {
           *p = g.accumulate ? (*p + acc[mi][ni][i]) : acc[mi][ni][i];
         }
       }
+  }
+}
+
+// Dense copy of a tile's hidden rows for the weight-gradient GEMM:
+// dst[r][0, h) = src[idx[base + r]][0, h) for the tile's valid rows r, 0 for
+// the other rows below nr_pad (h % 8 == 0, 16-byte aligned rows).
+__global__ void __launch_bounds__(256) k_gather_rows_bf16(const uint16_t* __restrict__ src, int64_t ld,
+                                                          const int* __restrict__ idx, const int* __restrict__ count,
+                                                          int64_t base, int tile_rows, int nr_pad, int h,
+                                                          uint16_t* __restrict__ dst) {
+  const int rows = tile_rows_of(count, base, tile_rows, 0);
+  const int nv = h / 8;
+  for (int r = blockIdx.x; r < nr_pad; r += gridDim.x) {
+    uint4* d = reinterpret_cast<uint4*>(dst + static_cast<int64_t>(r) * h);
+    if (r < rows) {
+      const uint4* sp = reinterpret_cast<const uint4*>(src + static_cast<int64_t>(idx[base + r]) * ld);
+      for (int i = threadIdx.x; i < nv; i += 256) d[i] = sp[i];
+    } else {
+      for (int i = threadIdx.x; i < nv; i += 256) d[i] = make_uint4(0, 0, 0, 0);
+    }
   }
 }
 
@@ -1115,104 +1209,62 @@ __global__ void __launch_bounds__(C::NT) k_out_gemm(OutGemmArgs g) {
   }
 }
 
-// Steps shared by both losses' backward: scored-row compaction, W^T, then per
-// tile of rows: dL/dlogits (launched by `launch_dz`, which also zero-pads rows
-// up to a multiple of 64 on the fast path), dHidden and dW.
-template <class LaunchDz>
-hipError_t backward_tiles(const LMHeadShape& sh, bool fast, int bm_fast, int bn_fast, float* grad_hidden,
-                          float* grad_weight,
-                          char* ws, const LMHeadWorkspace& w, hipStream_t s, LaunchDz&& launch_dz) {
-  using C = BwdCfg;
-  using F = DenseDtlCfg;
-  int* idx = reinterpret_cast<int*>(ws + w.idx_off);
-  int* count = reinterpret_cast<int*>(ws + w.count_off);
-  const int64_t tr = sh.tile_rows < sh.T ? sh.tile_rows : sh.T;
-  const int64_t tpad = static_cast<int64_t>(align_up(static_cast<size_t>(tr), 64));
-  const int64_t vpad = w.vpad;
-  uint16_t* dz = reinterpret_cast<uint16_t*>(ws + w.dz_off);
-  size_t off = align_up(w.dz_off + static_cast<size_t>(tpad) * vpad * 2, 256);
-  uint16_t* dzt = reinterpret_cast<uint16_t*>(ws + off);
-  off = align_up(off + static_cast<size_t>(tpad) * vpad * 2, 256);
-  uint16_t* wt = reinterpret_cast<uint16_t*>(ws + off);
-  off = align_up(off + static_cast<size_t>(sh.h) * vpad * 2, 256);
-  uint16_t* ht = reinterpret_cast<uint16_t*>(ws + off);
-  off = align_up(off + static_cast<size_t>(sh.h) * tpad * 2, 256);
-  float* hpart = reinterpret_cast<float*>(ws + off);  // split-K partials of dHidden (fast path)
-
+// First steps of both losses' backward: the scored-row list, and zeros in the
+// hidden gradient of the unscored rows.
+inline hipError_t backward_prologue(const LMHeadShape& sh, float* grad_hidden, int* idx, int* count, hipStream_t s) {
   {
     TimedLaunch tl("k_compact", s);
     hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, s, sh.mask, sh.T, idx, count, zero_outs());
   }
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !grad_hidden) return e;
+  {
+    TimedLaunch tl("k_zero_unscored_rows", s);
+    const unsigned blocks = static_cast<unsigned>(sh.T < 65536 ? sh.T : 65536);
+    hipLaunchKernelGGL(k_zero_unscored_rows, dim3(blocks), dim3(256), 0, s, sh.mask, sh.T, sh.h, grad_hidden);
+  }
+  return hipGetLastError();
+}
+
+// Generic tiles (any h % 8 == 0): per tile of rows, dL/dlogits (launched by
+// `launch_dz`) in both [row][vocab] and [vocab][row] order, then dHidden and
+// dW as NT GEMMs against a once-per-call W^T and the tile's H^T.
+template <class LaunchDz>
+hipError_t backward_tiles_generic(const LMHeadShape& sh, float* grad_hidden, float* grad_weight, char* ws,
+                                  const LMHeadWorkspace& w, hipStream_t s, LaunchDz&& launch_dz) {
+  using C = BwdCfg;
+  int* idx = reinterpret_cast<int*>(ws + w.idx_off);
+  int* count = reinterpret_cast<int*>(ws + w.count_off);
+  const int64_t tr = sh.tile_rows < sh.T ? sh.tile_rows : sh.T;
+  const int64_t tpad = static_cast<int64_t>(align_up(static_cast<size_t>(tr), 64));
+  const int64_t vpad = w.vpad;
+  const BwdBuffers bb = bwd_buffers(ws + w.dz_off, tr, sh.h, vpad);
+  hipError_t e = backward_prologue(sh, grad_hidden, idx, count, s);
   if (e != hipSuccess) return e;
   if (grad_hidden) {
-    {
-      TimedLaunch tl("k_zero_unscored_rows", s);
-      const unsigned blocks = static_cast<unsigned>(sh.T < 65536 ? sh.T : 65536);
-      hipLaunchKernelGGL(k_zero_unscored_rows, dim3(blocks), dim3(256), 0, s, sh.mask, sh.T, sh.h, grad_hidden);
-    }
-    if ((e = hipGetLastError()) != hipSuccess) return e;
     // W^T [h x vpad], zero past V
     dim3 g(static_cast<unsigned>((vpad + 63) / 64), static_cast<unsigned>((sh.h + 63) / 64));
     {
       TimedLaunch tl("k_transpose_bf16", s);
       hipLaunchKernelGGL(k_transpose_bf16, g, dim3(256), 0, s, sh.weight, sh.ld_w, static_cast<const int*>(nullptr),
-                         static_cast<const int*>(nullptr), int64_t(0), sh.V, sh.V, static_cast<int>(vpad), sh.h, wt,
+                         static_cast<const int*>(nullptr), int64_t(0), sh.V, sh.V, static_cast<int>(vpad), sh.h, bb.wt,
                          vpad);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  const int bm = fast ? bm_fast : C::BM;
-  const int bn = fast ? bn_fast : C::BN;
-  const int n_vb = (sh.V + bm - 1) / bm;
-  const int n_nb = static_cast<int>((tr + bn - 1) / bn);
+  const int n_vb = (sh.V + C::BM - 1) / C::BM;
+  const int n_nb = static_cast<int>((tr + C::BN - 1) / C::BN);
   for (int64_t base = 0; base < sh.T; base += tr) {
-    if ((e = launch_dz(base, tr, tpad, vpad, n_vb, n_nb, idx, count, dz, grad_weight ? dzt : nullptr)) != hipSuccess)
+    if ((e = launch_dz(base, tr, tpad, vpad, n_vb, n_nb, idx, count, bb.dz, grad_weight ? bb.dzt : nullptr)) !=
+        hipSuccess)
       return e;
-
-    if (grad_hidden && fast) {
-      // dHidden[idx[r]] = dZ[r] . W : K = vpad split into kSplitK ranges, then a fixed-order sum
-      DenseGemmArgs g;
-      g.a = dz;
-      g.lda = vpad;
-      g.M = 0;
-      g.b = wt;
-      g.ldb = vpad;
-      g.N = sh.h;
-      g.K = static_cast<int>(vpad);
-      g.count = count;
-      g.tile_base = base;
-      g.tile_rows = static_cast<int>(tr);
-      g.m_from_count = 1;
-      g.k_from_count = 0;
-      g.splits = kSplitK;
-      g.ksplit = static_cast<int>(align_up(static_cast<size_t>((vpad + kSplitK - 1) / kSplitK), 64));
-      g.out = hpart;
-      g.ldo = sh.h;
-      g.accumulate = 0;
-      g.n_mb = static_cast<int>((tr + F::BM - 1) / F::BM);
-      g.n_nb = (sh.h + F::BN - 1) / F::BN;
-      {
-        TimedLaunch tl("k_out_gemm_dhidden", s);
-        hipLaunchKernelGGL(k_dense_gemm_dtl<F>, dim3(static_cast<unsigned>(g.n_mb) * g.n_nb * kSplitK), dim3(F::NT),
-                           0, s, g);
-      }
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-      {
-        TimedLaunch tl("k_splitk_reduce", s);
-        const int64_t n4 = tr * sh.h / 4;
-        const unsigned blocks = static_cast<unsigned>(n4 < 65536 * 256 ? (n4 + 255) / 256 : 65536);
-        hipLaunchKernelGGL(k_splitk_reduce, dim3(blocks), dim3(256), 0, s, hpart, kSplitK, static_cast<int>(tr), sh.h,
-                           static_cast<const int*>(idx), static_cast<const int*>(count), base, grad_hidden);
-      }
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-    } else if (grad_hidden) {
+    if (grad_hidden) {
       // dHidden[idx[r]] = dZ[r] . W  :  A = dZ [rows x vpad], B = W^T [h x vpad], K = vpad
       OutGemmArgs g;
-      g.op.a = dz;
+      g.op.a = bb.dz;
       g.op.lda = vpad;
       g.op.M = 0;
-      g.op.b = wt;
+      g.op.b = bb.wt;
       g.op.ldb = vpad;
       g.op.b_rows = nullptr;
       g.op.N = sh.h;
@@ -1240,65 +1292,161 @@ hipError_t backward_tiles(const LMHeadShape& sh, bool fast, int bm_fast, int bn_
         TimedLaunch tl("k_transpose_bf16", s);
         hipLaunchKernelGGL(k_transpose_bf16, gt, dim3(256), 0, s, sh.hidden, sh.ld_h, static_cast<const int*>(idx),
                            static_cast<const int*>(count), base, 0, static_cast<int>(tr), static_cast<int>(tpad), sh.h,
-                           ht, tpad);
+                           bb.ht, tpad);
       }
       if ((e = hipGetLastError()) != hipSuccess) return e;
-      if (fast) {
-        // dW (+)= dZ^T . H_tile : A = dZ^T [V x tpad], B = H_tile^T [h x tpad], K = rows rounded up to 64
-        DenseGemmArgs g;
-        g.a = dzt;
-        g.lda = tpad;
-        g.M = sh.V;
-        g.b = ht;
-        g.ldb = tpad;
-        g.N = sh.h;
-        g.K = 0;
-        g.count = count;
-        g.tile_base = base;
-        g.tile_rows = static_cast<int>(tr);
-        g.m_from_count = 0;
-        g.k_from_count = 1;
-        g.splits = 1;
-        g.ksplit = static_cast<int>(tpad);
-        g.out = grad_weight;
-        g.ldo = sh.h;
-        g.accumulate = base == 0 ? 0 : 1;
-        g.n_mb = (sh.V + F::BM - 1) / F::BM;
-        g.n_nb = (sh.h + F::BN - 1) / F::BN;
-        {
-          TimedLaunch tl("k_out_gemm_dweight", s);
-          hipLaunchKernelGGL(k_dense_gemm_dtl<F>, dim3(static_cast<unsigned>(g.n_mb) * g.n_nb), dim3(F::NT), 0, s, g);
-        }
-      } else {
-        // dW (+)= dZ^T . H_tile : A = dZ^T [V x tpad], B = H_tile^T [h x tpad], K = rows8
-        OutGemmArgs g;
-        g.op.a = dzt;
-        g.op.lda = tpad;
-        g.op.M = sh.V;
-        g.op.b = ht;
-        g.op.ldb = tpad;
-        g.op.b_rows = nullptr;
-        g.op.N = sh.h;
-        g.op.K = 0;
-        g.count = count;
-        g.tile_base = base;
-        g.tile_rows = static_cast<int>(tr);
-        g.mode = 1;
-        g.out_rows = nullptr;
-        g.out = grad_weight;
-        g.ldo = sh.h;
-        g.accumulate = base == 0 ? 0 : 1;
-        g.n_mb = (sh.V + C::BM - 1) / C::BM;
-        g.n_nb = (sh.h + C::BN - 1) / C::BN;
-        {
-          TimedLaunch tl("k_out_gemm_dweight", s);
-          hipLaunchKernelGGL(k_out_gemm<C>, dim3(static_cast<unsigned>(g.n_mb) * g.n_nb), dim3(C::NT), 0, s, g);
-        }
+      // dW (+)= dZ^T . H_tile : A = dZ^T [V x tpad], B = H_tile^T [h x tpad], K = rows8
+      OutGemmArgs g;
+      g.op.a = bb.dzt;
+      g.op.lda = tpad;
+      g.op.M = sh.V;
+      g.op.b = bb.ht;
+      g.op.ldb = tpad;
+      g.op.b_rows = nullptr;
+      g.op.N = sh.h;
+      g.op.K = 0;
+      g.count = count;
+      g.tile_base = base;
+      g.tile_rows = static_cast<int>(tr);
+      g.mode = 1;
+      g.out_rows = nullptr;
+      g.out = grad_weight;
+      g.ldo = sh.h;
+      g.accumulate = base == 0 ? 0 : 1;
+      g.n_mb = (sh.V + C::BM - 1) / C::BM;
+      g.n_nb = (sh.h + C::BN - 1) / C::BN;
+      {
+        TimedLaunch tl("k_out_gemm_dweight", s);
+        hipLaunchKernelGGL(k_out_gemm<C>, dim3(static_cast<unsigned>(g.n_mb) * g.n_nb), dim3(C::NT), 0, s, g);
       }
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
   }
   return hipSuccess;
+}
+
+// Direct-to-LDS tiles (h % 64 == 0 and 32-bit offsets): per tile of rows,
+// dL/dlogits [row][vocab] only (launched by `launch_dz`, rows zero-padded up
+// to a multiple of 64), the tile's hidden rows copied densely, dHidden = dZ .
+// W on W as stored, and dW = dZ^T . H once per pair of consecutive tiles
+// (each tile's dZ and hidden rows go to one half of a two-tile buffer), so
+// the fp32 dW is read and written half as often.  No transposed copy of any
+// operand is made.
+template <class LaunchDz>
+hipError_t backward_tiles_fast(const LMHeadShape& sh, int bm, int bn, float* grad_hidden, float* grad_weight,
+                               char* ws, const LMHeadWorkspace& w, hipStream_t s, LaunchDz&& launch_dz) {
+  using FH = DenseDhCfg;
+  using FW = DenseDwCfg;
+  int* idx = reinterpret_cast<int*>(ws + w.idx_off);
+  int* count = reinterpret_cast<int*>(ws + w.count_off);
+  const int64_t tr = sh.tile_rows < sh.T ? sh.tile_rows : sh.T;
+  const int64_t tpad = static_cast<int64_t>(align_up(static_cast<size_t>(tr), 64));
+  const int64_t vpad = w.vpad;
+  const BwdBuffers bb = bwd_buffers(ws + w.dz_off, tr, sh.h, vpad);
+  // two tiles per dW launch when K of both still fits the 32-bit offsets
+  const int pair = dense_fast(vpad, tpad, sh.h, sh.ld_w, 2) ? 2 : 1;
+  hipError_t e = backward_prologue(sh, grad_hidden, idx, count, s);
+  if (e != hipSuccess) return e;
+  const int n_vb = (sh.V + bm - 1) / bm;
+  const int n_nb = static_cast<int>((tr + bn - 1) / bn);
+  int t = 0;
+  for (int64_t base = 0; base < sh.T; base += tr, ++t) {
+    const int slot = t % pair;
+    uint16_t* dz = bb.dz2 + slot * tpad * vpad;
+    if ((e = launch_dz(base, tr, tpad, vpad, n_vb, n_nb, idx, count, dz, nullptr)) != hipSuccess) return e;
+    if (grad_hidden) {
+      // dHidden[idx[r]] = dZ[r] . W : K = vpad split into kSplitK ranges, then a fixed-order sum
+      DenseGemmArgs g;
+      g.a = dz;
+      g.lda = vpad;
+      g.M = 0;
+      g.b = sh.weight;
+      g.ldb = sh.ld_w;
+      g.N = sh.h;
+      g.K = static_cast<int>(vpad);
+      g.kvalid_b = sh.V;
+      g.count = count;
+      g.tile_base = base;
+      g.tile_rows = static_cast<int>(tr);
+      g.tpad = tpad;
+      g.ntiles = 1;
+      g.m_from_count = 1;
+      g.k_from_count = 0;
+      g.splits = kSplitK;
+      g.ksplit = static_cast<int>(align_up(static_cast<size_t>((vpad + kSplitK - 1) / kSplitK), 64));
+      g.out = bb.hpart;
+      g.ldo = sh.h;
+      g.accumulate = 0;
+      g.n_mb = static_cast<int>((tr + FH::BM - 1) / FH::BM);
+      g.n_nb = (sh.h + FH::BN - 1) / FH::BN;
+      {
+        TimedLaunch tl("k_out_gemm_dhidden", s);
+        hipLaunchKernelGGL((k_dense_gemm_dtl<FH, LP_DH_GROUP>), dim3(static_cast<unsigned>(g.n_mb) * g.n_nb * kSplitK),
+                           dim3(FH::NT), 0, s, g);
+      }
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      {
+        TimedLaunch tl("k_splitk_reduce", s);
+        const int64_t n4 = tr * sh.h / 4;
+        const unsigned blocks = static_cast<unsigned>(n4 < 65536 * 256 ? (n4 + 255) / 256 : 65536);
+        hipLaunchKernelGGL(k_splitk_reduce, dim3(blocks), dim3(256), 0, s, bb.hpart, kSplitK, static_cast<int>(tr),
+                           sh.h, static_cast<const int*>(idx), static_cast<const int*>(count), base, grad_hidden);
+      }
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (grad_weight) {
+      {
+        TimedLaunch tl("k_gather_rows", s);
+        const unsigned blocks = static_cast<unsigned>(tpad < 65536 ? tpad : 65536);
+        hipLaunchKernelGGL(k_gather_rows_bf16, dim3(blocks), dim3(256), 0, s, sh.hidden, sh.ld_h,
+                           static_cast<const int*>(idx), static_cast<const int*>(count), base, static_cast<int>(tr),
+                           static_cast<int>(tpad), sh.h, bb.ht2 + slot * tpad * sh.h);
+      }
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      if (slot == pair - 1 || base + tr >= sh.T) {
+        // dW (+)= dZ^T . H over the rows of this launch's tiles
+        const int64_t base0 = base - slot * tr;
+        DenseGemmArgs g;
+        g.a = bb.dz2;
+        g.lda = vpad;
+        g.M = sh.V;
+        g.b = bb.ht2;
+        g.ldb = sh.h;
+        g.N = sh.h;
+        g.K = 0;
+        g.kvalid_b = 0x7fffffff;
+        g.count = count;
+        g.tile_base = base0;
+        g.tile_rows = static_cast<int>(tr);
+        g.tpad = tpad;
+        g.ntiles = slot + 1;
+        g.m_from_count = 0;
+        g.k_from_count = 1;
+        g.splits = 1;
+        g.ksplit = static_cast<int>(pair * tpad);
+        g.out = grad_weight;
+        g.ldo = sh.h;
+        g.accumulate = base0 == 0 ? 0 : 1;
+        g.n_mb = (sh.V + FW::BM - 1) / FW::BM;
+        g.n_nb = (sh.h + FW::BN - 1) / FW::BN;
+        {
+          TimedLaunch tl("k_out_gemm_dweight", s);
+          hipLaunchKernelGGL((k_dense_gemm_dtl<FW, LP_DW_GROUP>), dim3(static_cast<unsigned>(g.n_mb) * g.n_nb), dim3(FW::NT), 0, s,
+                             g);
+        }
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+      }
+    }
+  }
+  return hipSuccess;
+}
+
+template <class LaunchDz>
+hipError_t backward_tiles(const LMHeadShape& sh, bool fast, int bm_fast, int bn_fast, float* grad_hidden,
+                          float* grad_weight, char* ws, const LMHeadWorkspace& w, hipStream_t s,
+                          LaunchDz&& launch_dz) {
+  if (fast) return backward_tiles_fast(sh, bm_fast, bn_fast, grad_hidden, grad_weight, ws, w, s, launch_dz);
+  return backward_tiles_generic(sh, grad_hidden, grad_weight, ws, w, s, launch_dz);
 }
 
 

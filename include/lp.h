@@ -108,11 +108,15 @@ size_t lp_lm_head_workspace_bytes(int64_t T, int64_t h, int64_t V, int64_t tile_
  * with 32-bit per-lane byte offsets, so they also need
  *   (T x ld_h + h) x 2 < 2^32        (any hidden row may be gathered),
  *   (256 x ld_w + h) x 2 < 2^32      (one 256-row weight block),
- * and for the backward (backward != 0), with vpad = V rounded up to 64 and
- * tpad = min(tile_rows, T) rounded up to 64,
- *   (256 x vpad + vpad) x 2 < 2^32,  (256 x tpad + tpad) x 2 < 2^32
- * (blocks of the dZ, dZ^T, W^T and hidden-tile^T buffers of the gradient
- * GEMMs).  Shapes outside these run on the generic tiles, which use 64-bit
+ * and for the backward (backward != 0), with vpad = V rounded up to 64,
+ * tpad = min(tile_rows, T) rounded up to 64 and ks = vpad / 4 rounded up to 64,
+ *   (256 x vpad + vpad) x 2 < 2^32     (256-row blocks of the dZ buffer),
+ *   (ks x ld_w + 256) x 2 < 2^32       (the weight rows of one K range of the
+ *                                       hidden-gradient GEMM),
+ *   (tpad x vpad + 256) x 2 < 2^32, (tpad x h + 256) x 2 < 2^32
+ *                                      (dZ and the tile's hidden rows as the
+ *                                       weight-gradient GEMM's operands).
+ * Shapes outside these run on the generic tiles, which use 64-bit
  * addressing; results are the same up to summation order.  The backward also
  * takes the generic tiles when grad_hidden is not 16-byte aligned.  The KL
  * through the heads uses the fast tiles when both heads qualify.
