@@ -134,7 +134,7 @@ def _events_ms(torch, fn, steps):
 SETTLE_SECONDS = 2.0  # set from --settle-seconds in main()
 
 
-def _timed(lp, torch, fn, steps, warmup, kernels):
+def _timed(lp, torch, fn, steps, warmup, kernels, clocks=False):
     # Clock settle: the GPU idles while a path's inputs are generated on the
     # host, and it needs some time under load to reach its steady clocks.  Run
     # the step untimed for SETTLE_SECONDS first, then the W warm-up steps,
@@ -146,9 +146,11 @@ def _timed(lp, torch, fn, steps, warmup, kernels):
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    lp.lp_timing_enable(True)
+    lp.lp_timing_enable(2 if clocks else True)
     ms = _events_ms(torch, fn, steps)
     per_kernel = {k: lp.lp_timing_read(k) for k in kernels}
+    if clocks:
+        per_kernel["_clock"] = lp.lp_timing_clock("k_fwd_tile")
     lp.lp_timing_enable(False)
     return ms, per_kernel
 
@@ -247,7 +249,8 @@ def bench_lm_head_fwd(lp, torch, np, synth, steps, warmup, cpu_seconds, cfg=None
     def step():
         out["r"] = lp.lp_lm_head_logprobs_entropy(hid, W, y, m, cfg.temperature, cfg.tile_rows, workspace=ws)
 
-    ms, kt = _timed(lp, torch, step, steps, warmup, ["k_fwd_tile", "k_fwd_merge", "k_compact"])
+    ms, kt = _timed(lp, torch, step, steps, warmup, ["k_fwd_tile", "k_fwd_merge", "k_compact"], clocks=not tiny)
+    sclk, sclk_n = kt.pop("_clock", (None, 0))
     flop_step = 2.0 * Ts * cfg.V * cfg.h
     n_launch, gemm_ms = kt["k_fwd_tile"]
     n_tiles = (Ts + cfg.tile_rows - 1) // cfg.tile_rows
@@ -275,7 +278,11 @@ def bench_lm_head_fwd(lp, torch, np, synth, steps, warmup, cpu_seconds, cfg=None
             traffic_unit="HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             algorithmic_hbm_bytes_per_launch=(n_tiles * cfg.V * cfg.h * 2 + Ts * cfg.h * 2) / (n_launch / steps),
             launches_per_step=n_launch / steps, kernel_ms_per_step=gemm_ms / steps,
-            algorithmic_flop_per_step=flop_step, algorithmic_flop_per_launch=flop_step / (n_launch / steps))
+            algorithmic_flop_per_step=flop_step, algorithmic_flop_per_launch=flop_step / (n_launch / steps),
+            # the shader clock the kernel's workgroups ran at (last timed launch), and the fraction of the
+            # datasheet rate scaled to that clock (the datasheet figure assumes 2.4 GHz)
+            sclk_mhz_during_kernel=sclk or None, sclk_samples=sclk_n,
+            frac_at_observed_clock=(achieved / (BF16_PEAK_TFLOPS * sclk / 2400.0)) if sclk else None)
     res["memory"] = _memory_audit(
         torch, lambda: lp.lp_lm_head_logprobs_entropy(hid, W, y, m, cfg.temperature, cfg.tile_rows),
         ws_bytes, 3 * 4 * cfg.T, 4 * cfg.T * cfg.V)

@@ -19,7 +19,7 @@ from ._lib import LP_BF16, LP_FP16, LP_FP32, LPError, check, load
 __all__ = [
     "lp_logprobs_entropy", "lp_lm_head_logprobs_entropy", "lp_lm_head_logprobs_entropy_backward",
     "lp_lm_head_workspace_bytes", "lp_kl_full_vocab", "lp_prob_diff", "lp_version", "lp_timing_enable",
-    "lp_timing_read", "lp_logprobs_entropy_k", "lp_lm_head_logprobs_entropy_k",
+    "lp_timing_read", "lp_timing_clock", "lp_logprobs_entropy_k", "lp_lm_head_logprobs_entropy_k",
     "lp_lm_head_logprobs_entropy_backward_k", "lp_prob_diff_stats", "lp_lm_head_kl_workspace_bytes",
     "lp_lm_head_kl", "lp_lm_head_kl_backward", "LPError", "load",
 ]
@@ -106,9 +106,19 @@ def lp_version() -> int:
     return load().lp_version()
 
 
-def lp_timing_enable(on: bool) -> None:
-    """Start (clearing old records) or stop per-kernel HIP-event timing."""
-    load().lp_timing_enable(1 if on else 0)
+def lp_timing_enable(on) -> None:
+    """Start (clearing old records) or stop per-kernel HIP-event timing; 2 also
+    samples the fused forward GEMM's shader clock (lp_timing_clock)."""
+    load().lp_timing_enable(2 if on == 2 else (1 if on else 0))
+
+
+def lp_timing_clock(kernel: str = "k_fwd_tile"):
+    """(mean shader clock in MHz, workgroups sampled) of the last sampled launch."""
+    import ctypes
+    mhz = ctypes.c_double(0.0)
+    n = ctypes.c_int64(0)
+    check("lp_timing_clock", load().lp_timing_clock(kernel.encode(), ctypes.byref(mhz), ctypes.byref(n)))
+    return float(mhz.value), int(n.value)
 
 
 def lp_timing_read(kernel: str):

@@ -52,6 +52,7 @@ SIGNATURES = {
                                        c_vp]),
     "lp_timing_enable": (None, [c_int]),
     "lp_timing_read": (c_int, [ctypes.c_char_p, ctypes.POINTER(c_i64), ctypes.POINTER(ctypes.c_double)]),
+    "lp_timing_clock": (c_int, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_i64)]),
 }
 
 LP_OK, LP_ERR_INVALID_ARGUMENT, LP_ERR_UNSUPPORTED, LP_ERR_WORKSPACE_TOO_SMALL, LP_ERR_HIP = range(5)

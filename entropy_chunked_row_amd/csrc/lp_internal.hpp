@@ -26,6 +26,16 @@ class TimedLaunch {
   hipEvent_t a_;
 };
 
+// True while lp_timing_enable(2) is in force: the fast forward GEMM then also
+// records, per workgroup, the shader-clock and fixed-frequency counter deltas
+// of its run (read back by lp_timing_clock).
+bool timing_clocks_on();
+
+// Copies the per-workgroup clock samples of the last fast forward launch made
+// while timing_clocks_on(): pairs (shader-clock delta, fixed-clock delta) for
+// its first *n workgroups (*n = at most the samples held; 0 if none).
+hipError_t read_fwd_clocks(unsigned long long* pairs, int64_t* n);
+
 // Logits-input rows [row0, row0 + rows) of a [T x ld] matrix.
 struct RowArgs {
   const void* x;

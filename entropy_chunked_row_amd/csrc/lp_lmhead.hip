@@ -395,6 +395,7 @@ struct FwdArgs {
   int n_vb, n_nb;     // vocab blocks, row blocks of the launch
   float* part;        // [tile_rows][n_vb][3]
   float* zy;          // [tile_rows][K]
+  int clocks;         // record per-workgroup clock samples (timing mode 2)
 };
 
 // Block -> (vocab block, row block) of a launch.  The fast forward blocks the
@@ -548,19 +549,51 @@ __global__ void __launch_bounds__(C::NT) k_fwd_tile(FwdArgs a) {
   fwd_epilogue<C>(a, acc, vb, n0, rows, lds);
 }
 
+// Clock samples of the fast forward (timing mode 2, observability only): for
+// workgroup b < kClockSamples of the last such launch, the deltas of the
+// shader-clock counter and of the fixed-frequency counter over its run.
+constexpr int kClockSamples = 65536;
+__device__ unsigned long long g_fwd_clocks[2 * kClockSamples];
+int64_t g_fwd_clock_blocks = 0;  // workgroups of the last sampled launch (host)
+
+hipError_t read_fwd_clocks(unsigned long long* pairs, int64_t* n) {
+  const int64_t m = g_fwd_clock_blocks < kClockSamples ? g_fwd_clock_blocks : kClockSamples;
+  if (*n > m) *n = m;
+  if (*n <= 0) {
+    *n = 0;
+    return hipSuccess;
+  }
+  return hipMemcpyFromSymbol(pairs, HIP_SYMBOL(g_fwd_clocks), sizeof(unsigned long long) * 2 * (*n));
+}
+
 // Fast forward tile (h % 64 == 0): direct-to-LDS loads, 256 (vocab) x 320
 // (rows) block.
 template <class C>
 __global__ void __launch_bounds__(C::NT, LP_FWD_MIN_WAVES) k_fwd_tile_dtl(FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t lds[C::LDS_ELEMS];
+  // clock samples: the start values go to memory and are read back at the
+  // end (volatile), so nothing stays live in registers across the K loop
+  volatile unsigned long long* clk = g_fwd_clocks + 2 * blockIdx.x;
+  const bool sample = a.clocks && threadIdx.x == 0 && blockIdx.x < kClockSamples;
+  if (sample) {
+    clk[0] = __builtin_amdgcn_s_memtime();
+    clk[1] = __builtin_amdgcn_s_memrealtime();
+  }
   int vb, nb, rows;
-  if (!fwd_block<C::BN>(a, vb, nb, rows)) return;
+  if (!fwd_block<C::BN>(a, vb, nb, rows)) {
+    if (sample) clk[1] = 0;  // no work: a zero fixed-clock delta, skipped by the reader
+    return;
+  }
   const int n0 = nb * C::BN;
   const int v0 = vb * C::BM;
   f32x16_t acc[C::MI][C::NI];
   gemm_tile_dtl<C>(a.weight + static_cast<int64_t>(v0) * a.ld_w, a.ld_w, a.V - v0, a.hidden, a.ld_h,
-                     a.idx + a.tile_base + n0, rows - n0, a.h, lds, acc);
+                   a.idx + a.tile_base + n0, rows - n0, a.h, lds, acc);
   fwd_epilogue<C>(a, acc, vb, n0, rows, lds);
+  if (sample) {
+    clk[0] = __builtin_amdgcn_s_memtime() - clk[0];
+    clk[1] = __builtin_amdgcn_s_memrealtime() - clk[1];
+  }
 }
 
 struct MergeArgs {
@@ -650,6 +683,8 @@ hipError_t launch_lmhead_forward(const LMHeadShape& sh, float* logprob, float* e
     a.n_nb = n_nb;
     a.part = part;
     a.zy = zy;
+    a.clocks = fast && timing_clocks_on() ? 1 : 0;
+    if (a.clocks) g_fwd_clock_blocks = grid_blocks;
     {
       TimedLaunch tl("k_fwd_tile", s);
       const dim3 grid(static_cast<unsigned>(grid_blocks));

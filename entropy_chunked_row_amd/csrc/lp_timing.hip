@@ -22,6 +22,7 @@ struct Rec {
 
 std::mutex g_mu;
 bool g_on = false;
+bool g_clocks = false;
 std::vector<Rec> g_recs;
 std::vector<hipEvent_t> g_pool;
 
@@ -60,6 +61,11 @@ TimedLaunch::~TimedLaunch() {
   }
 }
 
+bool timing_clocks_on() {
+  std::lock_guard<std::mutex> lk(g_mu);
+  return g_clocks;
+}
+
 }  // namespace lp
 
 extern "C" {
@@ -67,6 +73,7 @@ extern "C" {
 void lp_timing_enable(int on) {
   std::lock_guard<std::mutex> lk(lp::g_mu);
   lp::g_on = on != 0;
+  lp::g_clocks = on == 2;
   for (auto& r : lp::g_recs) {
     lp::g_pool.push_back(r.a);
     lp::g_pool.push_back(r.b);
@@ -93,3 +100,29 @@ lp_status lp_timing_read(const char* kernel, int64_t* launches, double* total_ms
 }
 
 }  // extern "C"
+
+extern "C" lp_status lp_timing_clock(const char* kernel, double* mhz, int64_t* samples) {
+  if (!kernel || !mhz || !samples) return LP_ERR_INVALID_ARGUMENT;
+  if (strcmp(kernel, "k_fwd_tile") != 0) return LP_ERR_UNSUPPORTED;
+  *mhz = 0.0;
+  *samples = 0;
+  if (hipDeviceSynchronize() != hipSuccess) return LP_ERR_HIP;
+  int dev = 0, wall_khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&wall_khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || wall_khz <= 0)
+    return LP_ERR_HIP;
+  std::vector<unsigned long long> pairs(2 * 65536);
+  int64_t n = static_cast<int64_t>(pairs.size() / 2);
+  if (lp::read_fwd_clocks(pairs.data(), &n) != hipSuccess) return LP_ERR_HIP;
+  double sum = 0.0;
+  int64_t used = 0;
+  for (int64_t b = 0; b < n; ++b) {
+    const unsigned long long dt = pairs[2 * b], dr = pairs[2 * b + 1];
+    if (dr == 0) continue;
+    sum += static_cast<double>(dt) / static_cast<double>(dr);
+    ++used;
+  }
+  if (used) *mhz = sum / static_cast<double>(used) * wall_khz / 1e3;
+  *samples = used;
+  return LP_OK;
+}

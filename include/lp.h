@@ -343,6 +343,18 @@ lp_status lp_prob_diff_stats(const float* lp_a, const float* lp_b, const uint8_t
 void lp_timing_enable(int on);
 lp_status lp_timing_read(const char* kernel, int64_t* launches, double* total_ms);
 
+/*
+ * With lp_timing_enable(2) (timing plus clock samples), every workgroup of the
+ * fused forward's MFMA kernel on the direct-to-LDS tiles also records the
+ * deltas of the shader-clock counter and of the fixed-frequency counter over
+ * its run (a static device array of 65536 sample pairs, overwritten by each
+ * launch).  lp_timing_clock("k_fwd_tile", &mhz, &samples) waits for the
+ * device and returns the mean shader clock (MHz) over the workgroups of the
+ * last such launch that had work, and their number (0 if none).  Other
+ * kernel names: LP_ERR_UNSUPPORTED.
+ */
+lp_status lp_timing_clock(const char* kernel, double* mhz, int64_t* samples);
+
 #ifdef __cplusplus
 }
 #endif
