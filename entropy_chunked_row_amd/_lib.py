@@ -1,6 +1,7 @@
 """ctypes view of liblp.so: symbol loading and C signatures only.
 
-Loading the library does not touch the GPU.  There is no fallback: if the
+Loading the library does not touch the GPU (it imports torch first, whose HIP
+runtime liblp.so then binds to).  There is no fallback: if the
 library is missing the caller gets an error telling it to build.
 """
 from __future__ import annotations
@@ -74,6 +75,14 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with `python -m entropy_chunked_row_amd.build` "
                            "(there is no CPU fallback)")
+    # PyTorch ships its own HIP runtime.  Loaded first, it is the runtime
+    # liblp.so binds to (same soname); loaded after liblp.so, a second copy of
+    # the runtime would come up beside the one liblp.so brought in, and one of
+    # the two then sees no device.
+    try:
+        import torch  # noqa: F401
+    except ImportError:  # pragma: no cover - the binding needs torch for tensors anyway
+        pass
     lib = ctypes.CDLL(path)
     for name, (res, args) in SIGNATURES.items():
         f = getattr(lib, name)

@@ -32,6 +32,11 @@ lp_status hip_fail(hipError_t e, const char* where) {
   return fail(LP_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
 }
 
+// The launchers read hipGetLastError() after each launch; an error left
+// pending on this thread by an earlier, unrelated runtime call (the caller's
+// or another library's) would be reported as ours.  Clear it first.
+void clear_pending_hip_error() { (void)hipGetLastError(); }
+
 constexpr double kLog2eD = 1.44269504088896340736;
 constexpr int64_t kMaxV = (int64_t(1) << 30);
 
@@ -141,6 +146,7 @@ static lp_status logprobs_entropy_impl(const void* logits, lp_dtype dtype, int64
   a.entropy = entropy;
   a.row0 = 0;
   a.rows = T;
+  clear_pending_hip_error();
   hipError_t e = lp::launch_logprobs_entropy(static_cast<int>(dtype), a, s);
   if (e != hipSuccess) return hip_fail(e, "lp_logprobs_entropy launch");
   return ok();
@@ -237,6 +243,7 @@ static lp_status lm_head_forward_impl(const char* fn, const void* hidden, int64_
   if (!logprob) return fail(LP_ERR_INVALID_ARGUMENT, "%s: logprob is required", fn);
   if (!f32_aligned({logprob, entropy, lse})) return fail(LP_ERR_INVALID_ARGUMENT, "%s: misaligned fp32 output", fn);
   lp::LMHeadShape sh = make_shape(hidden, ld_h, weight, ld_w, T, h, V, targets, K, mask, temperature, tile_rows);
+  clear_pending_hip_error();
   hipError_t e = lp::launch_lmhead_forward(sh, logprob, entropy, lse, static_cast<char*>(workspace), w,
                                            static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, fn);
@@ -292,6 +299,7 @@ lp_status lp_lm_head_logprobs_entropy_noalloc(const void* hidden, int64_t ld_h, 
                   static_cast<int>(sd), device);
   }
   lp::LMHeadShape sh = make_shape(hidden, ld_h, weight, ld_w, T, h, V, targets, 1, mask, temperature, tile_rows);
+  clear_pending_hip_error();
   e = lp::launch_lmhead_forward(sh, logprob, entropy, lse, static_cast<char*>(ws), w, s);
   if (e != hipSuccess) return hip_fail(e, fn);
   return ok();
@@ -314,6 +322,7 @@ static lp_status lm_head_backward_impl(const char* fn, const void* hidden, int64
   if (T == 0) {
     // no rows: the weight gradient is still defined (all zero)
     if (grad_weight) {
+      clear_pending_hip_error();
       hipError_t e = lp::launch_zero_f32(grad_weight, V * h, s);
       if (e != hipSuccess) return hip_fail(e, fn);
     }
@@ -322,6 +331,7 @@ static lp_status lm_head_backward_impl(const char* fn, const void* hidden, int64
   if (!lse || !entropy || !grad_logprob)
     return fail(LP_ERR_INVALID_ARGUMENT, "%s: lse, entropy and grad_logprob are required", fn);
   lp::LMHeadShape sh = make_shape(hidden, ld_h, weight, ld_w, T, h, V, targets, K, mask, temperature, tile_rows);
+  clear_pending_hip_error();
   hipError_t e = lp::launch_lmhead_backward(sh, lse, entropy, grad_logprob, grad_entropy, grad_hidden,
                                             grad_weight, static_cast<char*>(workspace), w, s);
   if (e != hipSuccess) return hip_fail(e, fn);
@@ -419,6 +429,7 @@ lp_status lp_lm_head_kl(const void* student_hidden, int64_t ld_hs, const void* s
   const lp::LMHeadShape te = make_shape(teacher_hidden, ld_ht, teacher_weight, ld_wt, T, h_teacher, V, targets, 1,
                                         mask, 1.0f, tile_rows);
   const lp::KLHeadOutputs out{kl, lp_student, lp_teacher, prob_diff, lse_student, lse_teacher};
+  clear_pending_hip_error();
   hipError_t e = lp::launch_lmhead_kl_forward(su, te, targets, diff_mask, out, static_cast<char*>(workspace), w,
                                               static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, fn);
@@ -441,6 +452,7 @@ lp_status lp_lm_head_kl_backward(const void* student_hidden, int64_t ld_hs, cons
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (T == 0) {
     if (grad_weight) {
+      clear_pending_hip_error();
       hipError_t e = lp::launch_zero_f32(grad_weight, V * h_student, s);
       if (e != hipSuccess) return hip_fail(e, fn);
     }
@@ -452,6 +464,7 @@ lp_status lp_lm_head_kl_backward(const void* student_hidden, int64_t ld_hs, cons
                                         mask, 1.0f, tile_rows);
   const lp::LMHeadShape te = make_shape(teacher_hidden, ld_ht, teacher_weight, ld_wt, T, h_teacher, V, nullptr, 1,
                                         mask, 1.0f, tile_rows);
+  clear_pending_hip_error();
   hipError_t e = lp::launch_lmhead_kl_backward(su, te, lse_student, lse_teacher, grad_kl, grad_hidden, grad_weight,
                                                static_cast<char*>(workspace), w, s);
   if (e != hipSuccess) return hip_fail(e, fn);
@@ -491,6 +504,7 @@ lp_status lp_kl_full_vocab(const void* student, const void* teacher, lp_dtype dt
   a.lp_student = lp_student;
   a.lp_teacher = lp_teacher;
   a.prob_diff = prob_diff;
+  clear_pending_hip_error();
   hipError_t e = lp::launch_kl_full_vocab(static_cast<int>(dtype), a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, fn);
   return ok();
@@ -502,6 +516,7 @@ lp_status lp_prob_diff(const float* lp_a, const float* lp_b, const uint8_t* mask
   if (n == 0) return ok();
   if (!lp_a || !lp_b || !out) return fail(LP_ERR_INVALID_ARGUMENT, "lp_prob_diff: lp_a, lp_b, out required");
   if (!f32_aligned({lp_a, lp_b, out})) return fail(LP_ERR_INVALID_ARGUMENT, "lp_prob_diff: misaligned pointer");
+  clear_pending_hip_error();
   hipError_t e = lp::launch_prob_diff(lp_a, lp_b, mask, n, out, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "lp_prob_diff");
   return ok();
@@ -520,6 +535,7 @@ lp_status lp_prob_diff_stats(const float* lp_a, const float* lp_b, const uint8_t
     return fail(LP_ERR_WORKSPACE_TOO_SMALL, "%s: workspace needs %zu bytes", fn, lp::prob_diff_stats_workspace_bytes());
   if (!aligned(workspace, 256) || !aligned(out, 8))
     return fail(LP_ERR_INVALID_ARGUMENT, "%s: misaligned workspace or out", fn);
+  clear_pending_hip_error();
   hipError_t e = lp::launch_prob_diff_stats(lp_a, lp_b, mask, n, out, workspace, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, fn);
   return ok();

@@ -186,6 +186,13 @@ def test_kl_head_full_size_sampled():
     scale = dW.double().abs().sum(0)
     assert torch.isfinite(dW).all().item()
     assert (colsum.abs() <= 1e-2 * scale).all().item()
+    # dW summed over 4 tiles of 4096 against 8 tiles of 2048 (and 2 against 4 dW launches): a tile dropped,
+    # doubled or paired with the wrong hidden rows would differ by far more than the summation order does
+    _, dW2 = _lp().lp_lm_head_kl_backward(*heads, None, 2048, out[4], out[5], g_kl, need_grad_hidden=False)
+    diff = (dW - dW2).double()
+    rel_fro = (diff.norm() / dW2.double().norm()).item()
+    rel_max = (diff.abs().max() / dW2.double().abs().max()).item()
+    assert rel_fro <= TOL_GRAD and rel_max <= TOL_GRAD, (rel_fro, rel_max)
 
 
 def test_kl_head_matches_kl_on_fp32_logits():

@@ -203,6 +203,26 @@ def test_backward_fast_path_shapes(T, h, V, tile, tau):
     assert not dH[m == 0].any()
 
 
+def test_backward_odd_tile_count_single_last_pair():
+    """The fast backward multiplies dW once per pair of tiles; with three
+    scored tiles the last dW launch holds one tile (188 rows), and with a
+    ragged vocabulary (V % 64 != 0) the hidden gradient's weight rows past V
+    are clamped.  Every element against the oracle."""
+    T, h, V, tile, tau = 700, 128, 2021, 256, 0.8
+    hid, W, y, m = _case(T, h, V, seed=700, scored=1.0)
+    assert _lp().load().lp_lm_head_fast_tiles(T, h, V, h, h, tile, 1) == 1
+    rng = np.random.default_rng(701)
+    g = rng.normal(0, 1, size=T).astype(np.float32)
+    gH = rng.normal(0, 0.1, size=T).astype(np.float32)
+    lp, H, lse = _run_fwd(hid, W, y, m, tau, tile)
+    dH, dW = _lp().lp_lm_head_logprobs_entropy_backward(to_dev_bits(hid, "bf16"), to_dev_bits(W, "bf16"), to_dev(y),
+                                                        to_dev(m), tau, tile, lse, H, to_dev(g), to_dev(gH))
+    dH_o, dW_o = O.lm_head_backward(O.widen_bf16(hid), O.widen_bf16(W), y, m, tau, g, gH)
+    for nm, got, want in (("dH", host(dH), dH_o), ("dW", host(dW), dW_o)):
+        fro, mad = grad_errors(got, want)
+        assert fro <= TOL_GRAD and mad <= TOL_GRAD, (nm, fro, mad)
+
+
 class _LazyW:
     def __init__(self, bits):
         self.bits, self.shape = bits, bits.shape
