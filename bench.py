@@ -15,7 +15,11 @@ on the host cores over a bounded sample of the same workload (and compared
 with the GPU's outputs on those rows), and the device memory one call
 allocates.  Each path runs its step untimed for --settle-seconds (steady GPU
 clocks after the host-side input generation), then W warm-up steps, then
-exactly K timed steps.
+exactly K timed steps.  The board power (amdgpu hwmon, sampled on a host
+thread) is recorded over each timed region; the forward also records the
+shader clock its workgroups ran at and repeats its launch on all-zero
+operands, which shows how much of the gap to the datasheet rate is the power
+limit rather than the kernel.
 
 Inputs are seeded and synthetic (see synth/).  The fp64 oracle is used only in
 the CPU-baseline legs; every path's parity at full size is in tests/.
@@ -134,6 +138,59 @@ def _events_ms(torch, fn, steps):
 SETTLE_SECONDS = 2.0  # set from --settle-seconds in main()
 
 
+def _hwmon_dir():
+    """The amdgpu hwmon directory of the one visible GPU (board power in
+    microwatts: power1_input, cap power1_cap), or None where sysfs shows none
+    or several."""
+    import glob
+    found = sorted(d for d in glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*")
+                   if os.path.exists(os.path.join(d, "power1_input")))
+    return found[0] if len(found) == 1 else None
+
+
+class _PowerSampler:
+    """Samples the board power every 10 ms on a host thread while a timed
+    region runs (reads sysfs only; nothing on the GPU)."""
+
+    def __init__(self):
+        self.dir = _hwmon_dir()
+        self.samples = []
+
+    def _read(self, name):
+        try:
+            with open(os.path.join(self.dir, name)) as f:
+                return int(f.read()) / 1e6
+        except (OSError, ValueError, TypeError):
+            return None
+
+    def __enter__(self):
+        import threading
+        self._stop = threading.Event()
+
+        def run():
+            while not self._stop.is_set():
+                w = self._read("power1_input")
+                if w is not None:
+                    self.samples.append(w)
+                self._stop.wait(0.01)
+
+        self._t = threading.Thread(target=run, daemon=True)
+        if self.dir:
+            self._t.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self.dir:
+            self._t.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        return dict(mean_w=sum(self.samples) / len(self.samples), max_w=max(self.samples),
+                    samples=len(self.samples), cap_w=self._read("power1_cap"))
+
+
 def _timed(lp, torch, fn, steps, warmup, kernels, clocks=False):
     # Clock settle: the GPU idles while a path's inputs are generated on the
     # host, and it needs some time under load to reach its steady clocks.  Run
@@ -147,8 +204,10 @@ def _timed(lp, torch, fn, steps, warmup, kernels, clocks=False):
         fn()
     torch.cuda.synchronize()
     lp.lp_timing_enable(2 if clocks else True)
-    ms = _events_ms(torch, fn, steps)
+    with _PowerSampler() as pw:
+        ms = _events_ms(torch, fn, steps)
     per_kernel = {k: lp.lp_timing_read(k) for k in kernels}
+    per_kernel["_power"] = pw.summary()
     if clocks:
         per_kernel["_clock"] = lp.lp_timing_clock("k_fwd_tile")
     lp.lp_timing_enable(False)
@@ -251,6 +310,7 @@ def bench_lm_head_fwd(lp, torch, np, synth, steps, warmup, cpu_seconds, cfg=None
 
     ms, kt = _timed(lp, torch, step, steps, warmup, ["k_fwd_tile", "k_fwd_merge", "k_compact"], clocks=not tiny)
     sclk, sclk_n = kt.pop("_clock", (None, 0))
+    power = kt.pop("_power", None)
     flop_step = 2.0 * Ts * cfg.V * cfg.h
     n_launch, gemm_ms = kt["k_fwd_tile"]
     n_tiles = (Ts + cfg.tile_rows - 1) // cfg.tile_rows
@@ -282,7 +342,9 @@ def bench_lm_head_fwd(lp, torch, np, synth, steps, warmup, cpu_seconds, cfg=None
             # the shader clock the kernel's workgroups ran at (last timed launch), and the fraction of the
             # datasheet rate scaled to that clock (the datasheet figure assumes 2.4 GHz)
             sclk_mhz_during_kernel=sclk or None, sclk_samples=sclk_n,
-            frac_at_observed_clock=(achieved / (BF16_PEAK_TFLOPS * sclk / 2400.0)) if sclk else None)
+            frac_at_observed_clock=(achieved / (BF16_PEAK_TFLOPS * sclk / 2400.0)) if sclk else None,
+            board_power_during_timed_steps=power,
+            same_launch_on_zero_operands=_zero_operand_run(lp, torch, cfg, y, m, ws, flop_step))
     res["memory"] = _memory_audit(
         torch, lambda: lp.lp_lm_head_logprobs_entropy(hid, W, y, m, cfg.temperature, cfg.tile_rows),
         ws_bytes, 3 * 4 * cfg.T, 4 * cfg.T * cfg.V)
@@ -306,6 +368,27 @@ def bench_lm_head_fwd(lp, torch, np, synth, steps, warmup, cpu_seconds, cfg=None
     return res
 
 
+def _zero_operand_run(lp, torch, cfg, y, m, ws, flop_step, steps=3):
+    """The same forward launch on all-zero hidden rows and weights: identical
+    instructions, loads and LDS traffic, but matrix-core inputs that never
+    toggle.  Its clock and board power, next to the timed run's, show how far
+    the timed run's clock is set by the board's power limit (context only; the
+    reported throughput is the timed run on the seeded operands)."""
+    hid0 = torch.zeros((cfg.T, cfg.h), dtype=torch.bfloat16, device="cuda")
+    W0 = torch.zeros((cfg.V, cfg.h), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        lp.lp_lm_head_logprobs_entropy(hid0, W0, y, m, cfg.temperature, cfg.tile_rows, workspace=ws)
+
+    ms, kt = _timed(lp, torch, step, steps, 1, ["k_fwd_tile"], clocks=True)
+    sclk, n = kt["_clock"]
+    gemm_ms = kt["k_fwd_tile"][1]
+    del hid0, W0
+    achieved = flop_step * steps / (gemm_ms * 1e-3) / 1e12
+    return dict(kernel_ms_per_step=gemm_ms / steps, achieved_tflops=achieved, frac=achieved / BF16_PEAK_TFLOPS,
+                sclk_mhz_during_kernel=sclk or None, board_power=kt["_power"])
+
+
 def bench_tiny_lm_head(lp, torch, np, synth, steps, warmup, cpu_seconds):
     """T=64, h=256, V=1024, tile 16: launch-bound, reported in microseconds."""
     return bench_lm_head_fwd(lp, torch, np, synth, max(steps, 100), max(warmup, 10), cpu_seconds,
@@ -324,6 +407,7 @@ def bench_logits_input(lp, torch, np, synth, steps, warmup, cpu_seconds):
         lp.lp_logprobs_entropy(x, y, m, cfg.temperature, cfg.chunk_rows, logprob=lpo, entropy=Ho)
 
     ms, kt = _timed(lp, torch, step, steps, warmup, ["k_logprobs_entropy"])
+    power = kt.pop("_power")
     n_launch, kms = kt["k_logprobs_entropy"]
     bytes_step = Ts * (2 * cfg.V + 8 + 8) + cfg.T * 1 + (cfg.T - Ts) * 8
     achieved = bytes_step * steps / (kms * 1e-3) / 1e9
@@ -336,7 +420,8 @@ def bench_logits_input(lp, torch, np, synth, steps, warmup, cpu_seconds):
                       frac=achieved / HBM_PEAK_GBS, traffic=measured_traffic("k_logprobs_entropy"),
                       traffic_unit="HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                       algorithmic_bytes_per_launch=bytes_step / (n_launch / steps),
-                      launches_per_step=n_launch / steps, algorithmic_bytes_per_step=bytes_step))
+                      launches_per_step=n_launch / steps, algorithmic_bytes_per_step=bytes_step,
+                      board_power_during_timed_steps=power))
     res["memory"] = _memory_audit(torch, lambda: lp.lp_logprobs_entropy(x, y, m, cfg.temperature, cfg.chunk_rows),
                                   0, 2 * 4 * cfg.T, 4 * cfg.T * cfg.V)
     if cpu_seconds > 0:
@@ -367,6 +452,7 @@ def bench_kl(lp, torch, np, synth, steps, warmup, cpu_seconds):
         out["r"] = lp.lp_kl_full_vocab(u, v, y, dm)
 
     ms, kt = _timed(lp, torch, step, steps, warmup, ["k_kl_full_vocab"])
+    power = kt.pop("_power")
     n_launch, kms = kt["k_kl_full_vocab"]
     bytes_step = cfg.T * (2 * 2 * cfg.V + 8 + 1 + 4 * 4)
     achieved = bytes_step * steps / (kms * 1e-3) / 1e9
@@ -378,7 +464,8 @@ def bench_kl(lp, torch, np, synth, steps, warmup, cpu_seconds):
                       frac=achieved / HBM_PEAK_GBS, traffic=measured_traffic("k_kl_full_vocab"),
                       traffic_unit="HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                       algorithmic_bytes_per_launch=bytes_step / (n_launch / steps),
-                      launches_per_step=n_launch / steps, algorithmic_bytes_per_step=bytes_step))
+                      launches_per_step=n_launch / steps, algorithmic_bytes_per_step=bytes_step,
+                      board_power_during_timed_steps=power))
     res["memory"] = _memory_audit(torch, lambda: lp.lp_kl_full_vocab(u, v, y, dm), 0, 4 * 4 * cfg.T,
                                   2 * 4 * cfg.T * cfg.V)
     if cpu_seconds > 0:
@@ -422,6 +509,7 @@ def bench_lm_head_fwd_bwd(lp, torch, np, synth, steps, warmup, cpu_seconds):
     kernels = list(gemms) + ["k_gather_rows", "k_splitk_reduce", "k_fwd_merge", "k_compact",
                              "k_zero_unscored_rows", "k_transpose_bf16"]
     ms, kt = _timed(lp, torch, step, steps, warmup, kernels)
+    power = kt.pop("_power")
     flop_step = 8.0 * Ts * cfg.V * cfg.h
     mfma_ms = sum(kt[k][1] for k in gemms)
     achieved = flop_step * steps / (mfma_ms * 1e-3) / 1e12
@@ -441,7 +529,8 @@ def bench_lm_head_fwd_bwd(lp, torch, np, synth, steps, warmup, cpu_seconds):
                                    "copy-calibrated)",
                       algorithmic_flop_per_step=flop_step,
                       per_gemm_frac={k: (2.0 * Ts * cfg.V * cfg.h) * steps / (kt[k][1] * 1e-3) / 1e12
-                                     / BF16_PEAK_TFLOPS for k in gemms}),
+                                     / BF16_PEAK_TFLOPS for k in gemms},
+                      board_power_during_timed_steps=power),
         kernel_ms_per_step={k: v[1] / steps for k, v in kt.items()},
         launches_per_step={k: v[0] / steps for k, v in kt.items()})
     fwd_mem = _memory_audit(torch, lambda: lp.lp_lm_head_logprobs_entropy(hid, W, y, m, cfg.temperature,
@@ -508,6 +597,7 @@ def bench_kl_lm_head(lp, torch, np, synth, steps, warmup, cpu_seconds):
                                              workspace=wsb)
 
     ms, kt = _timed(lp, torch, fwd, steps, warmup, ["k_kl_teacher", "k_kl_student", "k_kl_merge"])
+    power = kt.pop("_power")
     n_launch, t_ms = kt["k_kl_teacher"]
     s_ms = kt["k_kl_student"][1]
     kms = t_ms + s_ms
@@ -522,6 +612,7 @@ def bench_kl_lm_head(lp, torch, np, synth, steps, warmup, cpu_seconds):
     bkernels = ["k_kl_teacher", "k_kl_student", "k_kl_dz", "k_out_gemm_dhidden", "k_out_gemm_dweight",
                 "k_gather_rows", "k_splitk_reduce", "k_transpose_bf16"]
     ms_b, kt_b = _timed(lp, torch, fwd_bwd, bsteps, min(1, warmup), bkernels)
+    power_b = kt_b.pop("_power")
     flop_fb = flop_fwd * 2 + 4.0 * cfg.T * cfg.V * cfg.h
     mfma_ms = sum(kt_b[k][1] for k in bkernels[:5])
     achieved_b = flop_fb * bsteps / (mfma_ms * 1e-3) / 1e12
@@ -538,11 +629,13 @@ def bench_kl_lm_head(lp, torch, np, synth, steps, warmup, cpu_seconds):
                       algorithmic_hbm_bytes_per_launch=pass_bytes,
                       launches_per_step=n_launch / steps, algorithmic_flop_per_step=flop_fwd,
                       algorithmic_flop_per_launch=flop_fwd / 2 / chunks,
-                      teacher_ms_per_launch=t_ms / n_launch, student_ms_per_launch=s_ms / n_launch),
+                      teacher_ms_per_launch=t_ms / n_launch, student_ms_per_launch=s_ms / n_launch,
+                      board_power_during_timed_steps=power),
         fwd_bwd=dict(ms_per_step=ms_b / bsteps, tokens_per_s=cfg.T * bsteps / (ms_b * 1e-3),
                      roofline=dict(bound="mfma", kernel="all MFMA GEMMs (2 fwd + 2 recompute + dHidden + dW)",
                                    achieved=achieved_b, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                                   frac=achieved_b / BF16_PEAK_TFLOPS, algorithmic_flop_per_step=flop_fb),
+                                   frac=achieved_b / BF16_PEAK_TFLOPS, algorithmic_flop_per_step=flop_fb,
+                                   board_power_during_timed_steps=power_b),
                      kernel_ms_per_step={k: v[1] / bsteps for k, v in kt_b.items()}))
     res["memory"] = _memory_audit(torch, lambda: lp.lp_lm_head_kl(*heads, None, y, dm, cfg.tile_rows), wsf_bytes,
                                   6 * 4 * cfg.T, 2 * 4 * cfg.T * cfg.V)

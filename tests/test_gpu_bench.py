@@ -33,6 +33,10 @@ def test_bench_prints_one_json_line_with_the_contract(monkeypatch, capsys):
     assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s" and r["peak"] == 2500.0
     assert r["achieved"] > 0 and abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-12
     assert r["traffic"] is None or r["traffic"] > 0
+    z = r["same_launch_on_zero_operands"]
+    assert z["kernel_ms_per_step"] > 0 and 0 < z["frac"] < 1.2
+    for pw in (r["board_power_during_timed_steps"], z["board_power"]):
+        assert pw is None or (pw["samples"] >= 1 and 0 < pw["mean_w"] <= pw["max_w"] < 5000)
     c = d["cpu_baseline"]
     assert c["kind"] == "oracle" and c["value"] > 0 and c["cores"] >= 1 and isinstance(c["sample"], str)
     assert c["parity_max_abs_err"] <= c["parity_tol"]
