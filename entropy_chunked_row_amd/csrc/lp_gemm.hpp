@@ -307,12 +307,26 @@ struct dtl_rsrc_t {
 };
 #endif
 
-template <int NINST>
+// LIN (dense K-contiguous rows): instruction j's rows are instruction 0's plus
+// j x LW x (64 / KC) rows, all with the same 16-byte chunk, so one offset, a
+// uniform step and a per-lane clamp describe them all (fewer live registers).
+template <int NINST, bool LIN = false>
 struct DtlRows {
+  static constexpr int N = NINST;
   dtl_rsrc_t rsrc;
-  uint32_t off[NINST];  // byte offsets from the operand base (the caller checks they fit in 32 bits)
-  uint32_t kstride;     // bytes per unit of K: 2 (K-contiguous) or ld * 2 (K-major)
-  int kvalid;           // K-major: rows of K that exist (the rest are clamped to the last)
+  uint32_t off[LIN ? 1 : NINST];  // byte offsets from the operand base (the caller checks they fit in 32 bits)
+  uint32_t jstride;               // LIN: bytes from one instruction's rows to the next's (uniform)
+  uint32_t offmax;                // LIN: offset of this lane's chunk in the last valid row
+  uint32_t kstride;               // bytes per unit of K: 2 (K-contiguous) or ld * 2 (K-major)
+  int kvalid;                     // K-major: rows of K that exist (the rest are clamped to the last)
+  __device__ __forceinline__ uint32_t at(int j) const {
+    if constexpr (LIN) {
+      const uint32_t o = off[0] + static_cast<uint32_t>(j) * jstride;
+      return o < offmax ? o : offmax;
+    } else {
+      return off[j];
+    }
+  }
 };
 
 // Raw buffer over [base, base + 4 GiB): offsets are kept in range by the row
@@ -339,17 +353,21 @@ __device__ __forceinline__ void dtl_load16(const dtl_rsrc_t& rsrc, uint16_t* dst
 }
 
 // K-contiguous operand: rows m0 + r of a row-major matrix (clamped to M - 1).
+// Instruction j moves rows r0 + j x LW x (64 / KC) with the lane's chunk kc;
+// the swizzle of a row depends only on row bits that j does not change (LW
+// even for 8 chunks per row, any LW for 4), so kc is the same for every j and
+// the clamp to row M - 1 is a clamp of the offset.
 template <class C, int NINST>
-__device__ __forceinline__ void dtl_rows_dense(DtlRows<NINST>& rw, int64_t ld, int M) {
+__device__ __forceinline__ void dtl_rows_dense(DtlRows<NINST, true>& rw, int64_t ld, int M) {
+  static_assert(C::KC == 4 || C::LW % 2 == 0, "chunk swizzle must not depend on the instruction index");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int j = 0; j < NINST; ++j) {
-    const int slot = (j * C::LW + wave) * 64 + lane;
-    const int r = slot / C::KC, pc = slot % C::KC;
-    const int kc = pc ^ lds_swz_k<C::KC>(r);
-    const int rr = r < M ? r : M - 1;
-    rw.off[j] = static_cast<uint32_t>((static_cast<int64_t>(rr) * ld + kc * 8) * 2);
-  }
+  const int slot = wave * 64 + lane;
+  const int r = slot / C::KC, pc = slot % C::KC;
+  const int kc = pc ^ lds_swz_k<C::KC>(r);
+  const int rr = r < M ? r : M - 1;
+  rw.off[0] = static_cast<uint32_t>((static_cast<int64_t>(rr) * ld + kc * 8) * 2);
+  rw.offmax = static_cast<uint32_t>((static_cast<int64_t>(M - 1) * ld + kc * 8) * 2);
+  rw.jstride = static_cast<uint32_t>(static_cast<int64_t>(C::LW * (64 / C::KC)) * ld * 2);
   rw.kstride = 2;
   rw.kvalid = 0x7fffffff;
 }
@@ -457,7 +475,7 @@ __device__ __forceinline__ void dtl_frag_piece(const uint16_t* stage, int kk, in
 // starting at K index kstart: rows past kvalid - 1 are moved back to it
 // (only in a stage that reaches past kvalid; the test is uniform).
 template <class C, int NINST, int ROWS>
-__device__ __forceinline__ uint32_t dtl_km_off(const DtlRows<NINST>& rw, int j, int kstart, int wave) {
+__device__ __forceinline__ uint32_t dtl_km_off(const DtlRows<NINST, false>& rw, int j, int kstart, int wave) {
   uint32_t voff = rw.off[j];
   if (kstart + C::BK > rw.kvalid) {
     const int lane = threadIdx.x & 63;
@@ -471,18 +489,27 @@ __device__ __forceinline__ uint32_t dtl_km_off(const DtlRows<NINST>& rw, int j, 
 // Issue global load instruction j (A for j < A_INST, else B) of the stage
 // starting at K index kstart; the per-lane part is a 32-bit offset, the
 // stage's K offset a scalar one.  Only the first LW waves load (see DtlCfg::LW).
-template <class C, int NA, int NB>
-__device__ __forceinline__ void dtl_issue_one(int j, int kstart, const DtlRows<NA>& ra, const DtlRows<NB>& rb,
-                                              uint16_t* stage, int wave) {
+template <class C, class RA, class RB>
+__device__ __forceinline__ void dtl_issue_one(int j, int kstart, const RA& ra, const RB& rb, uint16_t* stage,
+                                              int wave) {
+  constexpr int NA = RA::N;
   // `wave` is the uniform (scalar) wave index, so the LDS destination (M0) is scalar arithmetic
   if (j < NA) {
     uint16_t* dst = stage + (j * C::LW + wave) * 64 * 8;
-    const uint32_t voff = C::AKM ? dtl_km_off<C, NA, C::BM>(ra, j, kstart, wave) : ra.off[j];
+    uint32_t voff;
+    if constexpr (C::AKM)
+      voff = dtl_km_off<C, NA, C::BM>(ra, j, kstart, wave);
+    else
+      voff = ra.at(j);
     dtl_load16(ra.rsrc, dst, voff, static_cast<uint32_t>(kstart) * ra.kstride);
   } else {
     const int jb = j - NA;
     uint16_t* dst = stage + C::BM * C::BK + (jb * C::LW + wave) * 64 * 8;
-    const uint32_t voff = C::BKM ? dtl_km_off<C, NB, C::BN>(rb, jb, kstart, wave) : rb.off[jb];
+    uint32_t voff;
+    if constexpr (C::BKM)
+      voff = dtl_km_off<C, RB::N, C::BN>(rb, jb, kstart, wave);
+    else
+      voff = rb.at(jb);
     dtl_load16(rb.rsrc, dst, voff, static_cast<uint32_t>(kstart) * rb.kstride);
   }
 }
@@ -514,9 +541,9 @@ __device__ __forceinline__ void dtl_wait_vm(int pending) {
 //                      the first fragments of the next stage (from Y) and the
 //                      global loads of the stage NS steps ahead (into X),
 //                      which starts at K index k2.
-template <class C, bool NEXT, bool NEXT2>
-__device__ __forceinline__ void dtl_kstep(uint16_t* X, uint16_t* Y, int k2, const DtlRows<C::A_INST>& ra,
-                                          const DtlRows<C::B_INST>& rb, int wm, int wn,
+template <class C, bool NEXT, bool NEXT2, class RA, class RB>
+__device__ __forceinline__ void dtl_kstep(uint16_t* X, uint16_t* Y, int k2, const RA& ra,
+                                          const RB& rb, int wm, int wn,
                                           bf16x8_t (&fa)[2][C::MI], bf16x8_t (&fb)[2][C::NI],
                                           f32x16_t (&acc)[C::MI][C::NI], int pending, int wave) {
   constexpr int S = C::BK / 16;
@@ -550,7 +577,7 @@ __device__ __forceinline__ void dtl_kstep(uint16_t* X, uint16_t* Y, int k2, cons
 #pragma unroll
         for (int u = 0; u < (NL + NQ - 1) / NQ; ++u) {
           const int j = q * ((NL + NQ - 1) / NQ) + u;
-          if (j < NL) dtl_issue_one<C, C::A_INST, C::B_INST>(j, k2, ra, rb, X, wave);
+          if (j < NL) dtl_issue_one<C>(j, k2, ra, rb, X, wave);
         }
       }
       const int mi = q / C::NI, ni = q % C::NI;
@@ -571,9 +598,9 @@ __device__ __forceinline__ void dtl_kstep(uint16_t* X, uint16_t* Y, int k2, cons
 // fragments of the next substep go to the other A set in the first MI slots.
 // The last column's B fragment is read after the substep's last MFMA, before
 // the stage barrier, so no wave reads a stage that others may overwrite.
-template <class C, bool NEXT, bool NEXT2>
-__device__ __forceinline__ void dtl_kstep_bi(uint16_t* X, uint16_t* Y, int k2, const DtlRows<C::A_INST>& ra,
-                                             const DtlRows<C::B_INST>& rb, int wm, int wn,
+template <class C, bool NEXT, bool NEXT2, class RA, class RB>
+__device__ __forceinline__ void dtl_kstep_bi(uint16_t* X, uint16_t* Y, int k2, const RA& ra,
+                                             const RB& rb, int wm, int wn,
                                              bf16x8_t (&fa)[2][C::MI], bf16x8_t (&fb)[C::NI],
                                              f32x16_t (&acc)[C::MI][C::NI], int pending, int wave) {
   constexpr int S = C::BK / 16;
@@ -598,7 +625,7 @@ __device__ __forceinline__ void dtl_kstep_bi(uint16_t* X, uint16_t* Y, int k2, c
 #pragma unroll
         for (int u = 0; u < (NL + NQ - 1) / NQ; ++u) {
           const int j = q * ((NL + NQ - 1) / NQ) + u;
-          if (j < NL) dtl_issue_one<C, C::A_INST, C::B_INST>(j, k2, ra, rb, X, wave);
+          if (j < NL) dtl_issue_one<C>(j, k2, ra, rb, X, wave);
         }
       }
       const int ni = q / C::MI, mi = q % C::MI;
@@ -615,8 +642,8 @@ __device__ __forceinline__ void dtl_kstep_bi(uint16_t* X, uint16_t* Y, int k2, c
 
 // The K loop of one block on prepared row sources (see gemm_tile_dtl and
 // gemm_tile_dtl_dense below).  K is a multiple of BK and may be 0 (D = 0).
-template <class C>
-__device__ __forceinline__ void gemm_dtl_loop(const DtlRows<C::A_INST>& ra, const DtlRows<C::B_INST>& rb, int K,
+template <class C, class RA, class RB>
+__device__ __forceinline__ void gemm_dtl_loop(const RA& ra, const RB& rb, int K,
                                               uint16_t* lds, f32x16_t (&acc)[C::MI][C::NI]) {
   constexpr int NF = C::MI + C::NI;
   constexpr int NL = C::A_INST + C::B_INST;
@@ -638,7 +665,7 @@ __device__ __forceinline__ void gemm_dtl_loop(const DtlRows<C::A_INST>& ra, cons
       if (st < npro) {
 #pragma unroll
         for (int j = 0; j < NL; ++j)
-          dtl_issue_one<C, C::A_INST, C::B_INST>(j, st * C::BK, ra, rb, lds + st * C::STAGE_ELEMS, wave);
+          dtl_issue_one<C>(j, st * C::BK, ra, rb, lds + st * C::STAGE_ELEMS, wave);
       }
     }
     dtl_wait_vm<C>(npro - 1);
@@ -678,7 +705,7 @@ __device__ __forceinline__ void gemm_tile_dtl(const uint16_t* a, int64_t lda, in
                                               int64_t ldb, const int* b_rows, int N, int K, uint16_t* lds,
                                               f32x16_t (&acc)[C::MI][C::NI]) {
   static_assert(!C::AKM && !C::BKM, "K-contiguous operands");
-  DtlRows<C::A_INST> ra;
+  DtlRows<C::A_INST, true> ra;
   DtlRows<C::B_INST> rb;
   dtl_rows_dense<C, C::A_INST>(ra, lda, M);
   dtl_rows_gather<C, C::B_INST>(rb, ldb, b_rows, N);
@@ -700,8 +727,8 @@ template <class C>
 __device__ __forceinline__ void gemm_tile_dtl_dense(const uint16_t* a, int64_t lda, int M, int kvalid_a,
                                                     const uint16_t* b, int64_t ldb, int N, int kvalid_b, int K,
                                                     uint16_t* lds, f32x16_t (&acc)[C::MI][C::NI]) {
-  DtlRows<C::A_INST> ra;
-  DtlRows<C::B_INST> rb;
+  DtlRows<C::A_INST, !C::AKM> ra;
+  DtlRows<C::B_INST, !C::BKM> rb;
   if constexpr (C::AKM)
     dtl_rows_km<C, C::A_INST, C::BM>(ra, lda, M, kvalid_a);
   else
@@ -709,7 +736,7 @@ __device__ __forceinline__ void gemm_tile_dtl_dense(const uint16_t* a, int64_t l
   if constexpr (C::BKM)
     dtl_rows_km<C, C::B_INST, C::BN>(rb, ldb, N, kvalid_b);
   else
-    dtl_rows_gather<C, C::B_INST>(rb, ldb, nullptr, N);
+    dtl_rows_dense<C, C::B_INST>(rb, ldb, N);
   ra.rsrc = dtl_rsrc(a);
   rb.rsrc = dtl_rsrc(b);
   gemm_dtl_loop<C>(ra, rb, K, lds, acc);
