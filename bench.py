@@ -344,7 +344,10 @@ def bench_lm_head_fwd(lp, torch, np, synth, steps, warmup, cpu_seconds, cfg=None
             sclk_mhz_during_kernel=sclk or None, sclk_samples=sclk_n,
             frac_at_observed_clock=(achieved / (BF16_PEAK_TFLOPS * sclk / 2400.0)) if sclk else None,
             board_power_during_timed_steps=power,
-            same_launch_on_zero_operands=_zero_operand_run(lp, torch, cfg, y, m, ws, flop_step))
+            same_launch_on_zero_operands=_zero_operand_run(lp, torch, cfg, y, m, ws, flop_step),
+            library_gemm_same_shape=_library_gemm_same_shape(torch, hid, W, m, flop_step))
+        lib = res["roofline"]["library_gemm_same_shape"]
+        res["roofline"]["frac_of_library_gemm_same_shape"] = achieved / lib["achieved_tflops"]
     res["memory"] = _memory_audit(
         torch, lambda: lp.lp_lm_head_logprobs_entropy(hid, W, y, m, cfg.temperature, cfg.tile_rows),
         ws_bytes, 3 * 4 * cfg.T, 4 * cfg.T * cfg.V)
@@ -387,6 +390,30 @@ def _zero_operand_run(lp, torch, cfg, y, m, ws, flop_step, steps=3):
     achieved = flop_step * steps / (gemm_ms * 1e-3) / 1e12
     return dict(kernel_ms_per_step=gemm_ms / steps, achieved_tflops=achieved, frac=achieved / BF16_PEAK_TFLOPS,
                 sclk_mhz_during_kernel=sclk or None, board_power=kt["_power"])
+
+
+def _library_gemm_same_shape(torch, hid, W, m, flop_step, steps=5):
+    """Context only: the library bf16 GEMM (torch.matmul) of the scored hidden
+    rows by the weight, bf16 logits out, on the forward workload's shape -- the
+    matrix product alone, without the log-softmax / entropy the fused kernel
+    folds in, and with the [rows x V] logits it writes."""
+    hs = hid[torch.nonzero(m).flatten()].contiguous()
+    out = torch.empty((hs.shape[0], W.shape[0]), dtype=torch.bfloat16, device="cuda")
+    wt = W.t()
+
+    def step():
+        torch.matmul(hs, wt, out=out)
+
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < SETTLE_SECONDS:
+        step()
+        torch.cuda.synchronize()
+    with _PowerSampler() as pw:
+        ms = _events_ms(torch, step, steps) / steps
+    del hs, out
+    achieved = flop_step / (ms * 1e-3) / 1e12
+    return dict(ms_per_call=ms, achieved_tflops=achieved, frac=achieved / BF16_PEAK_TFLOPS, board_power=pw.summary(),
+                op="torch.matmul(hidden[scored rows], weight^T), bf16 in and out")
 
 
 def bench_tiny_lm_head(lp, torch, np, synth, steps, warmup, cpu_seconds):

@@ -33,6 +33,9 @@ def test_bench_prints_one_json_line_with_the_contract(monkeypatch, capsys):
     assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s" and r["peak"] == 2500.0
     assert r["achieved"] > 0 and abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-12
     assert r["traffic"] is None or r["traffic"] > 0
+    lg = r["library_gemm_same_shape"]
+    assert lg["ms_per_call"] > 0 and r["frac_of_library_gemm_same_shape"] == pytest.approx(
+        r["achieved"] / lg["achieved_tflops"])
     z = r["same_launch_on_zero_operands"]
     assert z["kernel_ms_per_step"] > 0 and 0 < z["frac"] < 1.2
     for pw in (r["board_power_during_timed_steps"], z["board_power"]):
