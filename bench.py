@@ -699,25 +699,28 @@ def _probe_lib():
     probe.lp_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     probe.lp_probe_mfma.restype = ctypes.c_int
     probe.lp_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    probe.lp_probe_exp.restype = ctypes.c_int
+    probe.lp_probe_exp.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     probe.lp_probe_clock_rates.restype = ctypes.c_int
     probe.lp_probe_clock_rates.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
     return probe
 
 
-def measure_mfma(torch, probe):
-    """Back-to-back v_mfma_f32_32x32x16_bf16 at two waves per SIMD on every CU
-    (liblp_probe.so), after SETTLE_SECONDS of the same work: the best of three
-    timed launches, and the shader clock the matrix cores ran at (ratio of the
-    shader-clock and fixed-frequency counters read inside the launch)."""
+def _clocked_probe(torch, probe, fn, iters, per_cu=1):
+    """Runs a liblp_probe.so kernel that records clock pairs (per_cu
+    workgroups per CU) for SETTLE_SECONDS, then three timed launches; returns
+    the best launch time (ms) and the shader clock (MHz) its workgroups ran at
+    (ratio of the shader-clock and fixed-frequency counters read inside the
+    launch)."""
     import ctypes
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    iters = 200000
-    clocks = torch.zeros(4 * cus, dtype=torch.int64, device="cuda")
+    blocks = per_cu * cus
+    clocks = torch.zeros(4 * blocks, dtype=torch.int64, device="cuda")
     sink = torch.zeros(1, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
 
     def run():
-        assert probe.lp_probe_mfma(cus, iters, clocks.data_ptr(), sink.data_ptr(), stream) == 0
+        assert fn(blocks, iters, clocks.data_ptr(), sink.data_ptr(), stream) == 0
 
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < SETTLE_SECONDS:
@@ -726,30 +729,53 @@ def measure_mfma(torch, probe):
     best, sclk = None, None
     wall, peak = ctypes.c_int(0), ctypes.c_int(0)
     rates_ok = probe.lp_probe_clock_rates(ctypes.byref(wall), ctypes.byref(peak)) == 0
-    flop = cus * 8 * iters * 8 * MFMA_FLOP
     for _ in range(3):
         ms = _events_ms(torch, run, 1)
-        tf = flop / (ms * 1e-3) / 1e12
-        if best is None or tf > best:
-            best = tf
+        if best is None or ms < best:
+            best = ms
             c = clocks.cpu().numpy().reshape(-1, 4).astype("float64")
             dt, dr = c[:, 1] - c[:, 0], c[:, 3] - c[:, 2]
             if rates_ok and (dr > 0).all():
                 sclk = float((dt / dr).mean() * wall.value / 1e3)  # MHz
     del clocks, sink
-    return dict(bf16_mfma_tflops=best, mfma_probe_sclk_mhz=sclk,
-                peak_sclk_mhz=peak.value / 1e3 if rates_ok else None,
+    return best, sclk, cus, (peak.value / 1e3 if rates_ok else None)
+
+
+def measure_mfma(torch, probe):
+    """Back-to-back v_mfma_f32_32x32x16_bf16 at two waves per SIMD on every CU
+    (liblp_probe.so), after SETTLE_SECONDS of the same work: the best of three
+    timed launches, and the shader clock the matrix cores ran at."""
+    iters = 200000
+    ms, sclk, cus, peak = _clocked_probe(torch, probe, probe.lp_probe_mfma, iters)
+    flop = cus * 8 * iters * 8 * MFMA_FLOP
+    return dict(bf16_mfma_tflops=flop / (ms * 1e-3) / 1e12, mfma_probe_sclk_mhz=sclk, peak_sclk_mhz=peak,
                 mfma_probe=f"{cus} workgroups x 8 waves x {iters} x 8 back-to-back v_mfma_f32_32x32x16_bf16 "
                            "(two waves per SIMD), best of 3 after the settle")
 
 
+def measure_exp(torch, probe):
+    """Back-to-back v_exp_f32 (sixteen independent chains per lane, two
+    workgroups of 16 waves per CU, so every SIMD holds 8 waves whatever CU the
+    dispatcher picks): the transcendental rate the row kernels draw on, one
+    exp2 per logit."""
+    iters = 20000
+    ms, sclk, cus, _ = _clocked_probe(torch, probe, probe.lp_probe_exp, iters, per_cu=2)
+    n = 2 * cus * 1024 * iters * 16
+    rate = n / (ms * 1e-3)
+    return dict(exp2_per_s=rate, exp_probe_sclk_mhz=sclk,
+                exp2_per_clk_per_cu=(rate / (sclk * 1e6) / cus) if sclk else None,
+                exp_probe=f"{2 * cus} workgroups x 1024 lanes x {iters} x 16 back-to-back v_exp_f32, best of 3")
+
+
 def measure_achievable(torch):
     """Second denominators beside the datasheet peaks, measured on this GPU:
-    the read bandwidth of a streaming read of 4 GiB and the bf16 matrix-core
-    rate of back-to-back MFMAs (both from the bench-only liblp_probe.so), and,
-    as context, a large library bf16 GEMM (torch.matmul, 8192^3)."""
+    the read bandwidth of a streaming read of 4 GiB, the bf16 matrix-core rate
+    of back-to-back MFMAs and the v_exp_f32 rate (all from the bench-only
+    liblp_probe.so), and, as context, a large library bf16 GEMM (torch.matmul,
+    8192^3)."""
     out = dict(hbm_read_gbs=None, bf16_mfma_tflops=None, mfma_probe_sclk_mhz=None, bf16_gemm_tflops=None,
-               source="liblp_probe.so: streaming read of 4 GiB (best of 5 grid sizes), back-to-back MFMAs; "
+               source="liblp_probe.so: streaming read of 4 GiB (best of 5 grid sizes), back-to-back MFMAs, "
+                      "back-to-back v_exp_f32; "
                       "torch.matmul bf16 8192^3 (library GEMM, context only)")
     a = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
     b = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
@@ -767,6 +793,7 @@ def measure_achievable(torch):
     probe = _probe_lib()
     if probe is not None:
         out.update(measure_mfma(torch, probe))
+        out.update(measure_exp(torch, probe))
         nbytes = 4 << 30
         buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
         sink = torch.zeros(1, dtype=torch.int32, device="cuda")
@@ -790,6 +817,10 @@ def _add_achievable(roof, ach):
         return
     if roof.get("unit") == "GB/s":
         ref = ach.get("hbm_read_gbs")
+        if ach.get("exp2_per_s"):
+            # the row kernels evaluate one exp2 per 2-byte logit they read: the share of the
+            # transcendental rate the probe measured that the achieved bandwidth draws on
+            roof["exp2_share_of_probe_rate"] = roof["achieved"] * 1e9 / 2 / ach["exp2_per_s"]
     else:
         ref = ach.get("bf16_mfma_tflops")
         if ach.get("bf16_gemm_tflops"):

@@ -11,6 +11,8 @@
 //                  each workgroup also reads the shader-clock counter and the
 //                  fixed-frequency counter at its start and end, which gives
 //                  the clock the matrix cores ran at.
+//   k_probe_exp    back-to-back v_exp_f32 (the transcendental unit that the
+//                  row kernels use once per logit), same clock records.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -90,7 +92,50 @@ __global__ void __launch_bounds__(512) k_probe_mfma(int iters, unsigned long lon
   if (s == 1234.5f) sink[0] = s;
 }
 
+// 16 waves per workgroup (four per SIMD: the exponential's latency needs
+// that many waves in flight to reach its issue rate); each lane runs 16
+// independent chains x <- 2^(-x) (one v_exp_f32 with a negated source per
+// step, no other arithmetic; the chains stay in (0.5, 1]).  Thread 0 records
+// the same clock pairs as k_probe_mfma.
+__global__ void __launch_bounds__(1024) k_probe_exp(int iters, unsigned long long* __restrict__ clocks,
+                                                    float* __restrict__ sink) {
+  float x[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) x[j] = 0.5f + static_cast<float>((threadIdx.x + j) & 63) * (1.0f / 128.0f);
+  __syncthreads();
+  unsigned long long t0 = 0, r0 = 0;
+  if (threadIdx.x == 0) {
+    t0 = __builtin_amdgcn_s_memtime();
+    r0 = __builtin_amdgcn_s_memrealtime();
+  }
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) x[j] = __builtin_amdgcn_exp2f(-x[j]);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) s += x[j];
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+    const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
+    clocks[4 * blockIdx.x + 0] = t0;
+    clocks[4 * blockIdx.x + 1] = t1;
+    clocks[4 * blockIdx.x + 2] = r0;
+    clocks[4 * blockIdx.x + 3] = r1;
+  }
+  if (s == 1234.5f) sink[0] = s;
+}
+
 }  // namespace
+
+extern "C" int lp_probe_exp(int blocks, int iters, unsigned long long* clocks, float* sink, void* stream) {
+  if (blocks <= 0 || iters <= 0 || !clocks || !sink) return 1;
+  if ((reinterpret_cast<uintptr_t>(clocks) & 7u) != 0 || (reinterpret_cast<uintptr_t>(sink) & 3u) != 0) return 1;
+  hipLaunchKernelGGL(k_probe_exp, dim3(static_cast<unsigned>(blocks)), dim3(1024), 0, static_cast<hipStream_t>(stream),
+                     iters, clocks, sink);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
 
 extern "C" int lp_probe_mfma(int blocks, int iters, unsigned long long* clocks, float* sink, void* stream) {
   if (blocks <= 0 || iters <= 0 || !clocks || !sink) return 1;

@@ -2,8 +2,10 @@
  * lp_probe.h -- measurement helper shipped beside liblp.so as liblp_probe.so.
  *
  * Not an entry point of the log-prob path: bench.py uses it to measure the
- * HBM read bandwidth and the bf16 matrix-core rate the GPU it runs on
- * reaches, reported next to the datasheet peaks as second denominators.
+ * HBM read bandwidth, the bf16 matrix-core rate and the v_exp_f32 rate the
+ * GPU it runs on reaches, reported next to the datasheet peaks as second
+ * denominators (and, for the exponential, the ALU budget of the row kernels,
+ * which evaluate one per logit).
  */
 #pragma once
 
@@ -40,6 +42,17 @@ int lp_probe_read(const void* buf, int64_t bytes, int blocks, unsigned* sink, vo
  * launch failed.
  */
 int lp_probe_mfma(int blocks, int iters, unsigned long long* clocks, float* sink, void* stream);
+
+/*
+ * Launches `blocks` workgroups of 1024 threads (16 waves, four per SIMD),
+ * each lane running `iters` x 16 v_exp_f32 (sixteen independent chains
+ * x <- 2^-x, no other arithmetic), on `stream`: total exp2 evaluations =
+ * blocks x 1024 x iters x 16.
+ * `clocks` and `sink` as for lp_probe_mfma (same clock records, same
+ * ownership).  Returns 0 on launch, 1 on an invalid argument (nothing
+ * launched), 2 if the launch failed.
+ */
+int lp_probe_exp(int blocks, int iters, unsigned long long* clocks, float* sink, void* stream);
 
 /*
  * Host query of the current device: the rate of the fixed-frequency counter

@@ -43,7 +43,7 @@ def test_probe_library_exports_its_declaration():
     it rejects bad arguments before launching anything."""
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "lp_probe.h")).read(), flags=re.S)
     names = re.findall(r"^\s*int\s+(lp_probe_[a-z_0-9]+)\s*\(", text, flags=re.M)
-    assert names == ["lp_probe_read", "lp_probe_mfma", "lp_probe_clock_rates"]
+    assert names == ["lp_probe_read", "lp_probe_mfma", "lp_probe_exp", "lp_probe_clock_rates"]
     path = os.path.join(ROOT, "entropy_chunked_row_amd", "liblp_probe.so")
     if not os.path.exists(path):
         pytest.skip("liblp_probe.so not built")
@@ -64,6 +64,13 @@ def test_probe_library_exports_its_declaration():
     assert g(256, 0, FAKE, FAKE, None) == 1
     assert g(256, 10, None, FAKE, None) == 1
     assert g(256, 10, FAKE + 4, FAKE, None) == 1  # clocks not 8-byte aligned
+    e = probe.lp_probe_exp
+    e.restype = ctypes.c_int
+    e.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    assert e(0, 10, FAKE, FAKE, None) == 1
+    assert e(256, 0, FAKE, FAKE, None) == 1
+    assert e(256, 10, FAKE, None, None) == 1
+    assert e(256, 10, FAKE, FAKE + 2, None) == 1  # sink not 4-byte aligned
     assert "lp_probe" not in " ".join(header_functions())
 
 

@@ -59,4 +59,7 @@ def test_bench_prints_one_json_line_with_the_contract(monkeypatch, capsys):
     a = d["achievable"]
     assert a["hbm_read_gbs"] > 1000 and a["bf16_mfma_tflops"] > 500 and a["bf16_gemm_tflops"] > 100
     assert a["mfma_probe_sclk_mhz"] is None or 100 < a["mfma_probe_sclk_mhz"] < 5000
+    # v_exp_f32: at most one per lane per clock on a SIMD of 16 lanes x 4 SIMDs, so below 64 per clock per CU
+    assert a["exp2_per_s"] > 1e11 and (a["exp2_per_clk_per_cu"] is None or 1 < a["exp2_per_clk_per_cu"] <= 64.5)
+    assert 0 < li["exp2_share_of_probe_rate"] < 1
     assert r["frac_of_achievable"] == pytest.approx(r["achieved"] / a["bf16_mfma_tflops"])
