@@ -233,13 +233,8 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
 #ifndef LP_FRAG_PER_SLOT
 #define LP_FRAG_PER_SLOT 2
 #endif
-#ifndef LP_SCHED_HINTS
-#define LP_SCHED_HINTS 0
-#endif
 
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 
 template <int BM_, int BN_, int WGM_, int WGN_, int BK_ = 64, int NS_ = 2, bool AKM_ = false, bool BKM_ = false>
 struct DtlCfg {
